@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Throughput of the Flash-MoE expert layer on one MI355X.
+
+A step is one pass of the whole layer (RMSNorm, router GEMV, softmax/top-K,
+fused gate+up dequant GEMV + SwiGLU for the K selected experts and the shared
+expert, down-projection with weighted combine, sigmoid-gated shared expert and
+residual) over one batch of synthetic tokens, through the C ABI.
+
+Default workload: the single-token layer of hidden 4096, FFN 1024, 512 4-bit
+experts + 1 shared, top-4.  Eight independent layers (8 x 3.6 GB) are resident
+and steps rotate over them and over a pool of 1024 tokens, so consecutive
+steps do not re-read the same experts from cache.
+
+Prints one JSON line.  `value` is tokens/s with all inputs resident in HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_BPS = 8.0e12  # MI355X HBM3E peak
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2048)
+    p.add_argument("--warmup", type=int, default=64)
+    p.add_argument("--workload", default="layer4", choices=["layer4", "layer2", "batch32", "tiny"])
+    p.add_argument("--layers", type=int, default=8, help="resident layers the steps rotate over")
+    p.add_argument("--pool", type=int, default=1024, help="distinct tokens the steps rotate over")
+    p.add_argument("--mode", default="graph", choices=["graph", "api"],
+                   help="graph: the timed steps are one captured HIP graph; api: one ABI call per step")
+    p.add_argument("--cpu-sample", type=int, default=24, help="tokens for the oracle CPU baseline (0: skip)")
+    p.add_argument("--quiet", action="store_true")
+    return p.parse_args()
+
+
+def log(args, msg):
+    if not args.quiet:
+        print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        msg = (f"bench.py: --gpus {args.gpus} is not supported: this build runs the expert layer on one GPU "
+               "(every expert resident in that GPU's HBM); run with --gpus 1")
+        print(msg, flush=True)
+        print(msg, file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_dequant_expert_router_amd as moe
+    import synthetic as syn
+    from bit_dequant_expert_router_amd.weights import layer_generated
+
+    wl = syn.WORKLOADS[args.workload]
+    dims = wl.dims
+    T = wl.n_tokens
+    K = dims.top_k
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    R = max(1, args.layers)
+    log(args, f"[bench] {wl.name}: {wl.description}; generating {R} layers on the device")
+    layers = [layer_generated(dims, syn.layer_dense(wl.seed, l, dims), wl.seed, l, device=dev) for l in range(R)]
+    descs = [lw.descriptor() for lw in layers]
+    P = max(1, args.pool)
+    pool = torch.from_numpy(syn.tokens(wl.seed, P * T, dims.hidden).reshape(P, T, dims.hidden)).to(dev)
+    out = torch.empty_like(pool)
+    ridx = torch.empty((P, T, K), dtype=torch.int32, device=dev)
+    rw = torch.empty((P, T, K), dtype=torch.float32, device=dev)
+    wsb = moe.moe_workspace_bytes(dims, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    moe.moe_workspace_init(ws)
+    torch.cuda.synchronize()
+
+    def step(i):
+        j = i % P
+        moe.moe_layer_forward(dims, descs[i % R], pool[j], out[j], T, ridx[j], rw[j], ws, wsb)
+
+    # warmup
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region
+    nsteps = args.steps
+    graph = None
+    if args.mode == "graph":
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                for i in range(nsteps):
+                    step(i)
+        torch.cuda.synchronize()
+        graph.replay()  # warm replay
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(nsteps):
+            step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / nsteps
+    tokens_per_s = nsteps * T / elapsed
+
+    # algorithmic expert-weight bytes: distinct selected experts per step + shared
+    idx_all = ridx.cpu().numpy()
+    eb = moe.moe_expert_bytes(dims)
+    distinct = [len(np.unique(idx_all[j].ravel())) + 1 for j in range(P)]
+    steps_idx = [i % P for i in range(nsteps)]
+    bytes_total = float(sum(distinct[j] for j in steps_idx)) * eb
+    bytes_per_step = bytes_total / nsteps
+    router_bytes = dims.n_experts * dims.hidden * 2
+
+    # per-launch duration, events on the launch stream (a separate pass over the same steps)
+    nprobe = min(nsteps, 512)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(nprobe)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(nprobe)]
+    for i in range(nprobe):
+        starts[i].record()
+        step(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    durs = np.array([starts[i].elapsed_time(ends[i]) for i in range(nprobe)]) * 1e-3  # seconds
+    launch_s = float(np.mean(durs))
+    bytes_probe = float(np.mean([distinct[i % P] for i in range(nprobe)])) * eb
+    achieved = bytes_probe / launch_s
+
+    result = {
+        "metric": "MoE-layer decode tokens/s (effective expert-weight HBM GB/s and % of peak alongside)",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": nsteps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: {wl.description}",
+            "hidden": dims.hidden, "ffn": dims.ffn, "n_experts": dims.n_experts, "top_k": K,
+            "bits": dims.bits, "group_size": dims.group_size, "tokens_per_step": T,
+            "resident_layers": R, "token_pool": P, "mode": args.mode,
+        },
+        "expert_bytes_per_step": round(bytes_per_step),
+        "router_bytes_per_step": router_bytes,
+        "effective_expert_GBps": round(bytes_per_step * nsteps / elapsed / 1e9, 1),
+        "pct_of_hbm_peak": round(100.0 * bytes_per_step * nsteps / elapsed / HBM_PEAK_BPS, 2),
+        "roofline": {
+            "kernel": "moe_layer_forward (k_router + k_gateup + k_down)",
+            "bound": "hbm",
+            "achieved": round(achieved / 1e9, 1),
+            "peak": HBM_PEAK_BPS / 1e9,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_BPS, 4),
+            "traffic": None,
+            "launch_us": round(launch_s * 1e6, 3),
+        },
+    }
+
+    if args.cpu_sample > 0:
+        result["cpu_baseline"] = cpu_baseline(args, wl, dims)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, wl, dims):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    import synthetic as syn
+    n = args.cpu_sample
+    R = max(1, args.layers)
+    xs = syn.tokens(wl.seed, n * wl.n_tokens, dims.hidden).reshape(n, wl.n_tokens, dims.hidden)
+    cache = {}
+
+    def fetch(layer):
+        def f(e):
+            key = (layer, e)
+            if key not in cache:
+                cache[key] = syn.expert_canonical(wl.seed, layer, e, dims)
+            return cache[key]
+        return f
+
+    dense = {l: syn.layer_dense(wl.seed, l, dims) for l in range(min(R, n))}
+    # routing first (untimed) so that input generation is outside the timed region
+    for i in range(n):
+        l = i % R % len(dense)
+        for t in range(wl.n_tokens):
+            h = oracle.rmsnorm(xs[i, t], dense[l]["norm_weight"], dims.rms_eps)
+            idx, _ = oracle.route(oracle.gemv_bf16(dense[l]["router_weight"], h), dims.top_k)
+            for e in list(idx) + [dims.n_experts]:
+                fetch(l)(int(e))
+    log(args, f"[bench] cpu baseline: oracle on {n} steps x {wl.n_tokens} tokens, {oracle.threads()} threads")
+    t0 = time.perf_counter()
+    for i in range(n):
+        l = i % R % len(dense)
+        for t in range(wl.n_tokens):
+            oracle.layer(dims, xs[i, t], dense[l], fetch(l))
+    el = time.perf_counter() - t0
+    return {
+        "value": round(n * wl.n_tokens / el, 3),
+        "unit": "tokens/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"{n} steps of the {wl.name} workload ({n * wl.n_tokens} tokens, layers rotating), "
+                  f"fp64 C oracle, {el:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()

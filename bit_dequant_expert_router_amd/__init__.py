@@ -1,0 +1,177 @@
+"""Python binding of libmoe, the MI355X (gfx950) Flash-MoE expert layer.
+
+Argument marshalling only: every function here forwards to the entry point of
+the same name in ``include/moe.h``.  Tensors are PyTorch tensors on the GPU
+(used for device memory and streams) or raw device addresses given as ints.
+There is no fallback: importing this package raises if ``libmoe.so`` has not
+been built (``python -m bit_dequant_expert_router_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m bit_dequant_expert_router_amd.build` "
+        "(there is no CPU fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_ALIGNMENT = -4
+MOE_ERR_HIP = -5
+
+
+class moe_dims_t(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("bits", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float)]
+
+
+class moe_layer_t(ctypes.Structure):
+    _fields_ = [("norm_weight", ctypes.c_void_p), ("router_weight", ctypes.c_void_p),
+                ("shared_gate", ctypes.c_void_p), ("experts", ctypes.c_void_p),
+                ("shared_expert", ctypes.c_void_p)]
+
+
+_vp = ctypes.c_void_p
+_dimsp = ctypes.POINTER(moe_dims_t)
+_layerp = ctypes.POINTER(moe_layer_t)
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "moe_abi_version": (ctypes.c_int, []),
+    "moe_check_dims": (ctypes.c_int, [_dimsp]),
+    "moe_expert_bytes": (_sz, [_dimsp]),
+    "moe_workspace_bytes": (_sz, [_dimsp, _i32]),
+    "moe_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
+    "moe_pack_expert": (ctypes.c_int, [_dimsp, _vp * 3, _vp * 3, _vp * 3, _vp, _vp]),
+    "moe_generate_layer": (ctypes.c_int, [_dimsp, ctypes.c_uint64, ctypes.c_uint32, _vp, _vp, _vp]),
+    "moe_layer_forward": (ctypes.c_int, [_dimsp, _layerp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "moe_stack_forward": (ctypes.c_int, [_dimsp, _layerp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {moe_status_string(status)} ({status})")
+        self.status = status
+
+
+def _addr(t) -> Optional[int]:
+    """Device address of a tensor, an int address, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream or None
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+def _check(fn: str, rc: int) -> int:
+    if rc != MOE_OK:
+        raise MoeError(fn, rc)
+    return rc
+
+
+def make_dims(hidden: int, ffn: int, n_experts: int, top_k: int, bits: int, group_size: int = 64,
+              rms_eps: float = 1e-6) -> moe_dims_t:
+    return moe_dims_t(hidden, ffn, n_experts, top_k, bits, group_size, rms_eps)
+
+
+def dims_of(d) -> moe_dims_t:
+    """moe_dims_t from any object with hidden/ffn/n_experts/top_k/bits fields."""
+    if isinstance(d, moe_dims_t):
+        return d
+    return make_dims(d.hidden, d.ffn, d.n_experts, d.top_k, d.bits, getattr(d, "group_size", 64),
+                     getattr(d, "rms_eps", 1e-6))
+
+
+def make_layer(norm_weight, router_weight, shared_gate, experts, shared_expert) -> moe_layer_t:
+    return moe_layer_t(_addr(norm_weight), _addr(router_weight), _addr(shared_gate), _addr(experts),
+                       _addr(shared_expert))
+
+
+# --------------------------------------------------------------------------- #
+# entry points (same names as the C ABI)
+# --------------------------------------------------------------------------- #
+def moe_abi_version() -> int:
+    return int(_lib.moe_abi_version())
+
+
+def moe_status_string(status: int) -> str:
+    return _lib.moe_status_string(int(status)).decode()
+
+
+def moe_check_dims(dims) -> int:
+    return int(_lib.moe_check_dims(ctypes.byref(dims_of(dims))))
+
+
+def moe_expert_bytes(dims) -> int:
+    return int(_lib.moe_expert_bytes(ctypes.byref(dims_of(dims))))
+
+
+def moe_workspace_bytes(dims, n_tokens: int) -> int:
+    return int(_lib.moe_workspace_bytes(ctypes.byref(dims_of(dims)), int(n_tokens)))
+
+
+def moe_workspace_init(workspace, workspace_bytes: Optional[int] = None, stream=None) -> int:
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    return _check("moe_workspace_init", _lib.moe_workspace_init(_addr(workspace), nbytes, _stream(stream)))
+
+
+def moe_pack_expert(dims, codes: Sequence, scale: Sequence, bias: Sequence, dst, stream=None) -> int:
+    c = (_vp * 3)(*[_addr(t) for t in codes])
+    s = (_vp * 3)(*[_addr(t) for t in scale])
+    b = (_vp * 3)(*[_addr(t) for t in bias])
+    return _check("moe_pack_expert",
+                  _lib.moe_pack_expert(ctypes.byref(dims_of(dims)), c, s, b, _addr(dst), _stream(stream)))
+
+
+def moe_generate_layer(dims, seed: int, layer: int, experts, shared_expert, stream=None) -> int:
+    return _check("moe_generate_layer",
+                  _lib.moe_generate_layer(ctypes.byref(dims_of(dims)), int(seed), int(layer), _addr(experts),
+                                          _addr(shared_expert), _stream(stream)))
+
+
+def moe_layer_forward(dims, layer: moe_layer_t, x, y, n_tokens: int, route_idx, route_w, workspace,
+                      workspace_bytes: Optional[int] = None, stream=None) -> int:
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    return _check("moe_layer_forward",
+                  _lib.moe_layer_forward(ctypes.byref(dims_of(dims)), ctypes.byref(layer), _addr(x), _addr(y),
+                                         int(n_tokens), _addr(route_idx), _addr(route_w), _addr(workspace),
+                                         nbytes, _stream(stream)))
+
+
+def moe_stack_forward(dims, layers: Sequence[moe_layer_t], x, y, n_tokens: int, route_idx, route_w,
+                      workspace, workspace_bytes: Optional[int] = None, stream=None) -> int:
+    arr = (moe_layer_t * len(layers))(*layers)
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    return _check("moe_stack_forward",
+                  _lib.moe_stack_forward(ctypes.byref(dims_of(dims)), arr, len(layers), _addr(x), _addr(y),
+                                         int(n_tokens), _addr(route_idx), _addr(route_w), _addr(workspace),
+                                         nbytes, _stream(stream)))

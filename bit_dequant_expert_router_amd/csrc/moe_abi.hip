@@ -1,0 +1,209 @@
+// moe_abi.hip -- the extern "C" boundary declared in include/moe.h.
+//
+// Every argument is checked on the host before anything is enqueued; the
+// checks make no HIP call, so they behave the same with or without a GPU.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+using namespace moe;
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_dims_impl(const moe_dims_t *d) {
+    if (!d) return MOE_ERR_INVALID_ARG;
+    if (d->hidden <= 0 || d->ffn <= 0 || d->n_experts <= 0 || d->top_k <= 0) return MOE_ERR_INVALID_ARG;
+    if (d->bits <= 0 || d->bits > 8) return MOE_ERR_INVALID_ARG;
+    if (d->group_size <= 0) return MOE_ERR_INVALID_ARG;
+    if (!(d->rms_eps >= 0.0f) || !isfinite(d->rms_eps)) return MOE_ERR_INVALID_ARG;
+    if (d->hidden % d->group_size != 0 || d->ffn % d->group_size != 0) return MOE_ERR_INVALID_ARG;
+    if (d->top_k > d->n_experts) return MOE_ERR_INVALID_ARG;
+    if (d->bits != 2 && d->bits != 4) return MOE_ERR_UNSUPPORTED;
+    if (d->group_size != kGroup) return MOE_ERR_UNSUPPORTED;
+    if (d->n_experts > kMaxExperts || d->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+    if (!is_pow2(d->hidden) || d->hidden < kMinDim || d->hidden > kMaxDim) return MOE_ERR_UNSUPPORTED;
+    if (!is_pow2(d->ffn) || d->ffn < kMinDim || d->ffn > kMaxDim) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+Shape shape_of(const moe_dims_t *d) {
+    Shape s;
+    s.H = d->hidden;
+    s.F = d->ffn;
+    s.E = d->n_experts;
+    s.K = d->top_k;
+    s.bits = d->bits;
+    s.eps = d->rms_eps;
+    return s;
+}
+
+int check_layer(const moe_layer_t *l) {
+    if (!l || !l->norm_weight || !l->router_weight || !l->shared_gate || !l->experts || !l->shared_expert)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(l->norm_weight, 16) || !aligned(l->router_weight, 16) || !aligned(l->shared_gate, 16) ||
+        !aligned(l->experts, kAlign) || !aligned(l->shared_expert, kAlign))
+        return MOE_ERR_ALIGNMENT;
+    return MOE_OK;
+}
+
+size_t workspace_bytes_checked(const moe_dims_t *dims, int32_t n_tokens) {
+    if (check_dims_impl(dims) != MOE_OK || n_tokens < 1) return 0;
+    return workspace_bytes(shape_of(dims), n_tokens);
+}
+
+bool overlap_not_equal(const void *a, const void *b, size_t bytes) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    if (x == y) return false;
+    return x < y + bytes && y < x + bytes;
+}
+
+int check_forward_common(const moe_dims_t *dims, const float *x, float *y, int32_t n_tokens,
+                         int32_t *route_idx, float *route_w, void *workspace, size_t workspace_bytes) {
+    int rc = check_dims_impl(dims);
+    if (rc != MOE_OK) return rc;
+    if (n_tokens < 1 || n_tokens > 65535) return MOE_ERR_INVALID_ARG;
+    if (!x || !y || !workspace) return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, kAlign)) return MOE_ERR_ALIGNMENT;
+    if ((route_idx && !aligned(route_idx, 4)) || (route_w && !aligned(route_w, 4))) return MOE_ERR_ALIGNMENT;
+    if (overlap_not_equal(x, y, (size_t)n_tokens * dims->hidden * sizeof(float))) return MOE_ERR_INVALID_ARG;
+    if (workspace_bytes < workspace_bytes_checked(dims, n_tokens)) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+int moe_check_dims(const moe_dims_t *dims) { return check_dims_impl(dims); }
+
+size_t moe_expert_bytes(const moe_dims_t *dims) {
+    if (check_dims_impl(dims) != MOE_OK) return 0;
+    return make_layout(dims->hidden, dims->ffn, dims->bits).bytes;
+}
+
+size_t moe_workspace_bytes(const moe_dims_t *dims, int32_t n_tokens) {
+    return workspace_bytes_checked(dims, n_tokens);
+}
+
+int moe_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
+    if (!workspace) return MOE_ERR_INVALID_ARG;
+    if (workspace_bytes < kCtrlBytes) return MOE_ERR_WORKSPACE;
+    if (!aligned(workspace, kAlign)) return MOE_ERR_ALIGNMENT;
+    return launch_clear_ctrl((uint32_t *)workspace, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_pack_expert(const moe_dims_t *dims, const uint8_t *const codes[3], const uint16_t *const scale[3],
+                    const uint16_t *const bias[3], void *dst, void *stream) {
+    int rc = check_dims_impl(dims);
+    if (rc != MOE_OK) return rc;
+    if (!codes || !scale || !bias || !dst) return MOE_ERR_INVALID_ARG;
+    PackArgs a;
+    for (int m = 0; m < 3; ++m) {
+        if (!codes[m] || !scale[m] || !bias[m]) return MOE_ERR_INVALID_ARG;
+        if (!aligned(scale[m], 2) || !aligned(bias[m], 2)) return MOE_ERR_ALIGNMENT;
+        a.codes[m] = codes[m];
+        a.scale[m] = scale[m];
+        a.bias[m] = bias[m];
+    }
+    if (!aligned(dst, kAlign)) return MOE_ERR_ALIGNMENT;
+    a.L = make_layout(dims->hidden, dims->ffn, dims->bits);
+    a.dst = (uint8_t *)dst;
+    return launch_pack(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_generate_layer(const moe_dims_t *dims, uint64_t seed, uint32_t layer, void *experts,
+                       void *shared_expert, void *stream) {
+    int rc = check_dims_impl(dims);
+    if (rc != MOE_OK) return rc;
+    if (!experts && !shared_expert) return MOE_ERR_INVALID_ARG;
+    if ((experts && !aligned(experts, kAlign)) || (shared_expert && !aligned(shared_expert, kAlign)))
+        return MOE_ERR_ALIGNMENT;
+    GenArgs a;
+    a.L = make_layout(dims->hidden, dims->ffn, dims->bits);
+    a.seed = seed;
+    a.layer = layer;
+    if (experts) {
+        a.first_expert = 0;
+        a.count = dims->n_experts;
+        a.dst = (uint8_t *)experts;
+        if (launch_generate(a, (hipStream_t)stream) != hipSuccess) return MOE_ERR_HIP;
+    }
+    if (shared_expert) {
+        a.first_expert = dims->n_experts;
+        a.count = 1;
+        a.dst = (uint8_t *)shared_expert;
+        if (launch_generate(a, (hipStream_t)stream) != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+}
+
+static FwdArgs make_fwd(const moe_dims_t *dims, const moe_layer_t *layer, const float *x, float *y, int T,
+                        int32_t *route_idx, float *route_w, void *workspace) {
+    FwdArgs a;
+    a.s = shape_of(dims);
+    a.L = make_layout(dims->hidden, dims->ffn, dims->bits);
+    a.gamma = layer->norm_weight;
+    a.router = layer->router_weight;
+    a.sgate = layer->shared_gate;
+    a.experts = (const uint8_t *)layer->experts;
+    a.shared = (const uint8_t *)layer->shared_expert;
+    a.x = x;
+    a.y = y;
+    a.T = T;
+    a.route_idx = route_idx;
+    a.route_w = route_w;
+    a.ws = carve_workspace(workspace, a.s, T);
+    return a;
+}
+
+int moe_layer_forward(const moe_dims_t *dims, const moe_layer_t *layer, const float *x, float *y,
+                      int32_t n_tokens, int32_t *route_idx, float *route_w, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    int rc = check_forward_common(dims, x, y, n_tokens, route_idx, route_w, workspace, workspace_bytes);
+    if (rc != MOE_OK) return rc;
+    rc = check_layer(layer);
+    if (rc != MOE_OK) return rc;
+    const FwdArgs a = make_fwd(dims, layer, x, y, n_tokens, route_idx, route_w, workspace);
+    return launch_forward(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_stack_forward(const moe_dims_t *dims, const moe_layer_t *layers, int32_t n_layers, const float *x,
+                      float *y, int32_t n_tokens, int32_t *route_idx, float *route_w, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    int rc = check_forward_common(dims, x, y, n_tokens, route_idx, route_w, workspace, workspace_bytes);
+    if (rc != MOE_OK) return rc;
+    if (!layers || n_layers < 1) return MOE_ERR_INVALID_ARG;
+    for (int l = 0; l < n_layers; ++l) {
+        rc = check_layer(&layers[l]);
+        if (rc != MOE_OK) return rc;
+    }
+    const size_t per_layer = (size_t)n_tokens * dims->top_k;
+    for (int l = 0; l < n_layers; ++l) {
+        const FwdArgs a = make_fwd(dims, &layers[l], l == 0 ? x : y, y, n_tokens,
+                                   route_idx ? route_idx + l * per_layer : nullptr,
+                                   route_w ? route_w + l * per_layer : nullptr, workspace);
+        if (launch_forward(a, (hipStream_t)stream) != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+}
+
+const char *moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or parameter";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_ALIGNMENT: return "misaligned pointer";
+        case MOE_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

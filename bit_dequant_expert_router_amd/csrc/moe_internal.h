@@ -1,0 +1,102 @@
+// moe_internal.h -- library-internal declarations shared by the ABI and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_layout.h"
+
+namespace moe {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kCtrlBytes = 256;
+
+MOE_HD size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+// Workspace of one forward call, carved from the caller's buffer.
+struct Workspace {
+    uint32_t *ctrl;  // control block (barrier counters), kCtrlBytes, zero between calls
+    float *h;        // [T][H]   normalised tokens
+    float *z;        // [T][E]   router logits
+    float *gs;       // [T]      shared-gate logits
+    int32_t *sel;    // [T][K]   selected experts
+    float *coef;     // [T][K+1] combine coefficients (renormalised weights, sigmoid(gs))
+    float *act;      // [T][K+1][F] SwiGLU activations of the selected experts and the shared one
+};
+
+struct Shape {
+    int H, F, E, K, bits;
+    float eps;
+};
+
+inline size_t workspace_bytes(const Shape &s, int T) {
+    size_t b = kCtrlBytes;
+    b += align_up((size_t)T * s.H * 4);
+    b += align_up((size_t)T * s.E * 4);
+    b += align_up((size_t)T * 4);
+    b += align_up((size_t)T * s.K * 4);
+    b += align_up((size_t)T * (s.K + 1) * 4);
+    b += align_up((size_t)T * (s.K + 1) * s.F * 4);
+    return b;
+}
+
+inline Workspace carve_workspace(void *base, const Shape &s, int T) {
+    char *p = (char *)base;
+    Workspace w;
+    w.ctrl = (uint32_t *)p;
+    p += kCtrlBytes;
+    w.h = (float *)p;
+    p += align_up((size_t)T * s.H * 4);
+    w.z = (float *)p;
+    p += align_up((size_t)T * s.E * 4);
+    w.gs = (float *)p;
+    p += align_up((size_t)T * 4);
+    w.sel = (int32_t *)p;
+    p += align_up((size_t)T * s.K * 4);
+    w.coef = (float *)p;
+    p += align_up((size_t)T * (s.K + 1) * 4);
+    w.act = (float *)p;
+    return w;
+}
+
+// Everything a forward launch needs (passed by value as a kernel argument).
+struct FwdArgs {
+    Shape s;
+    ExpertLayout L;
+    const uint16_t *gamma;
+    const uint16_t *router;
+    const uint16_t *sgate;
+    const uint8_t *experts;
+    const uint8_t *shared;
+    const float *x;
+    float *y;
+    int T;
+    int32_t *route_idx;
+    float *route_w;
+    Workspace ws;
+};
+
+hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
+
+struct PackArgs {
+    ExpertLayout L;
+    const uint8_t *codes[3];
+    const uint16_t *scale[3];
+    const uint16_t *bias[3];
+    uint8_t *dst;
+};
+hipError_t launch_pack(const PackArgs &a, hipStream_t stream);
+
+struct GenArgs {
+    ExpertLayout L;
+    uint64_t seed;
+    uint32_t layer;
+    int first_expert;  // expert index of dst's first expert (E = the shared expert)
+    int count;         // number of consecutive experts to write
+    uint8_t *dst;
+};
+hipError_t launch_generate(const GenArgs &a, hipStream_t stream);
+
+hipError_t launch_clear_ctrl(uint32_t *ctrl, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,187 @@
+/*
+ * moe.h -- C ABI of libmoe, an MI355X (gfx950) implementation of the
+ * Flash-MoE expert layer for decode.
+ *
+ * The layer (per token, per layer), as the pages describe it:
+ *   h   = RMSNorm(x)                        two passes: sum of squares, then scaling
+ *         ("48GB内存运行397B模型：Flash-Moe的极端量化与SSD流式加载实践", section
+ *          "Metal GPU管线：手写Kernel与FMA优化", RMS归一化)
+ *   z   = W_router h  over the experts; softmax; the top-K experts
+ *         (juejin post, "3. 流水线设计——严格串行反而更快": GPU routing, then top-K;
+ *          flash-moe README translation, "Pipeline mỗi lớp": softmax + topK routing)
+ *   for each selected expert and the shared expert:
+ *         a = silu(W_gate h) * (W_up h),  y = W_down a,
+ *         every weight w = code * scale + bias, computed as fma(code, scale*x, bias*x)
+ *         ("48GB内存运行397B模型", sections "量化策略" and "Metal GPU管线": 4-bit dequant
+ *          mat-vec with the FMA rewrite; Fused SwiGLU)
+ *   out = x + sum_k w_k y_k + sigmoid(g_s) y_shared,  g_s = w_sg . h
+ *         (same page, "Metal GPU管线": fused MoE combine + residual + sigmoid gate)
+ * 512 experts per layer, K = 4 active plus one shared expert, hidden 4096
+ * (same page, section "MoE稀疏架构").  The K selected probabilities are
+ * renormalised to sum to one.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device memory are HIP device pointers owned by the
+ *    caller; the library never allocates, frees or synchronises.  It keeps no
+ *    state between calls apart from the workspace the caller passes.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work; faults surface at the caller's next synchronisation.
+ *  - Arguments are checked on the host before anything is enqueued; a negative
+ *    moe_status_t is returned and nothing is launched.  The library never
+ *    aborts and never throws across this boundary.  A failed launch returns
+ *    MOE_ERR_HIP.
+ *  - Activations are fp32, [n_tokens][hidden] row-major.  bf16 tensors are
+ *    passed as their 16-bit patterns (uint16_t).
+ *  - Inputs are assumed finite; a NaN in x propagates to the outputs.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* NULL pointer, out-of-range size, bad dims   */
+    MOE_ERR_UNSUPPORTED = -2, /* valid in principle, not built (shape, bits) */
+    MOE_ERR_WORKSPACE = -3,   /* workspace smaller than moe_workspace_bytes   */
+    MOE_ERR_ALIGNMENT = -4,   /* pointer not aligned as documented            */
+    MOE_ERR_HIP = -5          /* a HIP launch or copy failed                  */
+} moe_status_t;
+
+/*
+ * Shape of one layer.
+ *   hidden      H, the token width (4096 in the pages' model)
+ *   ffn         F, the expert FFN width (1024)
+ *   n_experts   E, routed experts per layer (512), 1 <= E <= 1024
+ *   top_k       K, experts selected per token (4; the model's native 10), 1 <= K <= min(E, 16)
+ *   bits        2 or 4: width of a quantisation code
+ *   group_size  64: one bf16 scale and one bf16 bias per 64 consecutive
+ *               entries along a row's reduction axis
+ *   rms_eps     epsilon of the RMSNorm (1e-6)
+ * Built shapes: H and F powers of two in [128, 4096].  Other shapes return
+ * MOE_ERR_UNSUPPORTED.
+ */
+typedef struct moe_dims {
+    int32_t hidden;
+    int32_t ffn;
+    int32_t n_experts;
+    int32_t top_k;
+    int32_t bits;
+    int32_t group_size;
+    float rms_eps;
+} moe_dims_t;
+
+/*
+ * Weights of one layer (all device memory, 256-byte aligned).
+ *   norm_weight    bf16 [H]          RMSNorm weight gamma
+ *   router_weight  bf16 [E][H]       router matrix, row e gives logit e
+ *   shared_gate    bf16 [H]          sigmoid gate vector of the shared expert
+ *   experts        E packed experts, expert e at byte offset e * moe_expert_bytes()
+ *   shared_expert  one packed expert (the always-active shared expert)
+ * Packed experts are produced by moe_pack_expert or moe_generate_layer; their
+ * byte layout is private to the library.
+ */
+typedef struct moe_layer {
+    const uint16_t *norm_weight;
+    const uint16_t *router_weight;
+    const uint16_t *shared_gate;
+    const void *experts;
+    const void *shared_expert;
+} moe_layer_t;
+
+/* Returns MOE_OK if the library supports `dims`, else the status it would return. */
+int moe_check_dims(const moe_dims_t *dims);
+
+/*
+ * Bytes of one packed expert: codes of gate [F][H], up [F][H] and down [H][F]
+ * (bits/8 bytes per weight) plus a 4-byte bf16 scale+bias pair per group of 64:
+ *   3*H*F*bits/8 + 3*(H*F/64)*4.
+ * 7,077,888 B (6.75 MiB) at H=4096, F=1024, 4-bit -- the pages' "about 6.75MB per
+ * expert, 27MB for K=4" ("48GB内存运行397B模型", section "MoE稀疏架构").
+ * Returns 0 for unsupported dims.
+ */
+size_t moe_expert_bytes(const moe_dims_t *dims);
+
+/*
+ * Bytes of workspace a forward call with up to n_tokens tokens needs (the same
+ * for moe_layer_forward and moe_stack_forward).  Returns 0 for unsupported dims
+ * or n_tokens < 1.
+ */
+size_t moe_workspace_bytes(const moe_dims_t *dims, int32_t n_tokens);
+
+/*
+ * Zero the workspace's control block (device memory, >= 256 B, 256-B aligned).
+ * Needed once, before the first forward call on a new workspace; every forward
+ * call leaves the control block zero again.  Enqueued on `stream`.
+ */
+int moe_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Pack one expert from canonical tensors (all device memory):
+ *   codes[m]  uint8 [rows][cols], one code per byte, each < 2^bits
+ *   scale[m]  bf16  [rows][cols/64]
+ *   bias[m]   bf16  [rows][cols/64]
+ * for m = 0 gate [F][H], 1 up [F][H], 2 down [H][F] (row = output index,
+ * column = reduction index).  dst: moe_expert_bytes() bytes of device memory,
+ * 256-byte aligned.  Codes >= 2^bits are masked to their low `bits` bits.
+ */
+int moe_pack_expert(const moe_dims_t *dims, const uint8_t *const codes[3],
+                    const uint16_t *const scale[3], const uint16_t *const bias[3], void *dst,
+                    void *stream);
+
+/*
+ * Generate the packed synthetic experts of one layer on the device from a
+ * seed: codes uniform in [0, 2^bits), scales uniform in [0.005, 0.02), biases
+ * uniform in [-0.1, 0), all drawn from counter-based SplitMix64 streams keyed by
+ * (seed, layer, expert, matrix, kind).  The result equals moe_pack_expert of the
+ * canonical tensors that the same streams define (the stream definition is
+ * stated in the library's DESIGN notes and in the generator's source).
+ *   experts        E packed experts (NULL: skip), shared_expert: 1 (NULL: skip).
+ */
+int moe_generate_layer(const moe_dims_t *dims, uint64_t seed, uint32_t layer, void *experts,
+                       void *shared_expert, void *stream);
+
+/*
+ * One MoE layer for n_tokens tokens.
+ *   x          fp32 [n_tokens][H] device, 16-B aligned (may equal y: in place)
+ *   y          fp32 [n_tokens][H] device, 16-B aligned: x + routed combine + gated shared
+ *   route_idx  int32 [n_tokens][K] device or NULL: selected experts, ordered by
+ *              (logit descending, expert index ascending)
+ *   route_w    fp32 [n_tokens][K] device or NULL: renormalised weights (sum 1)
+ *   workspace  device, 256-B aligned, >= moe_workspace_bytes(dims, n_tokens),
+ *              control block zeroed once by moe_workspace_init.
+ * Calls that share one workspace must be ordered (same stream); calls on
+ * different streams need different workspaces.
+ */
+int moe_layer_forward(const moe_dims_t *dims, const moe_layer_t *layer, const float *x, float *y,
+                      int32_t n_tokens, int32_t *route_idx, float *route_w, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
+ * n_layers layers chained: x_{l+1} = layer_l(x_l), x_0 = x, y = x_{n_layers}
+ * (no final norm).  `layers` is a HOST array of n_layers layer descriptors.
+ * route_idx / route_w (device or NULL): [n_layers][n_tokens][K].
+ * Every layer is enqueued back to back on `stream`; nothing waits on the host.
+ */
+int moe_stack_forward(const moe_dims_t *dims, const moe_layer_t *layers, int32_t n_layers,
+                      const float *x, float *y, int32_t n_tokens, int32_t *route_idx,
+                      float *route_w, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *moe_status_string(int status);
+
+/* MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,76 @@
+"""Helpers of the GPU parity tests: run the C ABI on synthetic inputs and
+compare with the fp64 oracle."""
+from __future__ import annotations
+
+import functools
+import sys
+from typing import Dict, List, Optional
+
+import numpy as np
+
+import oracle
+import synthetic as syn
+
+# tolerances on the layer outputs (fp32 accumulation against an fp64 oracle)
+REL_L2 = 1e-4
+MAX_ABS = 1e-3
+W_ABS = 2e-6  # renormalised routing weights
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=64)
+def canon_expert(seed: int, layer: int, e: int, dims: syn.Dims):
+    return syn.expert_canonical(seed, layer, e, dims)
+
+
+@functools.lru_cache(maxsize=64)
+def dense_layer(seed: int, layer: int, dims: syn.Dims):
+    return syn.layer_dense(seed, layer, dims)
+
+
+def run_layer(dims, lw, x: np.ndarray, inplace: bool = False, want_route: bool = True):
+    import torch
+    import bit_dequant_expert_router_amd as moe
+    T = x.shape[0]
+    xt = torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+    yt = xt if inplace else torch.empty_like(xt)
+    ridx = torch.full((T, dims.top_k), -1, dtype=torch.int32, device="cuda") if want_route else None
+    rw = torch.full((T, dims.top_k), -1.0, dtype=torch.float32, device="cuda") if want_route else None
+    ws = torch.empty(moe.moe_workspace_bytes(dims, T), dtype=torch.uint8, device="cuda")
+    moe.moe_workspace_init(ws)
+    moe.moe_layer_forward(dims, lw.descriptor(), xt, yt, T, ridx, rw, ws)
+    torch.cuda.synchronize()
+    return (yt.cpu().numpy(), ridx.cpu().numpy() if want_route else None,
+            rw.cpu().numpy() if want_route else None)
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def check_token(out, idx, w, ref: Dict, K: int, what: str = "") -> bool:
+    """Asserts parity of one token; returns False when the routing is a near tie
+    that the GPU resolved differently (then outputs are not compared)."""
+    ref_idx = [int(v) for v in ref["idx"]]
+    if idx is not None and list(idx) != ref_idx:
+        assert oracle.near_tie(ref["z"], K), f"{what}: routed experts {list(idx)} != oracle {ref_idx}"
+        log(f"{what}: near tie, GPU chose {list(idx)}, oracle {ref_idx}")
+        return False
+    if w is not None:
+        assert np.max(np.abs(np.asarray(w, np.float64) - ref["w"])) <= W_ABS, f"{what}: weights {w} vs {ref['w']}"
+        assert abs(float(np.sum(w, dtype=np.float64)) - 1.0) <= 1e-6
+    e2 = rel_l2(out, ref["out"])
+    ea = float(np.max(np.abs(np.asarray(out, np.float64) - ref["out"])))
+    assert e2 <= REL_L2 and ea <= MAX_ABS, f"{what}: rel-L2 {e2:.3e}, max-abs {ea:.3e}"
+    return True
+
+
+def oracle_layer_generated(dims, seed: int, layer: int, x: np.ndarray):
+    dense = dense_layer(seed, layer, dims)
+    return oracle.layer(dims, x, dense, lambda e: canon_expert(seed, layer, e, dims))

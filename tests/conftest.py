@@ -10,3 +10,21 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+def _ensure_built():
+    """Build what is missing (only then): the C oracle and libmoe.so."""
+    import importlib.util
+    lib = os.path.join(ROOT, "bit_dequant_expert_router_amd", "libmoe.so")
+    if not os.path.exists(lib):
+        spec = importlib.util.spec_from_file_location(
+            "_moe_build", os.path.join(ROOT, "bit_dequant_expert_router_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    if not os.path.exists(os.path.join(ROOT, "oracle", "liboracle.so")):
+        import oracle
+        oracle.build()
+
+
+_ensure_built()

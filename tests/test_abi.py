@@ -1,0 +1,189 @@
+"""Host-side contract of the C ABI (no GPU needed): the library loads, exports
+every entry point the header declares, sizes match the closed forms, and every
+invalid argument is rejected with its documented status before anything is
+enqueued."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import bit_dequant_expert_router_amd as moe
+import synthetic as syn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+    assert set(moe.EXPORTED) == set(names)
+    assert moe.moe_abi_version() == 1
+
+
+def d(**kw):
+    base = dict(hidden=4096, ffn=1024, n_experts=512, top_k=4, bits=4)
+    base.update(kw)
+    return moe.make_dims(**base)
+
+
+def _gold(name):
+    with open(os.path.join(ROOT, "tests", "golden", name)) as f:
+        return {ln.split()[0]: float(ln.split()[1]) for ln in f if ln.strip() and not ln.startswith("#")}
+
+
+def test_expert_bytes_closed_form_and_pages():
+    for H, F, bits in ((4096, 1024, 4), (4096, 1024, 2), (256, 128, 4), (1024, 4096, 4), (128, 128, 2)):
+        closed = 3 * H * F * bits // 8 + 3 * (H * F // 64) * 4
+        assert moe.moe_expert_bytes(d(hidden=H, ffn=F, bits=bits)) == closed
+    assert moe.moe_expert_bytes(d()) == 7_077_888
+    assert moe.moe_expert_bytes(d(bits=2)) == 3_932_160
+    assert moe.moe_expert_bytes(syn.WORKLOADS["tiny"].dims) == 55_296
+    g = _gold("page_sizes.txt")
+    mib = 1 << 20
+    assert moe.moe_expert_bytes(d()) == g["expert_4bit"] * mib
+    assert 4 * moe.moe_expert_bytes(d()) == g["layer_k4_4bit"] * mib
+    assert abs(moe.moe_expert_bytes(d()) / 1e6 - g["blit_4x"]) < 0.1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=3), moe.MOE_ERR_UNSUPPORTED),
+    (dict(bits=8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(bits=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(bits=9), moe.MOE_ERR_INVALID_ARG),
+    (dict(group_size=32), moe.MOE_ERR_UNSUPPORTED),
+    (dict(group_size=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(hidden=4000), moe.MOE_ERR_INVALID_ARG),
+    (dict(ffn=1000), moe.MOE_ERR_INVALID_ARG),
+    (dict(hidden=3072), moe.MOE_ERR_UNSUPPORTED),
+    (dict(hidden=8192), moe.MOE_ERR_UNSUPPORTED),
+    (dict(hidden=64), moe.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(top_k=513), moe.MOE_ERR_INVALID_ARG),
+    (dict(top_k=17), moe.MOE_ERR_UNSUPPORTED),
+    (dict(n_experts=2048), moe.MOE_ERR_UNSUPPORTED),
+    (dict(n_experts=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(rms_eps=-1.0), moe.MOE_ERR_INVALID_ARG),
+    (dict(rms_eps=float("nan")), moe.MOE_ERR_INVALID_ARG),
+    (dict(rms_eps=float("inf")), moe.MOE_ERR_INVALID_ARG),
+])
+def test_check_dims_errors(kw, status):
+    assert moe.moe_check_dims(d(**kw)) == status
+    assert moe.moe_expert_bytes(d(**kw)) == 0
+    assert moe.moe_workspace_bytes(d(**kw), 1) == 0
+
+
+def test_valid_dims():
+    for w in syn.WORKLOADS.values():
+        assert moe.moe_check_dims(w.dims) == moe.MOE_OK
+    assert moe.moe_check_dims(d(top_k=16, n_experts=16, hidden=128, ffn=4096, bits=2)) == moe.MOE_OK
+    assert moe._lib.moe_check_dims(None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_bytes_monotone():
+    prev = 0
+    for T in (1, 2, 3, 8, 32, 100):
+        b = moe.moe_workspace_bytes(d(), T)
+        assert b > prev and b % 256 == 0
+        prev = b
+    assert moe.moe_workspace_bytes(d(), 0) == 0
+
+
+# fake, never-dereferenced device addresses: every call below must fail validation
+A = 1 << 40
+
+
+def _layer(**kw):
+    f = dict(norm_weight=A, router_weight=A + 0x10000, shared_gate=A + 0x20000, experts=A + 0x100000,
+             shared_expert=A + 0x200000)
+    f.update(kw)
+    return moe.moe_layer_t(*[f[k] for k in ("norm_weight", "router_weight", "shared_gate", "experts",
+                                            "shared_expert")])
+
+
+def _fwd(dims=None, layer=None, x=A + 0x300000, y=A + 0x400000, T=1, ridx=None, rw=None, ws=A + 0x500000,
+         wsb=None):
+    dims = dims or d()
+    layer = layer if layer is not None else _layer()
+    if wsb is None:
+        wsb = moe.moe_workspace_bytes(dims, max(T, 1))
+    return moe._lib.moe_layer_forward(ctypes.byref(dims), ctypes.byref(layer) if layer else None, x, y, T, ridx,
+                                      rw, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dims=d(bits=3)), moe.MOE_ERR_UNSUPPORTED),
+    (dict(x=None), moe.MOE_ERR_INVALID_ARG),
+    (dict(y=None), moe.MOE_ERR_INVALID_ARG),
+    (dict(ws=None), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=-3), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=70000), moe.MOE_ERR_INVALID_ARG),
+    (dict(x=A + 0x300004), moe.MOE_ERR_ALIGNMENT),
+    (dict(y=A + 0x400008), moe.MOE_ERR_ALIGNMENT),
+    (dict(ws=A + 0x500010), moe.MOE_ERR_ALIGNMENT),
+    (dict(ridx=A + 0x600002), moe.MOE_ERR_ALIGNMENT),
+    (dict(wsb=1024), moe.MOE_ERR_WORKSPACE),
+    (dict(y=A + 0x300000 + 4096), moe.MOE_ERR_INVALID_ARG),  # partial overlap of x and y
+    (dict(layer=False), moe.MOE_ERR_INVALID_ARG),
+    (dict(layer=_layer(experts=None)), moe.MOE_ERR_INVALID_ARG),
+    (dict(layer=_layer(norm_weight=None)), moe.MOE_ERR_INVALID_ARG),
+    (dict(layer=_layer(shared_expert=A + 0x200040)), moe.MOE_ERR_ALIGNMENT),
+    (dict(layer=_layer(router_weight=A + 0x10002)), moe.MOE_ERR_ALIGNMENT),
+])
+def test_forward_rejects(kw, status):
+    if kw.get("layer") is False:
+        kw = dict(kw, layer=None)
+        dims = d()
+        rc = moe._lib.moe_layer_forward(ctypes.byref(dims), None, A + 0x300000, A + 0x400000, 1, None, None,
+                                        A + 0x500000, moe.moe_workspace_bytes(dims, 1), None)
+        assert rc == status
+        return
+    assert _fwd(**kw) == status
+
+
+def test_stack_rejects():
+    dims = d()
+    lay = (moe.moe_layer_t * 2)(_layer(), _layer(experts=None))
+    wsb = moe.moe_workspace_bytes(dims, 1)
+    f = moe._lib.moe_stack_forward
+    assert f(ctypes.byref(dims), lay, 2, A, A + 0x400000, 1, None, None, A + 0x500000, wsb, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(dims), lay, 0, A, A + 0x400000, 1, None, None, A + 0x500000, wsb, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(dims), None, 1, A, A + 0x400000, 1, None, None, A + 0x500000, wsb, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(dims), lay, 1, A, A + 0x400000, 1, None, None, A + 0x500000, 16, None) == moe.MOE_ERR_WORKSPACE
+
+
+def test_pack_generate_init_reject():
+    dims = d()
+    P = moe._vp * 3
+    ok3 = P(A, A + 0x1000, A + 0x2000)
+    bad3 = P(A, None, A + 0x2000)
+    f = moe._lib.moe_pack_expert
+    assert f(ctypes.byref(dims), bad3, ok3, ok3, A + 0x100000, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(dims), ok3, ok3, ok3, A + 0x100010, None) == moe.MOE_ERR_ALIGNMENT
+    assert f(ctypes.byref(d(bits=3)), ok3, ok3, ok3, A + 0x100000, None) == moe.MOE_ERR_UNSUPPORTED
+    g = moe._lib.moe_generate_layer
+    assert g(ctypes.byref(dims), 0, 0, None, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert g(ctypes.byref(dims), 0, 0, A + 0x80, None, None) == moe.MOE_ERR_ALIGNMENT
+    i = moe._lib.moe_workspace_init
+    assert i(None, 4096, None) == moe.MOE_ERR_INVALID_ARG
+    assert i(A, 16, None) == moe.MOE_ERR_WORKSPACE
+    assert i(A + 8, 4096, None) == moe.MOE_ERR_ALIGNMENT
+
+
+def test_status_strings():
+    for s in range(0, -6, -1):
+        assert moe.moe_status_string(s) not in ("", "unknown status")
+    assert moe.moe_status_string(-99) == "unknown status"

@@ -1,0 +1,212 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Routed expert indices must match exactly (unless the oracle's logits have a
+near tie at the K-th place, then either choice is accepted and logged);
+outputs within rel-L2 1e-4 and max-abs 1e-3; routing weights within 2e-6.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as syn
+
+from _parity import (canon_expert, check_token, dense_layer, log, oracle_layer_generated, rel_l2,
+                     run_layer)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_dequant_expert_router_amd as m
+    return m
+
+
+def _canonical_layer(dims, seed=0, layer=0):
+    from bit_dequant_expert_router_amd.weights import layer_from_canonical
+    dense = syn.layer_dense(seed, layer, dims)
+    experts = [syn.expert_canonical(seed, layer, e, dims) for e in range(dims.n_experts + 1)]
+    return dense, experts, layer_from_canonical(dims, dense, experts)
+
+
+# --------------------------------------------------------------------------- #
+# tiny layer and small shapes: every expert packed from canonical tensors
+# --------------------------------------------------------------------------- #
+def test_tiny_layer(moe):
+    w = syn.WORKLOADS["tiny"]
+    dims = w.dims
+    log(f"tiny: {dims}")
+    dense, experts, lw = _canonical_layer(dims)
+    x = syn.tokens(0, 19, dims.hidden)  # a ragged batch, plus single-token calls
+    out, idx, wt = run_layer(dims, lw, x)
+    for t in range(x.shape[0]):
+        ref = oracle.layer_all(dims, x[t], dense, experts)
+        check_token(out[t], idx[t], wt[t], ref, dims.top_k, f"tiny token {t}")
+    for t in (0, 7):
+        o1, i1, w1 = run_layer(dims, lw, x[t:t + 1])
+        assert np.array_equal(o1[0], out[t]) and np.array_equal(i1[0], idx[t])
+
+
+SMALL_SHAPES = [
+    # hidden, ffn, experts, top_k, bits
+    (128, 128, 4, 1, 4),
+    (128, 256, 16, 16, 2),
+    (512, 128, 8, 8, 4),
+    (256, 4096, 3, 2, 2),
+    (4096, 128, 5, 3, 4),
+    (1024, 2048, 7, 7, 2),
+    (2048, 512, 33, 5, 4),
+    (256, 256, 1, 1, 2),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_small_shapes(moe, shape):
+    H, F, E, K, bits = shape
+    dims = syn.Dims(H, F, E, K, bits)
+    log(f"small shape {shape}")
+    dense, experts, lw = _canonical_layer(dims, seed=3, layer=1)
+    x = syn.tokens(3, 5, H)
+    out, idx, wt = run_layer(dims, lw, x)
+    for t in range(x.shape[0]):
+        ref = oracle.layer_all(dims, x[t], dense, experts)
+        check_token(out[t], idx[t], wt[t], ref, K, f"{shape} token {t}")
+
+
+def test_inplace_determinism_and_optional_outputs(moe):
+    dims = syn.WORKLOADS["tiny"].dims
+    log("tiny: in place / determinism")
+    dense, experts, lw = _canonical_layer(dims)
+    x = syn.tokens(1, 6, dims.hidden)
+    a, ia, wa = run_layer(dims, lw, x)
+    b, ib, wb = run_layer(dims, lw, x)
+    c, _, _ = run_layer(dims, lw, x, inplace=True)
+    d, _, _ = run_layer(dims, lw, x, want_route=False)
+    assert np.array_equal(a, b) and np.array_equal(ia, ib) and np.array_equal(wa, wb)
+    assert np.array_equal(a, c) and np.array_equal(a, d)
+
+
+def test_zero_router_selects_first_experts(moe):
+    """All-zero router: every logit is 0, so experts 0..K-1 with weight 1/K."""
+    dims = syn.WORKLOADS["tiny"].dims
+    dense, experts, lw = _canonical_layer(dims)
+    lw.router_weight.zero_()
+    x = syn.tokens(2, 3, dims.hidden)
+    out, idx, wt = run_layer(dims, lw, x)
+    assert (idx == np.arange(dims.top_k)).all() and np.all(wt == np.float32(1.0 / dims.top_k))
+    dense0 = dict(dense, router_weight=np.zeros_like(dense["router_weight"]))
+    for t in range(3):
+        check_token(out[t], idx[t], wt[t], oracle.layer_all(dims, x[t], dense0, experts), dims.top_k)
+
+
+# --------------------------------------------------------------------------- #
+# device generator == packing of the canonical tensors the stream defines
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("name", ["tiny", "layer4", "layer2"])
+def test_generated_equals_packed(moe, name):
+    from bit_dequant_expert_router_amd.weights import LayerWeights
+    dims = syn.WORKLOADS[name].dims
+    log(f"generator vs packer: {name}")
+    gen = LayerWeights(dims, dense_layer(0, 5, dims))
+    gen.generate(0, 5)
+    probe = LayerWeights(syn.Dims(dims.hidden, dims.ffn, 1, 1, dims.bits), dense_layer(0, 5, dims))
+    for e in sorted({0, 1, dims.n_experts // 2, dims.n_experts - 1, dims.n_experts}):
+        probe.pack(0, canon_expert(0, 5, e, dims))
+        torch.cuda.synchronize()
+        assert torch.equal(gen.expert_view(e), probe.expert_view(0)), f"expert {e}"
+
+
+# --------------------------------------------------------------------------- #
+# full-size single layers (4-bit and 2-bit), device-generated experts
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("name", ["layer4", "layer2"])
+def test_full_layer(moe, name):
+    from bit_dequant_expert_router_amd.weights import layer_generated
+    w = syn.WORKLOADS[name]
+    dims = w.dims
+    log(f"full layer {name}: {dims}")
+    lw = layer_generated(dims, dense_layer(w.seed, 0, dims), w.seed, 0)
+    x = syn.tokens(w.seed, 6, dims.hidden)
+    out_b, idx_b, w_b = run_layer(dims, lw, x)  # one call with 6 tokens
+    for t in range(x.shape[0]):
+        out1, idx1, w1 = run_layer(dims, lw, x[t:t + 1])  # the bench's single-token call
+        ref = oracle_layer_generated(dims, w.seed, 0, x[t])
+        check_token(out1[0], idx1[0], w1[0], ref, dims.top_k, f"{name} token {t}")
+        check_token(out_b[t], idx_b[t], w_b[t], ref, dims.top_k, f"{name} batched token {t}")
+
+
+# --------------------------------------------------------------------------- #
+# batched decode: 32 tokens, top-10 + shared
+# --------------------------------------------------------------------------- #
+def test_batch32(moe):
+    from bit_dequant_expert_router_amd.weights import layer_generated
+    w = syn.WORKLOADS["batch32"]
+    dims = w.dims
+    log(f"batch32: {dims}")
+    lw = layer_generated(dims, dense_layer(w.seed, 0, dims), w.seed, 0)
+    x = syn.tokens(w.seed, 32, dims.hidden)
+    out, idx, wt = run_layer(dims, lw, x)
+    for t in range(32):
+        ref = oracle_layer_generated(dims, w.seed, 0, x[t])
+        check_token(out[t], idx[t], wt[t], ref, dims.top_k, f"batch32 token {t}")
+
+
+# --------------------------------------------------------------------------- #
+# stacks: free-running and teacher-forced against the oracle
+# --------------------------------------------------------------------------- #
+def _stack(moe, n_layers, n_check_tokens=1):
+    from bit_dequant_expert_router_amd.weights import layer_generated
+    w = syn.WORKLOADS["stack60"]
+    dims = w.dims
+    log(f"stack of {n_layers} layers: generating")
+    layers = [layer_generated(dims, dense_layer(w.seed, l, dims), w.seed, l) for l in range(n_layers)]
+    torch.cuda.synchronize()
+    x = syn.tokens(w.seed, n_check_tokens, dims.hidden)
+    T = x.shape[0]
+    xt = torch.from_numpy(x).cuda()
+    yt = torch.empty_like(xt)
+    K = dims.top_k
+    ridx = torch.empty((n_layers, T, K), dtype=torch.int32, device="cuda")
+    rw = torch.empty((n_layers, T, K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_workspace_bytes(dims, T), dtype=torch.uint8, device="cuda")
+    moe.moe_workspace_init(ws)
+    log(f"stack of {n_layers} layers: forward")
+    moe.moe_stack_forward(dims, [l.descriptor() for l in layers], xt, yt, T, ridx, rw, ws)
+    torch.cuda.synchronize()
+    y = yt.cpu().numpy()
+    ridx = ridx.cpu().numpy()
+    rw = rw.cpu().numpy()
+    # per-layer GPU states, by single-layer calls (teacher forcing)
+    for t in range(T):
+        xo = x[t].astype(np.float32)  # oracle, free running
+        xg = x[t].astype(np.float32)  # GPU state fed to each oracle layer
+        free_ok = True
+        for l in range(n_layers):
+            ref_tf = oracle_layer_generated(dims, w.seed, l, xg)
+            og, ig, wg = run_layer(dims, layers[l], xg[None])
+            check_token(og[0], ig[0], wg[0], ref_tf, K, f"stack layer {l} (teacher-forced)")
+            if free_ok:
+                ref_fr = oracle_layer_generated(dims, w.seed, l, xo)
+                if list(ref_fr["idx"]) != list(ridx[l, t]):
+                    assert oracle.near_tie(ref_fr["z"], K), f"layer {l}: {ridx[l, t]} vs {ref_fr['idx']}"
+                    free_ok = False
+                xo = ref_fr["out"].astype(np.float32)
+            xg = og[0]
+        assert np.array_equal(xg, y[t]), "stack call and chained layer calls differ"
+        if free_ok:
+            e2 = rel_l2(y[t], ref_fr["out"])
+            ea = float(np.max(np.abs(y[t] - ref_fr["out"])))
+            log(f"stack free-running: rel-L2 {e2:.2e}, max-abs {ea:.2e}, |y| max {np.abs(y[t]).max():.1f}")
+            assert e2 <= 1e-4 and ea <= 1e-3
+
+
+def test_stack_4_layers(moe):
+    _stack(moe, 4)
+
+
+def test_stack_60_layers(moe):
+    _stack(moe, 60)
