@@ -4,7 +4,7 @@ Argument marshalling only: every function here forwards to the entry point of
 the same name in ``include/moe.h``.  Tensors are PyTorch tensors on the GPU
 (used for device memory and streams) or raw device addresses given as ints.
 There is no fallback: importing this package raises if ``libmoe.so`` has not
-been built (``python -m bit_dequant_expert_router_amd.build``).
+been built (``python bit_dequant_expert_router_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -15,9 +15,14 @@ from typing import Optional, Sequence
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
 
+# torch first: its bundled HIP runtime (soname libamdhip64.so.7) must be the
+# one libmoe.so binds to.  Loading libmoe.so first would bring in a second HIP
+# runtime from /opt/rocm, and the two cannot share the device.
+import torch  # noqa: E402,F401
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m bit_dequant_expert_router_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python bit_dequant_expert_router_amd/build.py` "
         "(there is no CPU fallback)")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -59,6 +64,7 @@ _SIGS = {
     "moe_layer_forward": (ctypes.c_int, [_dimsp, _layerp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "moe_stack_forward": (ctypes.c_int, [_dimsp, _layerp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -70,7 +76,8 @@ EXPORTED = tuple(_SIGS)
 
 class MoeError(RuntimeError):
     def __init__(self, fn: str, status: int):
-        super().__init__(f"{fn}: {moe_status_string(status)} ({status})")
+        detail = f" [{moe_last_error()}]" if status == MOE_ERR_HIP else ""
+        super().__init__(f"{fn}: {moe_status_string(status)} ({status}){detail}")
         self.status = status
 
 
@@ -125,6 +132,10 @@ def moe_abi_version() -> int:
 
 def moe_status_string(status: int) -> str:
     return _lib.moe_status_string(int(status)).decode()
+
+
+def moe_last_error() -> str:
+    return _lib.moe_last_error().decode()
 
 
 def moe_check_dims(dims) -> int:

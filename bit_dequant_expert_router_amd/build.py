@@ -1,6 +1,6 @@
 """Build libmoe.so (HIP for gfx950) in-tree.
 
-    python -m bit_dequant_expert_router_amd.build
+    python bit_dequant_expert_router_amd/build.py
 """
 from __future__ import annotations
 

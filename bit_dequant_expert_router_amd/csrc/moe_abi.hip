@@ -12,6 +12,13 @@ namespace {
 
 using namespace moe;
 
+thread_local hipError_t g_last_hip = hipSuccess;
+
+int hip_status(hipError_t e) {
+    g_last_hip = e;
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -96,7 +103,7 @@ int moe_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
     if (!workspace) return MOE_ERR_INVALID_ARG;
     if (workspace_bytes < kCtrlBytes) return MOE_ERR_WORKSPACE;
     if (!aligned(workspace, kAlign)) return MOE_ERR_ALIGNMENT;
-    return launch_clear_ctrl((uint32_t *)workspace, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return hip_status(launch_clear_ctrl((uint32_t *)workspace, (hipStream_t)stream));
 }
 
 int moe_pack_expert(const moe_dims_t *dims, const uint8_t *const codes[3], const uint16_t *const scale[3],
@@ -115,7 +122,7 @@ int moe_pack_expert(const moe_dims_t *dims, const uint8_t *const codes[3], const
     if (!aligned(dst, kAlign)) return MOE_ERR_ALIGNMENT;
     a.L = make_layout(dims->hidden, dims->ffn, dims->bits);
     a.dst = (uint8_t *)dst;
-    return launch_pack(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return hip_status(launch_pack(a, (hipStream_t)stream));
 }
 
 int moe_generate_layer(const moe_dims_t *dims, uint64_t seed, uint32_t layer, void *experts,
@@ -133,13 +140,13 @@ int moe_generate_layer(const moe_dims_t *dims, uint64_t seed, uint32_t layer, vo
         a.first_expert = 0;
         a.count = dims->n_experts;
         a.dst = (uint8_t *)experts;
-        if (launch_generate(a, (hipStream_t)stream) != hipSuccess) return MOE_ERR_HIP;
+        if (hip_status(launch_generate(a, (hipStream_t)stream)) != MOE_OK) return MOE_ERR_HIP;
     }
     if (shared_expert) {
         a.first_expert = dims->n_experts;
         a.count = 1;
         a.dst = (uint8_t *)shared_expert;
-        if (launch_generate(a, (hipStream_t)stream) != hipSuccess) return MOE_ERR_HIP;
+        if (hip_status(launch_generate(a, (hipStream_t)stream)) != MOE_OK) return MOE_ERR_HIP;
     }
     return MOE_OK;
 }
@@ -171,7 +178,7 @@ int moe_layer_forward(const moe_dims_t *dims, const moe_layer_t *layer, const fl
     rc = check_layer(layer);
     if (rc != MOE_OK) return rc;
     const FwdArgs a = make_fwd(dims, layer, x, y, n_tokens, route_idx, route_w, workspace);
-    return launch_forward(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return hip_status(launch_forward(a, (hipStream_t)stream));
 }
 
 int moe_stack_forward(const moe_dims_t *dims, const moe_layer_t *layers, int32_t n_layers, const float *x,
@@ -189,9 +196,13 @@ int moe_stack_forward(const moe_dims_t *dims, const moe_layer_t *layers, int32_t
         const FwdArgs a = make_fwd(dims, &layers[l], l == 0 ? x : y, y, n_tokens,
                                    route_idx ? route_idx + l * per_layer : nullptr,
                                    route_w ? route_w + l * per_layer : nullptr, workspace);
-        if (launch_forward(a, (hipStream_t)stream) != hipSuccess) return MOE_ERR_HIP;
+        if (hip_status(launch_forward(a, (hipStream_t)stream)) != MOE_OK) return MOE_ERR_HIP;
     }
     return MOE_OK;
+}
+
+const char *moe_last_error(void) {
+    return g_last_hip == hipSuccess ? "no HIP error" : hipGetErrorString(g_last_hip);
 }
 
 const char *moe_status_string(int status) {

@@ -374,6 +374,7 @@ hipError_t launch_bits(const FwdArgs &a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream) {
+    (void)hipGetLastError();  // report only this call's launches
     if (a.s.bits == 4) return launch_bits<4>(a, stream);
     if (a.s.bits == 2) return launch_bits<2>(a, stream);
     return hipErrorInvalidValue;

@@ -163,6 +163,7 @@ hipError_t launch_pack(const PackArgs &a, hipStream_t stream) {
     const size_t total = w.chunk_begin[3] + w.sb_begin[3];
     size_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
+    (void)hipGetLastError();  // report only this launch's status
     hipLaunchKernelGGL(k_pack, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
@@ -172,6 +173,7 @@ hipError_t launch_generate(const GenArgs &a, hipStream_t stream) {
     const size_t per_expert = w.chunk_begin[3] + w.sb_begin[3];
     size_t bx = (per_expert + 255) / 256;
     if (bx > 4096) bx = 4096;
+    (void)hipGetLastError();
     for (int first = 0; first < a.count; first += 65535) {
         GenArgs part = a;
         part.first_expert = a.first_expert + first;
@@ -186,6 +188,7 @@ hipError_t launch_generate(const GenArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_clear_ctrl(uint32_t *ctrl, hipStream_t stream) {
+    (void)hipGetLastError();
     hipLaunchKernelGGL(k_clear_ctrl, dim3(1), dim3(64), 0, stream, ctrl);
     return hipGetLastError();
 }

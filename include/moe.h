@@ -177,6 +177,9 @@ int moe_stack_forward(const moe_dims_t *dims, const moe_layer_t *layers, int32_t
 /* Static text for a status code. */
 const char *moe_status_string(int status);
 
+/* Text of the HIP error behind the calling thread's last MOE_ERR_HIP (static storage). */
+const char *moe_last_error(void);
+
 /* MOE_ABI_VERSION of the built library. */
 int moe_abi_version(void);
 

@@ -54,9 +54,14 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
-def check_token(out, idx, w, ref: Dict, K: int, what: str = "") -> bool:
+def check_token(out, idx, w, ref: Dict, K: int, what: str = "", unit_scale: bool = False) -> bool:
     """Asserts parity of one token; returns False when the routing is a near tie
-    that the GPU resolved differently (then outputs are not compared)."""
+    that the GPU resolved differently (then outputs are not compared).
+
+    unit_scale: apply the max-abs bound to the output normalised to unit RMS
+    (|d|max <= 1e-3 * max(1, rms(ref))).  Used for chained layers, whose
+    residual stream grows far beyond the range where an absolute 1e-3 is
+    representable in fp32."""
     ref_idx = [int(v) for v in ref["idx"]]
     if idx is not None and list(idx) != ref_idx:
         assert oracle.near_tie(ref["z"], K), f"{what}: routed experts {list(idx)} != oracle {ref_idx}"
@@ -67,7 +72,8 @@ def check_token(out, idx, w, ref: Dict, K: int, what: str = "") -> bool:
         assert abs(float(np.sum(w, dtype=np.float64)) - 1.0) <= 1e-6
     e2 = rel_l2(out, ref["out"])
     ea = float(np.max(np.abs(np.asarray(out, np.float64) - ref["out"])))
-    assert e2 <= REL_L2 and ea <= MAX_ABS, f"{what}: rel-L2 {e2:.3e}, max-abs {ea:.3e}"
+    scale = max(1.0, float(np.sqrt(np.mean(np.square(ref["out"]))))) if unit_scale else 1.0
+    assert e2 <= REL_L2 and ea <= MAX_ABS * scale, f"{what}: rel-L2 {e2:.3e}, max-abs {ea:.3e} (scale {scale:.3g})"
     return True
 
 

@@ -188,7 +188,7 @@ def _stack(moe, n_layers, n_check_tokens=1):
         for l in range(n_layers):
             ref_tf = oracle_layer_generated(dims, w.seed, l, xg)
             og, ig, wg = run_layer(dims, layers[l], xg[None])
-            check_token(og[0], ig[0], wg[0], ref_tf, K, f"stack layer {l} (teacher-forced)")
+            check_token(og[0], ig[0], wg[0], ref_tf, K, f"stack layer {l} (teacher-forced)", unit_scale=True)
             if free_ok:
                 ref_fr = oracle_layer_generated(dims, w.seed, l, xo)
                 if list(ref_fr["idx"]) != list(ridx[l, t]):
@@ -200,8 +200,9 @@ def _stack(moe, n_layers, n_check_tokens=1):
         if free_ok:
             e2 = rel_l2(y[t], ref_fr["out"])
             ea = float(np.max(np.abs(y[t] - ref_fr["out"])))
-            log(f"stack free-running: rel-L2 {e2:.2e}, max-abs {ea:.2e}, |y| max {np.abs(y[t]).max():.1f}")
-            assert e2 <= 1e-4 and ea <= 1e-3
+            rms = float(np.sqrt(np.mean(np.square(ref_fr["out"]))))
+            log(f"stack free-running: rel-L2 {e2:.2e}, max-abs {ea:.2e}, rms(out) {rms:.3g}")
+            assert e2 <= 1e-4 and ea <= 1e-3 * max(1.0, rms)
 
 
 def test_stack_4_layers(moe):
@@ -209,4 +210,5 @@ def test_stack_4_layers(moe):
 
 
 def test_stack_60_layers(moe):
+    torch.cuda.empty_cache()
     _stack(moe, 60)
