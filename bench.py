@@ -128,19 +128,25 @@ def main():
     bytes_per_step = bytes_total / nsteps
     router_bytes = dims.n_experts * dims.hidden * 2
 
-    # per-launch duration, events on the launch stream (a separate pass over the same steps)
+    # per-kernel durations: each stage of the layer enqueued on its own between
+    # events on the launch stream (a separate pass over the same steps)
     nprobe = min(nsteps, 512)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(nprobe)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(nprobe)]
+    nst = 3
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(nprobe)]
     for i in range(nprobe):
-        starts[i].record()
-        step(i)
-        ends[i].record()
+        j = i % P
+        evs[i][0].record()
+        for st in range(nst):
+            moe.moe_layer_forward_stage(dims, descs[i % R], pool[j], out[j], T, ridx[j], rw[j], ws, wsb, st)
+            evs[i][st + 1].record()
     torch.cuda.synchronize()
-    durs = np.array([starts[i].elapsed_time(ends[i]) for i in range(nprobe)]) * 1e-3  # seconds
-    launch_s = float(np.mean(durs))
-    bytes_probe = float(np.mean([distinct[i % P] for i in range(nprobe)])) * eb
-    achieved = bytes_probe / launch_s
+    stage_s = np.array([[evs[i][st].elapsed_time(evs[i][st + 1]) for st in range(nst)] for i in range(nprobe)]) * 1e-3
+    stage_mean = stage_s.mean(axis=0)
+    # algorithmic bytes of the gate/up stage: gate + up codes and scale/bias of
+    # the distinct selected experts and the shared one
+    per_matrix = dims.ffn * dims.hidden * dims.bits // 8 + (dims.ffn * dims.hidden // 64) * 4
+    gu_bytes = float(np.mean([distinct[i % P] for i in range(nprobe)])) * 2 * per_matrix
+    achieved = gu_bytes / stage_mean[1]
 
     result = {
         "metric": "MoE-layer decode tokens/s (effective expert-weight HBM GB/s and % of peak alongside)",
@@ -166,15 +172,19 @@ def main():
         "effective_expert_GBps": round(bytes_per_step * nsteps / elapsed / 1e9, 1),
         "pct_of_hbm_peak": round(100.0 * bytes_per_step * nsteps / elapsed / HBM_PEAK_BPS, 2),
         "roofline": {
-            "kernel": "moe_layer_forward (k_router + k_gateup + k_down)",
+            "kernel": "k_gateup (routing + fused gate/up dequant GEMV + SwiGLU)",
             "bound": "hbm",
             "achieved": round(achieved / 1e9, 1),
             "peak": HBM_PEAK_BPS / 1e9,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_BPS, 4),
             "traffic": None,
-            "launch_us": round(launch_s * 1e6, 3),
+            "bytes_per_launch": round(gu_bytes),
+            "launch_us": round(float(stage_mean[1]) * 1e6, 3),
         },
+        "stage_us": {"k_router": round(float(stage_mean[0]) * 1e6, 3),
+                     "k_gateup": round(float(stage_mean[1]) * 1e6, 3),
+                     "k_down": round(float(stage_mean[2]) * 1e6, 3)},
     }
 
     if args.cpu_sample > 0:

@@ -62,6 +62,7 @@ _SIGS = {
     "moe_pack_expert": (ctypes.c_int, [_dimsp, _vp * 3, _vp * 3, _vp * 3, _vp, _vp]),
     "moe_generate_layer": (ctypes.c_int, [_dimsp, ctypes.c_uint64, ctypes.c_uint32, _vp, _vp, _vp]),
     "moe_layer_forward": (ctypes.c_int, [_dimsp, _layerp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "moe_layer_forward_stage": (ctypes.c_int, [_dimsp, _layerp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _i32, _vp]),
     "moe_stack_forward": (ctypes.c_int, [_dimsp, _layerp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -176,6 +177,15 @@ def moe_layer_forward(dims, layer: moe_layer_t, x, y, n_tokens: int, route_idx, 
                   _lib.moe_layer_forward(ctypes.byref(dims_of(dims)), ctypes.byref(layer), _addr(x), _addr(y),
                                          int(n_tokens), _addr(route_idx), _addr(route_w), _addr(workspace),
                                          nbytes, _stream(stream)))
+
+
+def moe_layer_forward_stage(dims, layer: moe_layer_t, x, y, n_tokens: int, route_idx, route_w, workspace,
+                            workspace_bytes: Optional[int], stage: int, stream=None) -> int:
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    return _check("moe_layer_forward_stage",
+                  _lib.moe_layer_forward_stage(ctypes.byref(dims_of(dims)), ctypes.byref(layer), _addr(x),
+                                               _addr(y), int(n_tokens), _addr(route_idx), _addr(route_w),
+                                               _addr(workspace), nbytes, int(stage), _stream(stream)))
 
 
 def moe_stack_forward(dims, layers: Sequence[moe_layer_t], x, y, n_tokens: int, route_idx, route_w,

@@ -181,6 +181,18 @@ int moe_layer_forward(const moe_dims_t *dims, const moe_layer_t *layer, const fl
     return hip_status(launch_forward(a, (hipStream_t)stream));
 }
 
+int moe_layer_forward_stage(const moe_dims_t *dims, const moe_layer_t *layer, const float *x, float *y,
+                            int32_t n_tokens, int32_t *route_idx, float *route_w, void *workspace,
+                            size_t workspace_bytes, int32_t stage, void *stream) {
+    int rc = check_forward_common(dims, x, y, n_tokens, route_idx, route_w, workspace, workspace_bytes);
+    if (rc != MOE_OK) return rc;
+    rc = check_layer(layer);
+    if (rc != MOE_OK) return rc;
+    if (stage < 0 || stage >= kForwardStages) return MOE_ERR_INVALID_ARG;
+    const FwdArgs a = make_fwd(dims, layer, x, y, n_tokens, route_idx, route_w, workspace);
+    return hip_status(launch_forward_stage(a, stage, (hipStream_t)stream));
+}
+
 int moe_stack_forward(const moe_dims_t *dims, const moe_layer_t *layers, int32_t n_layers, const float *x,
                       float *y, int32_t n_tokens, int32_t *route_idx, float *route_w, void *workspace,
                       size_t workspace_bytes, void *stream) {

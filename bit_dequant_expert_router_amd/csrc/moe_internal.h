@@ -22,6 +22,9 @@ struct Workspace {
     int32_t *sel;    // [T][K]   selected experts
     float *coef;     // [T][K+1] combine coefficients (renormalised weights, sigmoid(gs))
     float *act;      // [T][K+1][F] SwiGLU activations of the selected experts and the shared one
+    int8_t *hl;      // [T][3][H]  limbs of the fixed-point normalised tokens
+    float *hs;       // [T][H/64]  group scales (powers of two) of the limbs
+    float *hx;       // [T][H/32]  sums of h over each half group
 };
 
 struct Shape {
@@ -37,6 +40,9 @@ inline size_t workspace_bytes(const Shape &s, int T) {
     b += align_up((size_t)T * s.K * 4);
     b += align_up((size_t)T * (s.K + 1) * 4);
     b += align_up((size_t)T * (s.K + 1) * s.F * 4);
+    b += align_up((size_t)T * 3 * s.H);
+    b += align_up((size_t)T * (s.H / 64) * 4);
+    b += align_up((size_t)T * (s.H / 32) * 4);
     return b;
 }
 
@@ -56,6 +62,12 @@ inline Workspace carve_workspace(void *base, const Shape &s, int T) {
     w.coef = (float *)p;
     p += align_up((size_t)T * (s.K + 1) * 4);
     w.act = (float *)p;
+    p += align_up((size_t)T * (s.K + 1) * s.F * 4);
+    w.hl = (int8_t *)p;
+    p += align_up((size_t)T * 3 * s.H);
+    w.hs = (float *)p;
+    p += align_up((size_t)T * (s.H / 64) * 4);
+    w.hx = (float *)p;
     return w;
 }
 
@@ -76,7 +88,9 @@ struct FwdArgs {
     Workspace ws;
 };
 
+constexpr int kForwardStages = 3;
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_forward_stage(const FwdArgs &a, int stage, hipStream_t stream);
 
 struct PackArgs {
     ExpertLayout L;

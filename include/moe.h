@@ -165,6 +165,20 @@ int moe_layer_forward(const moe_dims_t *dims, const moe_layer_t *layer, const fl
                       size_t workspace_bytes, void *stream);
 
 /*
+ * Enqueue one stage of moe_layer_forward, for profiling or for interleaving
+ * other work between stages.  Stage 0: RMSNorm, router GEMV and shared-gate
+ * logit; stage 1: softmax/top-K/renormalise and the fused gate+up dequant GEMV
+ * with SwiGLU for the selected and the shared experts; stage 2: down-projection
+ * with the weighted combine, sigmoid-gated shared expert and residual.
+ * Stages 0, 1, 2 enqueued in this order with identical arguments (same
+ * workspace, stream order) produce exactly what moe_layer_forward produces.
+ * Arguments as for moe_layer_forward; stage outside 0..2 is MOE_ERR_INVALID_ARG.
+ */
+int moe_layer_forward_stage(const moe_dims_t *dims, const moe_layer_t *layer, const float *x, float *y,
+                            int32_t n_tokens, int32_t *route_idx, float *route_w, void *workspace,
+                            size_t workspace_bytes, int32_t stage, void *stream);
+
+/*
  * n_layers layers chained: x_{l+1} = layer_l(x_l), x_0 = x, y = x_{n_layers}
  * (no final norm).  `layers` is a HOST array of n_layers layer descriptors.
  * route_idx / route_w (device or NULL): [n_layers][n_tokens][K].

@@ -154,6 +154,20 @@ def test_forward_rejects(kw, status):
     assert _fwd(**kw) == status
 
 
+def test_stage_rejects():
+    dims = d()
+    wsb = moe.moe_workspace_bytes(dims, 1)
+    f = moe._lib.moe_layer_forward_stage
+    lay = _layer()
+    for stage in (-1, 3, 100):
+        assert f(ctypes.byref(dims), ctypes.byref(lay), A + 0x300000, A + 0x400000, 1, None, None, A + 0x500000,
+                 wsb, stage, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(dims), ctypes.byref(lay), A + 0x300000, A + 0x400000, 1, None, None, A + 0x500000,
+             16, 0, None) == moe.MOE_ERR_WORKSPACE
+    assert f(ctypes.byref(dims), None, A + 0x300000, A + 0x400000, 1, None, None, A + 0x500000,
+             wsb, 0, None) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_stack_rejects():
     dims = d()
     lay = (moe.moe_layer_t * 2)(_layer(), _layer(experts=None))

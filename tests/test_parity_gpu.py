@@ -90,6 +90,36 @@ def test_inplace_determinism_and_optional_outputs(moe):
     assert np.array_equal(a, c) and np.array_equal(a, d)
 
 
+def test_stages_equal_full_forward(moe):
+    """Stages 0, 1, 2 enqueued one by one give exactly the one-call result."""
+    dims = syn.WORKLOADS["tiny"].dims
+    dense, experts, lw = _canonical_layer(dims)
+    x = syn.tokens(4, 5, dims.hidden)
+    full, fidx, fw = run_layer(dims, lw, x)
+    xt = torch.from_numpy(x).cuda()
+    yt = torch.empty_like(xt)
+    ridx = torch.empty((5, dims.top_k), dtype=torch.int32, device="cuda")
+    rw = torch.empty((5, dims.top_k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_workspace_bytes(dims, 5), dtype=torch.uint8, device="cuda")
+    moe.moe_workspace_init(ws)
+    for stage in range(3):
+        moe.moe_layer_forward_stage(dims, lw.descriptor(), xt, yt, 5, ridx, rw, ws, None, stage)
+    torch.cuda.synchronize()
+    assert np.array_equal(yt.cpu().numpy(), full) and np.array_equal(ridx.cpu().numpy(), fidx)
+    assert np.array_equal(rw.cpu().numpy(), fw)
+
+
+def test_nan_propagates(moe):
+    """A NaN in x reaches every output of its token and no other token."""
+    dims = syn.WORKLOADS["tiny"].dims
+    dense, experts, lw = _canonical_layer(dims)
+    x = syn.tokens(5, 3, dims.hidden)
+    x[1, 17] = np.nan
+    out, idx, wt = run_layer(dims, lw, x)
+    assert np.all(np.isnan(out[1]))
+    assert np.all(np.isfinite(out[0])) and np.all(np.isfinite(out[2]))
+
+
 def test_zero_router_selects_first_experts(moe):
     """All-zero router: every logit is 0, so experts 0..K-1 with weight 1/K."""
     dims = syn.WORKLOADS["tiny"].dims
