@@ -21,13 +21,14 @@
 // the group-level form of the pages' fma(nibble, scale*x, bias*x) rewrite.
 // The code products sum_i q_i v_i are taken exactly in integers: each group of
 // the activation vector v is written as V_i * S with S a power of two
-// (max|v| < 2^22 S) and V_i an integer split into three signed 8-bit limbs,
-// V = L2*65536 + L1*256 + L0; v_dot4 instructions accumulate q * L per limb
-// (4 codes per instruction, exact int32), and one fp32 combination per group
-// restores s*S*(D2*65536 + D1*256 + D0).  The only roundings are the 22-bit
-// fixed point of v (relative 2^-23 of the group maximum) and fp32 sums,
-// comparable to an fp32 dot product; VALU work drops to ~1.2 instructions per
-// weight from ~2.3 for convert-and-FMA.
+// (max|v| < 2^30 S) and V_i an integer split into four signed 8-bit limbs,
+// V = L3*2^24 + L2*2^16 + L1*2^8 + L0; v_dot4 instructions accumulate q * L per
+// limb (4 codes per instruction, exact int32), and one fp32 combination per
+// group restores s*S*(D3*2^24 + D2*2^16 + D1*2^8 + D0).  Every value within a
+// factor 2^7 of its group's maximum is represented exactly (a float has 24
+// significant bits); smaller ones carry an absolute error below 2^-31 of the
+// maximum, so the result matches an fp32 dot product.  VALU work is ~1.4
+// instructions per weight against ~2.3 for convert-and-FMA.
 #include "moe_internal.h"
 
 namespace moe {
@@ -37,34 +38,76 @@ namespace {
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
 
-// Sum over aligned groups of `width` lanes (a power of two <= 64); every lane
-// of a group receives the group's sum.
-__device__ __forceinline__ float lane_group_sum(float v, int width) {
-    for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+// ---------------------------------------------------------------------------
+// cross-lane reductions on the VALU: DPP quad permutations and row mirrors
+// inside 16-lane rows, then v_permlane16_swap / v_permlane32_swap across rows.
+// Each step is one VALU instruction (no LDS round trip).  Callers keep every
+// lane of a reduced group active.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside each half row
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i inside each row
 
-template <int W>
-__device__ __forceinline__ float lane_sum(float v) {
-#pragma unroll
-    for (int o = W >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
+struct SumOp {
+    __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct MaxOp {  // keeps a NaN (fmaxf would drop it)
+    __device__ __forceinline__ float operator()(float a, float b) const {
+        return (a != a || b != b) ? (a + b) : fmaxf(a, b);
+    }
+};
 
-template <int W>
-__device__ __forceinline__ float lane_max(float v) {
-#pragma unroll
-    for (int o = W >> 1; o > 0; o >>= 1) {
-        const float u = __shfl_xor(v, o, 64);
-        v = (v != v || u != u) ? (v + u) : fmaxf(v, u);
+// reduce over aligned groups of W lanes (W a power of two <= 64); every lane
+// of a group receives the result
+template <int W, typename Op>
+__device__ __forceinline__ float lane_reduce(float v, Op op) {
+    if constexpr (W >= 2) v = op(v, __uint_as_float(dpp_u<kDppXor1>(__float_as_uint(v))));
+    if constexpr (W >= 4) v = op(v, __uint_as_float(dpp_u<kDppXor2>(__float_as_uint(v))));
+    if constexpr (W >= 8) v = op(v, __uint_as_float(dpp_u<kDppHalfMirror>(__float_as_uint(v))));
+    if constexpr (W >= 16) v = op(v, __uint_as_float(dpp_u<kDppMirror>(__float_as_uint(v))));
+    if constexpr (W >= 32) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = op(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    }
+    if constexpr (W >= 64) {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = op(__uint_as_float(p[0]), __uint_as_float(p[1]));
     }
     return v;
 }
 
+template <int W>
+__device__ __forceinline__ float lane_sum(float v) { return lane_reduce<W>(v, SumOp()); }
+template <int W>
+__device__ __forceinline__ float lane_max(float v) { return lane_reduce<W>(v, MaxOp()); }
+
+// sum over aligned groups of a runtime width (uniform across the wave)
+__device__ __forceinline__ float lane_group_sum(float v, int width) {
+    switch (width) {
+        case 1: return v;
+        case 2: return lane_sum<2>(v);
+        case 4: return lane_sum<4>(v);
+        case 8: return lane_sum<8>(v);
+        case 16: return lane_sum<16>(v);
+        case 32: return lane_sum<32>(v);
+        default: return lane_sum<64>(v);
+    }
+}
+
+// value of a wave-uniform lane index
+__device__ __forceinline__ int lane_bcast(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+__device__ __forceinline__ float lane_bcast(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
 __device__ __forceinline__ float sigmoidf_(float t) { return 1.0f / (1.0f + expf(-t)); }
 
-// max that keeps a NaN (fmaxf would drop it)
-__device__ __forceinline__ float nan_max(float a, float b) { return (a != a || b != b) ? (a + b) : fmaxf(a, b); }
+__device__ __forceinline__ float nan_max(float a, float b) { return MaxOp()(a, b); }
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -78,28 +121,34 @@ __device__ __forceinline__ uint32_t ld_stream4(const uint32_t *p) { return __bui
 // ---------------------------------------------------------------------------
 // fixed-point limbs
 // ---------------------------------------------------------------------------
-// Exponent e with max|v| < 2^e, clamped so that 2^(e-22) and 2^(22-e) are
-// normal floats.  NaN / inf maxima give e = 255 (flagged by limb_scale).
+constexpr int kLimbs = 4;
+constexpr int kFixBits = 8 * kLimbs - 2;  // |V| <= 2^30
+
+// Exponent e with max|v| < 2^e, clamped so that 2^(e-30) and 2^(30-e) are
+// normal floats.  NaN / inf maxima are flagged by limb_scale.
 __device__ __forceinline__ int limb_exponent(float m) {
     const uint32_t E = (__float_as_uint(m) >> 23) & 0xFFu;
     int e = (E == 0 ? 1 : (int)E) - 126;  // m < 2^e
-    return e < -100 ? -100 : e;
+    return e < -90 ? -90 : e;
 }
 __device__ __forceinline__ float pow2f(int p) { return __uint_as_float((uint32_t)(p + 127) << 23); }
-// scale S of a group: 2^(e-22), or NaN when the group holds a NaN or an inf
+// scale S of a group: 2^(e-30), or NaN when the group holds a NaN or an inf
 __device__ __forceinline__ float limb_scale(float m) {
-    return (m <= 3.4028234663852886e38f) ? pow2f(limb_exponent(m) - 22) : __uint_as_float(0x7FC00000u);
+    return (m <= 3.4028234663852886e38f) ? pow2f(limb_exponent(m) - kFixBits) : __uint_as_float(0x7FC00000u);
 }
-// integer V = rint(v / S) for finite groups (|V| <= 2^22), 0 otherwise
+// integer V = rint(v / S) for finite groups (|V| <= 2^30), 0 otherwise
 __device__ __forceinline__ int limb_value(float v, float m) {
     if (!(m <= 3.4028234663852886e38f)) return 0;
-    return (int)rintf(v * pow2f(22 - limb_exponent(m)));
+    return (int)rintf(v * pow2f(kFixBits - limb_exponent(m)));
 }
-__device__ __forceinline__ void limb_split(int V, int &l0, int &l1, int &l2) {
-    l0 = ((V + 128) & 255) - 128;
-    const int v1 = (V - l0) >> 8;
-    l1 = ((v1 + 128) & 255) - 128;
-    l2 = (v1 - l1) >> 8;
+// balanced base-256 digits: V = sum_x l[x] 256^x, l[0..2] in [-128, 127], l[3] in [-64, 64]
+__device__ __forceinline__ void limb_split(int V, int (&l)[kLimbs]) {
+#pragma unroll
+    for (int x = 0; x < kLimbs - 1; ++x) {
+        l[x] = ((V + 128) & 255) - 128;
+        V = (V - l[x]) >> 8;
+    }
+    l[kLimbs - 1] = V;
 }
 
 // ---------------------------------------------------------------------------
@@ -112,13 +161,28 @@ __device__ __forceinline__ uint64_t route_key(float z, int e) {
     return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)e);
 }
 
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint32_t blo, uint32_t bhi) {
+    const uint64_t b = ((uint64_t)bhi << 32) | blo;
+    return b > a ? b : a;
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+    return max_u64(v, dpp_u<CTRL>((uint32_t)v), dpp_u<CTRL>((uint32_t)(v >> 32)));
+}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
-        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-        const uint64_t other = ((uint64_t)hi << 32) | lo;
-        v = other > v ? other : v;
+    v = dpp_max_u64<kDppXor1>(v);
+    v = dpp_max_u64<kDppXor2>(v);
+    v = dpp_max_u64<kDppHalfMirror>(v);
+    v = dpp_max_u64<kDppMirror>(v);
+    {
+        const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+        v = max_u64(((uint64_t)hi[0] << 32) | lo[0], lo[1], hi[1]);
+    }
+    {
+        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+        v = max_u64(((uint64_t)hi[0] << 32) | lo[0], lo[1], hi[1]);
     }
     return v;
 }
@@ -128,38 +192,65 @@ __device__ __forceinline__ float route_key_value(uint64_t key) {
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
-__device__ __forceinline__ void route_wave(const float *__restrict__ z, int E, int K, int &my_sel, float &my_w) {
+// the router logits of one token, EPL per lane (clamped index: all loads in flight at once)
+template <int EPL>
+__device__ __forceinline__ void load_logits(const float *__restrict__ z, int E, float (&zv)[EPL]) {
     const int lane = threadIdx.x & 63;
-    constexpr int kPer = kMaxExperts / 64;
-    float zv[kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {  // unconditional (clamped) loads: all in flight at once
+    for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
         zv[i] = z[e < E ? e : E - 1];
     }
-    uint64_t key[kPer];
+}
+
+// bitonic sort of n = EPL keys, descending
+template <int EPL>
+__device__ __forceinline__ void sort_desc(uint64_t (&key)[EPL]) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int k = 2; k <= EPL; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const bool desc = (i & k) == 0;
+                    const uint64_t a = key[i], b = key[l];
+                    const bool swap = desc ? (a < b) : (a > b);
+                    key[i] = swap ? b : a;
+                    key[l] = swap ? a : b;
+                }
+            }
+}
+
+// Softmax -> top-K -> renormalise by one wave.  Each lane sorts its EPL keys;
+// every round takes the wave maximum of the list heads and the winning lane
+// pops its head.  Lane k < K ends with the k-th selected expert and weight.
+template <int EPL>
+__device__ __forceinline__ void route_wave(const float (&zv)[EPL], int E, int K, int &my_sel, float &my_w) {
+    const int lane = threadIdx.x & 63;
+    uint64_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
         key[i] = (e < E) ? route_key(zv[i], e) : 0ull;
     }
+    sort_desc<EPL>(key);
     my_sel = 0;
     float my_z = 0.0f;
     for (int k = 0; k < K; ++k) {
-        uint64_t best = 0ull;
+        const uint64_t best = wave_max_u64(key[0]);
+        const bool win = key[0] == best;  // keys are unique: the index is part of the key
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_u64(best);
-#pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if (key[i] == best) key[i] = 0ull;
+        for (int i = 0; i < EPL - 1; ++i) key[i] = win ? key[i + 1] : key[i];
+        key[EPL - 1] = win ? 0ull : key[EPL - 1];
         if (lane == k) {
             my_sel = (int)(~(uint32_t)best);
             my_z = route_key_value(best);
         }
     }
     // softmax restricted to the selection == renormalised full softmax
-    const float z0 = __shfl(my_z, 0, 64);
+    const float z0 = lane_bcast(my_z, 0);
     const float p = (lane < K) ? expf(my_z - z0) : 0.0f;
     const float denom = lane_sum<64>(p);
     my_w = p / denom;
@@ -182,7 +273,7 @@ struct QSlice {
 template <int BITS, int CPL>
 struct LimbSlice {
     using Q = QSlice<BITS, CPL>;
-    int L[3][Q::NL];
+    int L[kLimbs][Q::NL];
     float S[Q::NGL];  // group scale (power of two)
     float X[Q::NGL];  // sum of the activations of the slice within the group
 };
@@ -191,9 +282,11 @@ template <int BITS, int CPL>
 __device__ __forceinline__ float qdot(const uint4 (&c)[CPL], const uint32_t (&sb)[QSlice<BITS, CPL>::NGL],
                                       const LimbSlice<BITS, CPL> &v) {
     using Q = QSlice<BITS, CPL>;
-    int acc[Q::NGL][3];
+    int acc[Q::NGL][kLimbs];
 #pragma unroll
-    for (int g = 0; g < Q::NGL; ++g) acc[g][0] = acc[g][1] = acc[g][2] = 0;
+    for (int g = 0; g < Q::NGL; ++g)
+#pragma unroll
+        for (int x = 0; x < kLimbs; ++x) acc[g][x] = 0;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const uint32_t d[4] = {c[j].x, c[j].y, c[j].z, c[j].w};
@@ -205,14 +298,16 @@ __device__ __forceinline__ float qdot(const uint4 (&c)[CPL], const uint32_t (&sb
                 const int li = (j * Q::C + w4 * Q::D) / 4 + n;  // limb dword of these 4 codes
                 const int g = (4 * li) / Q::GL;
 #pragma unroll
-                for (int x = 0; x < 3; ++x) acc[g][x] = __builtin_amdgcn_sdot4(m, v.L[x][li], acc[g][x], false);
+                for (int x = 0; x < kLimbs; ++x) acc[g][x] = __builtin_amdgcn_sdot4(m, v.L[x][li], acc[g][x], false);
             }
         }
     }
     float total = 0.0f;
 #pragma unroll
     for (int g = 0; g < Q::NGL; ++g) {
-        const float f = fmaf((float)acc[g][2], 65536.0f, fmaf((float)acc[g][1], 256.0f, (float)acc[g][0]));
+        float f = (float)acc[g][kLimbs - 1];
+#pragma unroll
+        for (int x = kLimbs - 2; x >= 0; --x) f = fmaf(f, 256.0f, (float)acc[g][x]);
         total = fmaf(bf16_lo(sb[g]) * v.S[g], f, total);
         total = fmaf(bf16_hi(sb[g]), v.X[g], total);
     }
@@ -235,8 +330,10 @@ __device__ __forceinline__ void load_row(const uint8_t *__restrict__ ex, const Q
 // k_router: one router row-step per wave; the first ceil(H/256) blocks also
 // write the limb form of h for k_gateup.
 // ---------------------------------------------------------------------------
+constexpr int kRouterWaves = 2;
+
 template <int CPLR>
-__global__ __launch_bounds__(256) void k_router(FwdArgs a) {
+__global__ __launch_bounds__(64 * kRouterWaves) void k_router(FwdArgs a) {
     const int t = blockIdx.y;
     const int H = a.s.H, E = a.s.E;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -246,12 +343,14 @@ __global__ __launch_bounds__(256) void k_router(FwdArgs a) {
     const int rpi = 64 / lpr;
     const int lr = lane % lpr, rsub = lane / lpr;
     const int nrs = (E + 1 + rpi - 1) / rpi;
-    const int rs = blockIdx.x * 4 + wave;
+    const int rs = blockIdx.x * kRouterWaves + wave;
     const int r = rs * rpi + rsub;
     const bool has_row = rs < nrs && r <= E;
 
     // issue the router row loads first
     uint4 wv[CPLR];
+#pragma unroll
+    for (int j = 0; j < CPLR; ++j) wv[j] = make_uint4(0u, 0u, 0u, 0u);
     if (has_row) {
         const uint16_t *row = (r < E) ? a.router + (size_t)r * H : a.sgate;
 #pragma unroll
@@ -276,44 +375,38 @@ __global__ __launch_bounds__(256) void k_router(FwdArgs a) {
     ss = lane_group_sum(ss, lpr);
     const float inv = 1.0f / sqrtf(ss / (float)H + a.s.eps);
 
-    // pass 2 + router dot product
-    if (has_row) {
-        float acc = 0.0f;
+    // pass 2 + router dot product (lanes without a row add zeros)
+    float acc = 0.0f;
 #pragma unroll
-        for (int j = 0; j < CPLR; ++j) {
-            const uint32_t w[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
-            const uint32_t g[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
+    for (int j = 0; j < CPLR; ++j) {
+        const uint32_t w[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+        const uint32_t g[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc = fmaf(bf16_lo(w[q]), xv[8 * j + 2 * q] * inv * bf16_lo(g[q]), acc);
-                acc = fmaf(bf16_hi(w[q]), xv[8 * j + 2 * q + 1] * inv * bf16_hi(g[q]), acc);
-            }
+        for (int q = 0; q < 4; ++q) {
+            acc = fmaf(bf16_lo(w[q]), xv[8 * j + 2 * q] * inv * bf16_lo(g[q]), acc);
+            acc = fmaf(bf16_hi(w[q]), xv[8 * j + 2 * q + 1] * inv * bf16_hi(g[q]), acc);
         }
-        acc = lane_group_sum(acc, lpr);
-        if (lr == 0) {
-            if (r < E)
-                a.ws.z[(size_t)t * E + r] = acc;
-            else
-                a.ws.gs[t] = acc;
-        }
-    } else {
-        (void)lane_group_sum(0.0f, lpr);
+    }
+    acc = lane_group_sum(acc, lpr);
+    if (has_row && lr == 0) {
+        if (r < E)
+            a.ws.z[(size_t)t * E + r] = acc;
+        else
+            a.ws.gs[t] = acc;
     }
 
-    // limb form of h[256 b .. 256 b + 255]: one wave = one group of 64
-    const int k = blockIdx.x * 256 + threadIdx.x;
-    if (blockIdx.x * 256 < H) {
+    // limb form of h[64 kRouterWaves b ..]: one wave = one group of 64
+    const int k = blockIdx.x * 64 * kRouterWaves + threadIdx.x;
+    if (blockIdx.x * 64 * kRouterWaves < H) {
         const float h = (k < H) ? x[k] * inv * __uint_as_float((uint32_t)a.gamma[k] << 16) : 0.0f;
         const float m = lane_max<64>(fabsf(h));
-        const int V = limb_value(h, m);
-        int l0, l1, l2;
-        limb_split(V, l0, l1, l2);
+        int l[kLimbs];
+        limb_split(limb_value(h, m), l);
         const float half = lane_sum<32>(h);
         if (k < H) {
-            int8_t *hl = a.ws.hl + (size_t)t * 3 * H;
-            hl[k] = (int8_t)l0;
-            hl[H + k] = (int8_t)l1;
-            hl[2 * H + k] = (int8_t)l2;
+            int8_t *hl = a.ws.hl + (size_t)t * kLimbs * H;
+#pragma unroll
+            for (int x = 0; x < kLimbs; ++x) hl[(size_t)x * H + k] = (int8_t)l[x];
             if (lane == 0) a.ws.hs[(size_t)t * (H / 64) + k / 64] = limb_scale(m);
             if ((lane & 31) == 0) a.ws.hx[(size_t)t * (H / 32) + k / 32] = half;
         }
@@ -323,7 +416,7 @@ __global__ __launch_bounds__(256) void k_router(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // k_gateup: RPW row-steps per wave over the (K+1) x F gate/up row pairs
 // ---------------------------------------------------------------------------
-template <int BITS, int CPL, int RPW>
+template <int BITS, int CPL, int RPW, int EPL>
 __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
     using Q = QSlice<BITS, CPL>;
     const int t = blockIdx.y;
@@ -335,68 +428,110 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
     const int lr = lane % lpr, rsub = lane / lpr;
     const int nrs = (K + 1) * F / rpi;
     const int rs0 = (blockIdx.x * 4 + wave) * RPW;
-    if (rs0 >= nrs) return;
+    const bool active = rs0 < nrs;
+    // row-steps are slot-major: the block needs the routing iff its first row is routed
+    const bool block_routed = (blockIdx.x * 4 * RPW * rpi) / F < K;
+    const bool wave_shared_only = (rs0 * rpi) / F >= K;
 
-    // the lane's limb slice of h
-    const int k0 = lr * Q::NV;
-    LimbSlice<BITS, CPL> hv;
+    __shared__ int s_sel[kMaxTopK];
+    __shared__ float s_w[kMaxTopK];
+    __shared__ __align__(16) int8_t s_hl[kLimbs * kMaxDim];  // limbs of h, [kLimbs][H]
+    __shared__ float s_hs[kMaxDim / 64];
+    __shared__ float s_hx[kMaxDim / 32];
+
+    // wave 0 routes for the whole block: its logit loads go first (loads complete in order)
+    float zv[EPL];
+    if (block_routed && wave == 0) load_logits<EPL>(a.ws.z + (size_t)t * E, E, zv);
+
+    // stage the limb form of h in LDS, once per block
     {
-        const int8_t *hl = a.ws.hl + (size_t)t * 3 * H + k0;
-#pragma unroll
-        for (int x = 0; x < 3; ++x)
-#pragma unroll
-            for (int i = 0; i < Q::NL / 4; ++i) {
-                const int4 v = *(const int4 *)(hl + (size_t)x * H + 16 * i);
-                hv.L[x][4 * i + 0] = v.x; hv.L[x][4 * i + 1] = v.y;
-                hv.L[x][4 * i + 2] = v.z; hv.L[x][4 * i + 3] = v.w;
+        const int4 *src = (const int4 *)(a.ws.hl + (size_t)t * kLimbs * H);
+        const int n16 = kLimbs * H / 16;
+        constexpr int kStage = kLimbs * kMaxDim / 16 / 256;
+        int4 st0, st1, st2, st3;  // kStage == 4 staged 16-byte pieces per thread
+        static_assert(kStage == 4, "staging assumes 4 pieces per thread");
+        {
+            const int i0 = threadIdx.x, i1 = threadIdx.x + 256, i2 = threadIdx.x + 512, i3 = threadIdx.x + 768;
+            st0 = src[i0 < n16 ? i0 : 0];
+            st1 = src[i1 < n16 ? i1 : 0];
+            st2 = src[i2 < n16 ? i2 : 0];
+            st3 = src[i3 < n16 ? i3 : 0];
+        }
+        float hs = 0.0f, hx = 0.0f;
+        if (threadIdx.x < H / 64) hs = a.ws.hs[(size_t)t * (H / 64) + threadIdx.x];
+        if (threadIdx.x < H / 32) hx = a.ws.hx[(size_t)t * (H / 32) + threadIdx.x];
+        if (block_routed && wave == 0) {
+            int my_sel;
+            float my_w;
+            route_wave<EPL>(zv, E, K, my_sel, my_w);
+            if (lane < K) {
+                s_sel[lane] = my_sel;
+                s_w[lane] = my_w;
             }
-        if constexpr (Q::NL % 4 != 0) {
-#pragma unroll
-            for (int x = 0; x < 3; ++x)
-#pragma unroll
-                for (int i = (Q::NL / 4) * 4; i < Q::NL; ++i)
-                    hv.L[x][i] = *(const int *)(hl + (size_t)x * H + 4 * i);
+            if (blockIdx.x == 0) {
+                if (lane < K) {
+                    a.ws.sel[t * K + lane] = my_sel;
+                    a.ws.coef[t * (K + 1) + lane] = my_w;
+                    if (a.route_idx) a.route_idx[t * K + lane] = my_sel;
+                    if (a.route_w) a.route_w[t * K + lane] = my_w;
+                } else if (lane == K) {
+                    a.ws.coef[t * (K + 1) + K] = sigmoidf_(a.ws.gs[t]);
+                }
+            }
         }
-#pragma unroll
-        for (int g = 0; g < Q::NGL; ++g) {
-            hv.S[g] = a.ws.hs[(size_t)t * (H / 64) + k0 / 64 + g];
-            float xs = 0.0f;
-#pragma unroll
-            for (int hh = 0; hh < Q::GL / 32; ++hh) xs += a.ws.hx[(size_t)t * (H / 32) + (k0 + g * 64) / 32 + hh];
-            hv.X[g] = xs;
+        {
+            int4 *dst = (int4 *)s_hl;
+            const int i0 = threadIdx.x, i1 = threadIdx.x + 256, i2 = threadIdx.x + 512, i3 = threadIdx.x + 768;
+            if (i0 < n16) dst[i0] = st0;
+            if (i1 < n16) dst[i1] = st1;
+            if (i2 < n16) dst[i2] = st2;
+            if (i3 < n16) dst[i3] = st3;
         }
+        if (threadIdx.x < H / 64) s_hs[threadIdx.x] = hs;
+        if (threadIdx.x < H / 32) s_hx[threadIdx.x] = hx;
     }
 
-    // routing (every wave that touches a routed expert computes it)
-    int my_sel = 0;
-    float my_w = 0.0f;
-    if ((rs0 * rpi) / F < K) route_wave(a.ws.z + (size_t)t * E, E, K, my_sel, my_w);
-    if (blockIdx.x == 0 && wave == 0) {
-        if (lane < K) {
-            a.ws.sel[t * K + lane] = my_sel;
-            a.ws.coef[t * (K + 1) + lane] = my_w;
-            if (a.route_idx) a.route_idx[t * K + lane] = my_sel;
-            if (a.route_w) a.route_w[t * K + lane] = my_w;
-        } else if (lane == K) {
-            a.ws.coef[t * (K + 1) + K] = sigmoidf_(a.ws.gs[t]);
-        }
-    }
-
-    // all weight loads of this wave
+    // weight loads: shared-only waves issue theirs before the routing is known
     uint4 gc[RPW][CPL], uc[RPW][CPL];
     uint32_t gsb[RPW][Q::NGL], usb[RPW][Q::NGL];
+    auto issue_loads = [&]() {
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int rs = rs0 + i;
-        if (rs < nrs) {
-            const int p = rs * rpi + rsub;
-            const int s = p / F, j = p % F;
-            const int e = __shfl(my_sel, s < K ? s : 0, 64);
-            const uint8_t *ex = (s < K) ? a.experts + (size_t)e * a.L.bytes : a.shared;
-            load_row<BITS, CPL>(ex, G, j, lr, gc[i], gsb[i]);
-            load_row<BITS, CPL>(ex, U, j, lr, uc[i], usb[i]);
+        for (int i = 0; i < RPW; ++i) {
+            const int rs = rs0 + i;
+            if (rs < nrs) {
+                const int p = rs * rpi + rsub;
+                const int s = p / F, j = p % F;
+                const uint8_t *ex = (s < K) ? a.experts + (size_t)s_sel[s] * a.L.bytes : a.shared;
+                load_row<BITS, CPL>(ex, G, j, lr, gc[i], gsb[i]);
+                load_row<BITS, CPL>(ex, U, j, lr, uc[i], usb[i]);
+            }
         }
+    };
+    if (active && wave_shared_only) issue_loads();
+    __syncthreads();
+    if (!active) return;
+    if (!wave_shared_only) issue_loads();
+
+    // the lane's limb slice of h, from LDS
+    const int k0 = lr * Q::NV;
+    LimbSlice<BITS, CPL> hv;
+#pragma unroll
+    for (int x = 0; x < kLimbs; ++x)
+#pragma unroll
+        for (int i = 0; i < Q::NL / 4; ++i) {
+            const int4 v = *(const int4 *)(s_hl + x * H + k0 + 16 * i);
+            hv.L[x][4 * i + 0] = v.x; hv.L[x][4 * i + 1] = v.y;
+            hv.L[x][4 * i + 2] = v.z; hv.L[x][4 * i + 3] = v.w;
+        }
+#pragma unroll
+    for (int g = 0; g < Q::NGL; ++g) {
+        hv.S[g] = s_hs[k0 / 64 + g];
+        float xs = 0.0f;
+#pragma unroll
+        for (int hh = 0; hh < Q::GL / 32; ++hh) xs += s_hx[(k0 + g * 64) / 32 + hh];
+        hv.X[g] = xs;
     }
+
     float *act = a.ws.act + (size_t)t * (K + 1) * F;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
@@ -412,11 +547,55 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_down: RPW row-steps of the H output rows per wave, all K+1 experts, in
-// batches of SB experts whose activations are turned into limbs in LDS.
+// k_down: RPW row-steps of the H output rows per wave, all K+1 experts in
+// batches of SB slots whose loads are all in flight together.  The SwiGLU
+// activations vary widely in magnitude, so this product stays in fp32:
+// codes are converted with v_cvt_f32_ubyte and folded per group as
+// s * sum(q a) + b * sum(a).
 // ---------------------------------------------------------------------------
-template <int BITS, int CPL, int RPW, int SB>
-__global__ __launch_bounds__(256) void k_down(FwdArgs a) {
+template <int BITS, int CPL>
+__device__ __forceinline__ float qdot_f32(const uint4 (&c)[CPL], const uint32_t (&sb)[QSlice<BITS, CPL>::NGL],
+                                          const float (&av)[QSlice<BITS, CPL>::NV],
+                                          const float (&X)[QSlice<BITS, CPL>::NGL]) {
+    using Q = QSlice<BITS, CPL>;
+    float acc[Q::NGL];
+#pragma unroll
+    for (int g = 0; g < Q::NGL; ++g) acc[g] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const uint32_t d[4] = {c[j].x, c[j].y, c[j].z, c[j].w};
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+#pragma unroll
+            for (int n = 0; n < 8 / BITS; ++n) {
+                // isolate slot n of every byte in place: byte value = q << (BITS n); the
+                // power of two is undone by scaling the group sum below
+                const uint32_t m = d[w4] & (Q::kByteMask << (BITS * n));
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int i = j * Q::C + w4 * Q::D + 4 * n + b;
+                    const float q = (float)((m >> (8 * b)) & 0xFFu) * (1.0f / (float)(1 << (BITS * n)));
+                    acc[i / Q::GL] = fmaf(q, av[i], acc[i / Q::GL]);
+                }
+            }
+        }
+    }
+    float total = 0.0f;
+#pragma unroll
+    for (int g = 0; g < Q::NGL; ++g) {
+        total = fmaf(bf16_lo(sb[g]), acc[g], total);
+        total = fmaf(bf16_hi(sb[g]), X[g], total);
+    }
+    return total;
+}
+
+// k_down processes the K+1 slots in batches of at most kDownBatch; a batch's
+// activations and their half-group sums are staged in LDS once per block.
+constexpr int kDownBatch = 5;
+constexpr size_t kDownLdsBudget = 64 * 1024;
+
+template <int BITS, int CPL, int RPW>
+__global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
     using Q = QSlice<BITS, CPL>;
     const int t = blockIdx.y;
     const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K;
@@ -426,12 +605,12 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a) {
     const int lr = lane % lpr, rsub = lane / lpr;
     const int nrs = H / rpi;
     const int rs0 = (blockIdx.x * 4 + wave) * RPW;
+    const bool active = rs0 < nrs;
     const int k0 = lr * Q::NV;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    int8_t *sl = (int8_t *)smem;                          // [SB][3][F]
-    float *ss = (float *)(smem + (size_t)SB * 3 * F);     // [SB][F/64]
-    float *sx = ss + SB * (F / 64);                       // [SB][F/32]
+    float *s_act = (float *)smem;              // [batch][F]
+    float *s_half = s_act + (size_t)batch * F;  // [batch][F/32]
 
     // lane s (s <= K) holds slot s: expert index and combine coefficient
     const int my_e = (lane < K) ? a.ws.sel[t * K + lane] : E;
@@ -441,15 +620,17 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < RPW; ++i) acc[i] = 0.0f;
 
-    for (int s0 = 0; s0 <= K; s0 += SB) {
-        const int nb = (K + 1 - s0) < SB ? (K + 1 - s0) : SB;
-        // weight loads of this batch
-        uint4 wc[SB][RPW][CPL];
-        uint32_t wsb[SB][RPW][Q::NGL];
+    // slot positions run shared, 0, 1, ..., K-1: the shared expert's loads need no routing
+    for (int b0 = 0; b0 <= K; b0 += batch) {
+        const int nb = (K + 1 - b0) < batch ? (K + 1 - b0) : batch;
+        // weights of up to kDownBatch slots of this batch, all in flight together
+        uint4 wc[kDownBatch][RPW][CPL];
+        uint32_t wsb[kDownBatch][RPW][Q::NGL];
 #pragma unroll
-        for (int si = 0; si < SB; ++si) {
-            if (si < nb) {
-                const int e = __shfl(my_e, s0 + si, 64);
+        for (int si = 0; si < kDownBatch; ++si) {
+            if (si < nb && active) {
+                const int s = (b0 + si == 0) ? K : b0 + si - 1;
+                const int e = (s == K) ? E : lane_bcast(my_e, s);
                 const uint8_t *ex = (e < E) ? a.experts + (size_t)e * a.L.bytes : a.shared;
 #pragma unroll
                 for (int i = 0; i < RPW; ++i) {
@@ -458,56 +639,49 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a) {
                 }
             }
         }
-        // limbs of this batch's activations, in LDS
-        __syncthreads();
-        const float *act = a.ws.act + ((size_t)t * (K + 1) + s0) * F;
-        for (int v0 = threadIdx.x * 4; v0 < SB * F; v0 += 1024) {
+        // stage this batch's activations and half-group sums
+        __syncthreads();  // the previous batch is done with the LDS
+        for (int v0 = threadIdx.x * 4; v0 < batch * F; v0 += 1024) {
             const bool live = v0 < nb * F;
-            const float4 v = live ? *(const float4 *)(act + v0) : make_float4(0.f, 0.f, 0.f, 0.f);
-            float m = nan_max(nan_max(fabsf(v.x), fabsf(v.y)), nan_max(fabsf(v.z), fabsf(v.w)));
-            m = lane_max<16>(m);  // 16 lanes x 4 values = one group of 64
-            int l[4][3];
-            const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) limb_split(limb_value(vv[q], m), l[q][0], l[q][1], l[q][2]);
-            const float half = lane_sum<8>(v.x + v.y + v.z + v.w);
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             if (live) {
-                const int sidx = v0 / F, j = v0 % F;
-#pragma unroll
-                for (int x = 0; x < 3; ++x) {
-                    const uint32_t packed = (uint32_t)(l[0][x] & 255) | ((uint32_t)(l[1][x] & 255) << 8) |
-                                            ((uint32_t)(l[2][x] & 255) << 16) | ((uint32_t)(l[3][x] & 255) << 24);
-                    *(uint32_t *)(sl + ((size_t)sidx * 3 + x) * F + j) = packed;
-                }
-                if ((threadIdx.x & 15) == 0) ss[sidx * (F / 64) + j / 64] = limb_scale(m);
-                if ((threadIdx.x & 7) == 0) sx[sidx * (F / 32) + j / 32] = half;
+                const int si = v0 / F, j = v0 % F;
+                const int s = (b0 + si == 0) ? K : b0 + si - 1;
+                v = *(const float4 *)(a.ws.act + ((size_t)t * (K + 1) + s) * F + j);
+                *(float4 *)(s_act + v0) = v;
             }
+            const float half = lane_sum<8>((v.x + v.y) + (v.z + v.w));  // 8 threads = 32 values
+            if (live && (threadIdx.x & 7) == 0) s_half[v0 / 32] = half;
         }
         __syncthreads();
-        // products of this batch
+        if (active) {
 #pragma unroll
-        for (int si = 0; si < SB; ++si) {
-            if (si < nb) {
-                const float c = __shfl(my_c, s0 + si, 64);
-                LimbSlice<BITS, CPL> av;
+            for (int si = 0; si < kDownBatch; ++si) {
+                if (si < nb) {
+                    const int s = (b0 + si == 0) ? K : b0 + si - 1;
+                    const float c = lane_bcast(my_c, s);
+                    float av[Q::NV];
 #pragma unroll
-                for (int x = 0; x < 3; ++x)
+                    for (int i = 0; i < Q::NV / 4; ++i) {
+                        const float4 v = *(const float4 *)(s_act + (size_t)si * F + k0 + 4 * i);
+                        av[4 * i] = v.x; av[4 * i + 1] = v.y; av[4 * i + 2] = v.z; av[4 * i + 3] = v.w;
+                    }
+                    float X[Q::NGL];
 #pragma unroll
-                    for (int i = 0; i < Q::NL; ++i) av.L[x][i] = *(const int *)(sl + ((size_t)si * 3 + x) * F + k0 + 4 * i);
+                    for (int g = 0; g < Q::NGL; ++g) {
+                        float x = 0.0f;
 #pragma unroll
-                for (int g = 0; g < Q::NGL; ++g) {
-                    av.S[g] = ss[si * (F / 64) + k0 / 64 + g];
-                    float xs = 0.0f;
+                        for (int hh = 0; hh < Q::GL / 32; ++hh) x += s_half[si * (F / 32) + (k0 + g * 64) / 32 + hh];
+                        X[g] = x;
+                    }
 #pragma unroll
-                    for (int hh = 0; hh < Q::GL / 32; ++hh) xs += sx[si * (F / 32) + (k0 + g * 64) / 32 + hh];
-                    av.X[g] = xs;
+                    for (int i = 0; i < RPW; ++i)
+                        if (rs0 + i < nrs) acc[i] = fmaf(c, qdot_f32<BITS, CPL>(wc[si][i], wsb[si][i], av, X), acc[i]);
                 }
-#pragma unroll
-                for (int i = 0; i < RPW; ++i)
-                    if (rs0 + i < nrs) acc[i] = fmaf(c, qdot<BITS, CPL>(wc[si][i], wsb[si][i], av), acc[i]);
             }
         }
     }
+    if (!active) return;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int rs = rs0 + i;
@@ -519,9 +693,8 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a) {
     }
 }
 
-constexpr int kRpwGateUp = 5;
+constexpr int kRpwGateUp = 3;
 constexpr int kRpwDown = 2;
-constexpr int kSlotBatch = 5;
 
 template <int BITS>
 hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
@@ -529,15 +702,16 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
     if (stage == 0) {  // RMSNorm + router + limbs of h
         const int nch = H / 8, lpr = nch < 64 ? nch : 64, cplr = nch / lpr, rpi = 64 / lpr;
         const int nrs = (E + 1 + rpi - 1) / rpi;
-        int blocks = (nrs + 3) / 4;
-        const int enc_blocks = (H + 255) / 256;
+        int blocks = (nrs + kRouterWaves - 1) / kRouterWaves;
+        const int enc_blocks = (H + 64 * kRouterWaves - 1) / (64 * kRouterWaves);
         if (blocks < enc_blocks) blocks = enc_blocks;
         dim3 grid(blocks, T);
+        const dim3 blk(64 * kRouterWaves);
         switch (cplr) {
-            case 1: hipLaunchKernelGGL(k_router<1>, grid, dim3(256), 0, st, a); break;
-            case 2: hipLaunchKernelGGL(k_router<2>, grid, dim3(256), 0, st, a); break;
-            case 4: hipLaunchKernelGGL(k_router<4>, grid, dim3(256), 0, st, a); break;
-            case 8: hipLaunchKernelGGL(k_router<8>, grid, dim3(256), 0, st, a); break;
+            case 1: hipLaunchKernelGGL(k_router<1>, grid, blk, 0, st, a); break;
+            case 2: hipLaunchKernelGGL(k_router<2>, grid, blk, 0, st, a); break;
+            case 4: hipLaunchKernelGGL(k_router<4>, grid, blk, 0, st, a); break;
+            case 8: hipLaunchKernelGGL(k_router<8>, grid, blk, 0, st, a); break;
             default: return hipErrorInvalidValue;
         }
     } else if (stage == 1) {  // routing + gate/up + SwiGLU
@@ -546,9 +720,12 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
         const int nrs = (K + 1) * F / rpi;
         const int blocks = (nrs + 4 * kRpwGateUp - 1) / (4 * kRpwGateUp);
         dim3 grid(blocks, T);
-        switch (G.cpl) {
-            case 1: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp>), grid, dim3(256), 0, st, a); break;
-            case 2: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp>), grid, dim3(256), 0, st, a); break;
+        const bool wide = E > 512;
+        switch (G.cpl * 2 + (wide ? 1 : 0)) {
+            case 2: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8>), grid, dim3(256), 0, st, a); break;
+            case 3: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16>), grid, dim3(256), 0, st, a); break;
+            case 4: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 8>), grid, dim3(256), 0, st, a); break;
+            case 5: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 16>), grid, dim3(256), 0, st, a); break;
             default: return hipErrorInvalidValue;
         }
     } else if (stage == 2) {  // down + combine + residual
@@ -556,11 +733,16 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
         const int rpi = 64 / Dm.lpr;
         const int nrs = H / rpi;
         const int blocks = (nrs + 4 * kRpwDown - 1) / (4 * kRpwDown);
-        const size_t lds = (size_t)kSlotBatch * 3 * F + (size_t)kSlotBatch * (F / 64) * 4 + (size_t)kSlotBatch * (F / 32) * 4;
         dim3 grid(blocks, T);
+        const size_t per_slot = (size_t)F * 4 + (size_t)(F / 32) * 4;
+        int batch = (int)(kDownLdsBudget / per_slot);
+        if (batch > kDownBatch) batch = kDownBatch;
+        if (batch > K + 1) batch = K + 1;
+        if (batch < 1) batch = 1;
+        const size_t lds = per_slot * batch;
         switch (Dm.cpl) {
-            case 1: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, kSlotBatch>), grid, dim3(256), lds, st, a); break;
-            case 2: hipLaunchKernelGGL((k_down<BITS, 2, kRpwDown, kSlotBatch>), grid, dim3(256), lds, st, a); break;
+            case 1: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown>), grid, dim3(256), lds, st, a, batch); break;
+            case 2: hipLaunchKernelGGL((k_down<BITS, 2, kRpwDown>), grid, dim3(256), lds, st, a, batch); break;
             default: return hipErrorInvalidValue;
         }
     } else {
