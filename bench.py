@@ -128,24 +128,45 @@ def main():
     bytes_per_step = bytes_total / nsteps
     router_bytes = dims.n_experts * dims.hidden * 2
 
-    # per-kernel durations: each stage of the layer enqueued on its own between
-    # events on the launch stream (a separate pass over the same steps)
-    nprobe = min(nsteps, 512)
-    nst = 3
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(nprobe)]
-    for i in range(nprobe):
-        j = i % P
-        evs[i][0].record()
-        for st in range(nst):
-            moe.moe_layer_forward_stage(dims, descs[i % R], pool[j], out[j], T, ridx[j], rw[j], ws, wsb, st)
-            evs[i][st + 1].record()
+    # per-kernel durations: each kernel of the layer timed on its own.  NW
+    # steps (token j, layer j mod R) get a workspace each, filled by one full
+    # forward; then, for each stage, a HIP graph of M back-to-back launches of
+    # that stage alone over those steps is replayed between two events on the
+    # launch stream: duration per launch = elapsed / M.
+    NW = min(P, 64)
+    wss = [torch.empty(wsb, dtype=torch.uint8, device=dev) for _ in range(NW)]
+    for w in wss:
+        moe.moe_workspace_init(w)
+    for j in range(NW):
+        moe.moe_layer_forward(dims, descs[j % R], pool[j], out[j], T, ridx[j], rw[j], wss[j], wsb)
     torch.cuda.synchronize()
-    stage_s = np.array([[evs[i][st].elapsed_time(evs[i][st + 1]) for st in range(nst)] for i in range(nprobe)]) * 1e-3
-    stage_mean = stage_s.mean(axis=0)
-    # algorithmic bytes of the gate/up stage: gate + up codes and scale/bias of
+    M = 512
+    stage_s = []
+    for st in range(3):
+        sg = torch.cuda.Stream()
+        sg.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(sg):
+            with torch.cuda.graph(g, stream=sg):
+                for i in range(M):
+                    j = i % NW
+                    moe.moe_layer_forward_stage(dims, descs[j % R], pool[j], out[j], T, ridx[j], rw[j], wss[j], wsb, st)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        stage_s.append(e0.elapsed_time(e1) * 1e-3 / M)
+        del g
+    stage_mean = np.array(stage_s)
+    # algorithmic bytes of the gate/up kernel: gate + up codes and scale/bias of
     # the distinct selected experts and the shared one
     per_matrix = dims.ffn * dims.hidden * dims.bits // 8 + (dims.ffn * dims.hidden // 64) * 4
-    gu_bytes = float(np.mean([distinct[i % P] for i in range(nprobe)])) * 2 * per_matrix
+    gu_bytes = float(np.mean([distinct[j] for j in range(NW)])) * 2 * per_matrix
     achieved = gu_bytes / stage_mean[1]
 
     result = {

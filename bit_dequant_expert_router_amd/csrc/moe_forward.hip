@@ -19,16 +19,23 @@
 // axis and walks rows; a 64-entry group with scale s and bias b contributes
 //     sum_i (q_i s + b) v_i = s * sum_i q_i v_i + b * sum_i v_i,
 // the group-level form of the pages' fma(nibble, scale*x, bias*x) rewrite.
-// The code products sum_i q_i v_i are taken exactly in integers: each group of
-// the activation vector v is written as V_i * S with S a power of two
-// (max|v| < 2^30 S) and V_i an integer split into four signed 8-bit limbs,
-// V = L3*2^24 + L2*2^16 + L1*2^8 + L0; v_dot4 instructions accumulate q * L per
-// limb (4 codes per instruction, exact int32), and one fp32 combination per
-// group restores s*S*(D3*2^24 + D2*2^16 + D1*2^8 + D0).  Every value within a
-// factor 2^7 of its group's maximum is represented exactly (a float has 24
-// significant bits); smaller ones carry an absolute error below 2^-31 of the
-// maximum, so the result matches an fp32 dot product.  VALU work is ~1.4
-// instructions per weight against ~2.3 for convert-and-FMA.
+//
+// Gate/up (activation h, the normalised token): the code products sum_i q_i h_i
+// are taken exactly in integers.  Each group of h is written as V_i * S with S a
+// power of two (max|h| < 2^26 S) and V_i an integer split into seven signed
+// base-16 digits (limbs) V = sum_x L_x 16^x, L_x in [-8, 7].  Eight limbs of
+// consecutive entries are packed per dword, the operand form of v_dot8_i32_i4;
+// the codes q, made signed as q - 8 by one XOR per 8 codes (4-bit), are the other
+// operand, so one instruction accumulates 8 exact code x limb products.  Per group
+// and limb the sums stay below 2^12; one fp32 combination restores
+// s*S*sum_x D_x 16^x, and the -8 folds into the bias term, (b + 8 s) * sum h.
+// Values within a factor 4 of their group's maximum are represented exactly
+// (a float has 24 significant bits), smaller ones with an absolute error below
+// 2^-27 of it, so the result matches an fp32 dot product; the VALU does 1.0
+// instruction per weight against ~2.3 for convert-and-FMA.
+//
+// Down (activation a = SwiGLU output, widely spread magnitudes): fp32, codes
+// converted with v_cvt_f32_ubyte (byte code order) and folded per group.
 #include "moe_internal.h"
 
 namespace moe {
@@ -121,10 +128,10 @@ __device__ __forceinline__ uint32_t ld_stream4(const uint32_t *p) { return __bui
 // ---------------------------------------------------------------------------
 // fixed-point limbs
 // ---------------------------------------------------------------------------
-constexpr int kLimbs = 4;
-constexpr int kFixBits = 8 * kLimbs - 2;  // |V| <= 2^30
+constexpr int kLimbs = 7;                  // signed base-16 digits
+constexpr int kFixBits = 4 * kLimbs - 2;   // |V| <= 2^26
 
-// Exponent e with max|v| < 2^e, clamped so that 2^(e-30) and 2^(30-e) are
+// Exponent e with max|v| < 2^e, clamped so that 2^(e-26) and 2^(26-e) are
 // normal floats.  NaN / inf maxima are flagged by limb_scale.
 __device__ __forceinline__ int limb_exponent(float m) {
     const uint32_t E = (__float_as_uint(m) >> 23) & 0xFFu;
@@ -132,23 +139,31 @@ __device__ __forceinline__ int limb_exponent(float m) {
     return e < -90 ? -90 : e;
 }
 __device__ __forceinline__ float pow2f(int p) { return __uint_as_float((uint32_t)(p + 127) << 23); }
-// scale S of a group: 2^(e-30), or NaN when the group holds a NaN or an inf
+// scale S of a group: 2^(e-26), or NaN when the group holds a NaN or an inf
 __device__ __forceinline__ float limb_scale(float m) {
     return (m <= 3.4028234663852886e38f) ? pow2f(limb_exponent(m) - kFixBits) : __uint_as_float(0x7FC00000u);
 }
-// integer V = rint(v / S) for finite groups (|V| <= 2^30), 0 otherwise
+// integer V = rint(v / S) for finite groups (|V| <= 2^26), 0 otherwise
 __device__ __forceinline__ int limb_value(float v, float m) {
     if (!(m <= 3.4028234663852886e38f)) return 0;
     return (int)rintf(v * pow2f(kFixBits - limb_exponent(m)));
 }
-// balanced base-256 digits: V = sum_x l[x] 256^x, l[0..2] in [-128, 127], l[3] in [-64, 64]
+// balanced base-16 digits: V = sum_x l[x] 16^x, l[0..5] in [-8, 7], l[6] in [-4, 4]
 __device__ __forceinline__ void limb_split(int V, int (&l)[kLimbs]) {
 #pragma unroll
     for (int x = 0; x < kLimbs - 1; ++x) {
-        l[x] = ((V + 128) & 255) - 128;
-        V = (V - l[x]) >> 8;
+        l[x] = ((V + 8) & 15) - 8;
+        V = (V - l[x]) >> 4;
     }
     l[kLimbs - 1] = V;
+}
+
+// OR over aligned groups of 8 lanes (every lane receives the result)
+__device__ __forceinline__ uint32_t lane_or8(uint32_t v) {
+    v |= dpp_u<kDppXor1>(v);
+    v |= dpp_u<kDppXor2>(v);
+    v |= dpp_u<kDppHalfMirror>(v);
+    return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -264,10 +279,11 @@ struct QSlice {
     static constexpr int C = 128 / BITS;          // codes per 16-byte chunk
     static constexpr int D = 32 / BITS;           // codes per dword
     static constexpr int NV = CPL * C;            // codes per lane per row
-    static constexpr int NL = NV / 4;             // limb dwords per limb
+    static constexpr int NL = NV / 8;             // limb dwords per limb (8 nibbles each)
     static constexpr int GL = NV < 64 ? NV : 64;  // codes of one group inside the slice
     static constexpr int NGL = NV / GL;           // groups touched by the slice
     static constexpr uint32_t kByteMask = BITS == 4 ? 0x0F0F0F0Fu : 0x03030303u;
+    static constexpr float kCodeOffset = BITS == 4 ? 8.0f : 0.0f;  // signed code = q - offset
 };
 
 template <int BITS, int CPL>
@@ -278,6 +294,7 @@ struct LimbSlice {
     float X[Q::NGL];  // sum of the activations of the slice within the group
 };
 
+// nibble-order codes (gate, up) against the lane's limb slice
 template <int BITS, int CPL>
 __device__ __forceinline__ float qdot(const uint4 (&c)[CPL], const uint32_t (&sb)[QSlice<BITS, CPL>::NGL],
                                       const LimbSlice<BITS, CPL> &v) {
@@ -292,13 +309,22 @@ __device__ __forceinline__ float qdot(const uint4 (&c)[CPL], const uint32_t (&sb
         const uint32_t d[4] = {c[j].x, c[j].y, c[j].z, c[j].w};
 #pragma unroll
         for (int w4 = 0; w4 < 4; ++w4) {
+            if constexpr (BITS == 4) {
+                const int q = (int)(d[w4] ^ 0x88888888u);  // eight signed codes q - 8
+                const int li = j * 4 + w4;
+                const int g = (8 * li) / Q::GL;
 #pragma unroll
-            for (int n = 0; n < 8 / BITS; ++n) {
-                const int m = (int)((d[w4] >> (BITS * n)) & Q::kByteMask);
-                const int li = (j * Q::C + w4 * Q::D) / 4 + n;  // limb dword of these 4 codes
-                const int g = (4 * li) / Q::GL;
+                for (int x = 0; x < kLimbs; ++x) acc[g][x] = __builtin_amdgcn_sdot8(q, v.L[x][li], acc[g][x], false);
+            } else {
+                const int qa = (int)(d[w4] & 0x33333333u);         // codes 0..7 of the dword
+                const int qb = (int)((d[w4] >> 2) & 0x33333333u);  // codes 8..15
+                const int li = j * 8 + 2 * w4;
+                const int g = (8 * li) / Q::GL;
 #pragma unroll
-                for (int x = 0; x < kLimbs; ++x) acc[g][x] = __builtin_amdgcn_sdot4(m, v.L[x][li], acc[g][x], false);
+                for (int x = 0; x < kLimbs; ++x) {
+                    acc[g][x] = __builtin_amdgcn_sdot8(qa, v.L[x][li], acc[g][x], false);
+                    acc[g][x] = __builtin_amdgcn_sdot8(qb, v.L[x][li + 1], acc[g][x], false);
+                }
             }
         }
     }
@@ -307,9 +333,10 @@ __device__ __forceinline__ float qdot(const uint4 (&c)[CPL], const uint32_t (&sb
     for (int g = 0; g < Q::NGL; ++g) {
         float f = (float)acc[g][kLimbs - 1];
 #pragma unroll
-        for (int x = kLimbs - 2; x >= 0; --x) f = fmaf(f, 256.0f, (float)acc[g][x]);
-        total = fmaf(bf16_lo(sb[g]) * v.S[g], f, total);
-        total = fmaf(bf16_hi(sb[g]), v.X[g], total);
+        for (int x = kLimbs - 2; x >= 0; --x) f = fmaf(f, 16.0f, (float)acc[g][x]);
+        const float s = bf16_lo(sb[g]);
+        total = fmaf(s * v.S[g], f, total);
+        total = fmaf(fmaf(Q::kCodeOffset, s, bf16_hi(sb[g])), v.X[g], total);
     }
     return total;
 }
@@ -403,10 +430,15 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router(FwdArgs a) {
         int l[kLimbs];
         limb_split(limb_value(h, m), l);
         const float half = lane_sum<32>(h);
-        if (k < H) {
-            int8_t *hl = a.ws.hl + (size_t)t * kLimbs * H;
+        uint32_t packed[kLimbs];
 #pragma unroll
-            for (int x = 0; x < kLimbs; ++x) hl[(size_t)x * H + k] = (int8_t)l[x];
+        for (int xl = 0; xl < kLimbs; ++xl) packed[xl] = lane_or8((uint32_t)(l[xl] & 15) << (4 * (lane & 7)));
+        if (k < H) {
+            uint32_t *hl = (uint32_t *)a.ws.hl + (size_t)t * kLimbs * (H / 8);
+            if ((lane & 7) == 0) {
+#pragma unroll
+                for (int xl = 0; xl < kLimbs; ++xl) hl[(size_t)xl * (H / 8) + k / 8] = packed[xl];
+            }
             if (lane == 0) a.ws.hs[(size_t)t * (H / 64) + k / 64] = limb_scale(m);
             if ((lane & 31) == 0) a.ws.hx[(size_t)t * (H / 32) + k / 32] = half;
         }
@@ -435,7 +467,7 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
 
     __shared__ int s_sel[kMaxTopK];
     __shared__ float s_w[kMaxTopK];
-    __shared__ __align__(16) int8_t s_hl[kLimbs * kMaxDim];  // limbs of h, [kLimbs][H]
+    __shared__ __align__(16) uint32_t s_hl[kLimbs * kMaxDim / 8];  // limbs of h, [kLimbs][H/8]
     __shared__ float s_hs[kMaxDim / 64];
     __shared__ float s_hx[kMaxDim / 32];
 
@@ -445,9 +477,9 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
 
     // stage the limb form of h in LDS, once per block
     {
-        const int4 *src = (const int4 *)(a.ws.hl + (size_t)t * kLimbs * H);
-        const int n16 = kLimbs * H / 16;
-        constexpr int kStage = kLimbs * kMaxDim / 16 / 256;
+        const int4 *src = (const int4 *)((const uint32_t *)a.ws.hl + (size_t)t * kLimbs * (H / 8));
+        const int n16 = kLimbs * H / 32;
+        constexpr int kStage = (kLimbs * kMaxDim / 32 + 255) / 256;
         int4 st0, st1, st2, st3;  // kStage == 4 staged 16-byte pieces per thread
         static_assert(kStage == 4, "staging assumes 4 pieces per thread");
         {
@@ -519,7 +551,7 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
     for (int x = 0; x < kLimbs; ++x)
 #pragma unroll
         for (int i = 0; i < Q::NL / 4; ++i) {
-            const int4 v = *(const int4 *)(s_hl + x * H + k0 + 16 * i);
+            const int4 v = *(const int4 *)(s_hl + x * (H / 8) + k0 / 8 + 4 * i);
             hv.L[x][4 * i + 0] = v.x; hv.L[x][4 * i + 1] = v.y;
             hv.L[x][4 * i + 2] = v.z; hv.L[x][4 * i + 3] = v.w;
         }
@@ -558,24 +590,26 @@ __device__ __forceinline__ float qdot_f32(const uint4 (&c)[CPL], const uint32_t 
                                           const float (&av)[QSlice<BITS, CPL>::NV],
                                           const float (&X)[QSlice<BITS, CPL>::NGL]) {
     using Q = QSlice<BITS, CPL>;
-    float acc[Q::NGL];
+    constexpr int NS = 8 / BITS;  // code slots per byte
+    // one accumulator per slot: slot n holds q << (BITS n) once masked in place,
+    // and the power of two is removed once per group
+    float acc[Q::NGL][NS];
 #pragma unroll
-    for (int g = 0; g < Q::NGL; ++g) acc[g] = 0.0f;
+    for (int g = 0; g < Q::NGL; ++g)
+#pragma unroll
+        for (int n = 0; n < NS; ++n) acc[g][n] = 0.0f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const uint32_t d[4] = {c[j].x, c[j].y, c[j].z, c[j].w};
 #pragma unroll
         for (int w4 = 0; w4 < 4; ++w4) {
 #pragma unroll
-            for (int n = 0; n < 8 / BITS; ++n) {
-                // isolate slot n of every byte in place: byte value = q << (BITS n); the
-                // power of two is undone by scaling the group sum below
+            for (int n = 0; n < NS; ++n) {
                 const uint32_t m = d[w4] & (Q::kByteMask << (BITS * n));
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const int i = j * Q::C + w4 * Q::D + 4 * n + b;
-                    const float q = (float)((m >> (8 * b)) & 0xFFu) * (1.0f / (float)(1 << (BITS * n)));
-                    acc[i / Q::GL] = fmaf(q, av[i], acc[i / Q::GL]);
+                    acc[i / Q::GL][n] = fmaf((float)((m >> (8 * b)) & 0xFFu), av[i], acc[i / Q::GL][n]);
                 }
             }
         }
@@ -583,7 +617,10 @@ __device__ __forceinline__ float qdot_f32(const uint4 (&c)[CPL], const uint32_t 
     float total = 0.0f;
 #pragma unroll
     for (int g = 0; g < Q::NGL; ++g) {
-        total = fmaf(bf16_lo(sb[g]), acc[g], total);
+        float qa = acc[g][NS - 1];
+#pragma unroll
+        for (int n = NS - 2; n >= 0; --n) qa = fmaf(qa, 1.0f / (float)(1 << BITS), acc[g][n]);
+        total = fmaf(bf16_lo(sb[g]), qa, total);
         total = fmaf(bf16_hi(sb[g]), X[g], total);
     }
     return total;
@@ -592,7 +629,7 @@ __device__ __forceinline__ float qdot_f32(const uint4 (&c)[CPL], const uint32_t 
 // k_down processes the K+1 slots in batches of at most kDownBatch; a batch's
 // activations and their half-group sums are staged in LDS once per block.
 constexpr int kDownBatch = 5;
-constexpr size_t kDownLdsBudget = 64 * 1024;
+constexpr int kDownStageValues = 5120;  // activations staged per batch (batch * F <= this)
 
 template <int BITS, int CPL, int RPW>
 __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
@@ -621,8 +658,22 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
     for (int i = 0; i < RPW; ++i) acc[i] = 0.0f;
 
     // slot positions run shared, 0, 1, ..., K-1: the shared expert's loads need no routing
+    constexpr int kStageMax = kDownStageValues / 1024;  // float4 pieces per thread and batch
     for (int b0 = 0; b0 <= K; b0 += batch) {
         const int nb = (K + 1 - b0) < batch ? (K + 1 - b0) : batch;
+        // this batch's activations first: the staging then waits on them only
+        // (loads complete in order), while the weight loads stay in flight
+        float4 stv[kStageMax];
+#pragma unroll
+        for (int r = 0; r < kStageMax; ++r) {
+            const int v0 = threadIdx.x * 4 + 1024 * r;
+            stv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (v0 < nb * F) {
+                const int si = v0 / F, j = v0 % F;
+                const int s = (b0 + si == 0) ? K : b0 + si - 1;
+                stv[r] = *(const float4 *)(a.ws.act + ((size_t)t * (K + 1) + s) * F + j);
+            }
+        }
         // weights of up to kDownBatch slots of this batch, all in flight together
         uint4 wc[kDownBatch][RPW][CPL];
         uint32_t wsb[kDownBatch][RPW][Q::NGL];
@@ -640,18 +691,17 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
             }
         }
         // stage this batch's activations and half-group sums
-        __syncthreads();  // the previous batch is done with the LDS
-        for (int v0 = threadIdx.x * 4; v0 < batch * F; v0 += 1024) {
-            const bool live = v0 < nb * F;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (live) {
-                const int si = v0 / F, j = v0 % F;
-                const int s = (b0 + si == 0) ? K : b0 + si - 1;
-                v = *(const float4 *)(a.ws.act + ((size_t)t * (K + 1) + s) * F + j);
-                *(float4 *)(s_act + v0) = v;
+        if (b0 > 0) __syncthreads();  // the previous batch is done with the LDS
+#pragma unroll
+        for (int r = 0; r < kStageMax; ++r) {
+            const int v0 = threadIdx.x * 4 + 1024 * r;
+            if (1024 * r < batch * F) {  // uniform: whole 8-thread groups are live or not
+                const bool live = v0 < nb * F;
+                if (live) *(float4 *)(s_act + v0) = stv[r];
+                const float4 v = stv[r];
+                const float half = lane_sum<8>((v.x + v.y) + (v.z + v.w));  // 8 threads = 32 values
+                if (live && (threadIdx.x & 7) == 0) s_half[v0 / 32] = half;
             }
-            const float half = lane_sum<8>((v.x + v.y) + (v.z + v.w));  // 8 threads = 32 values
-            if (live && (threadIdx.x & 7) == 0) s_half[v0 / 32] = half;
         }
         __syncthreads();
         if (active) {
@@ -735,7 +785,7 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
         const int blocks = (nrs + 4 * kRpwDown - 1) / (4 * kRpwDown);
         dim3 grid(blocks, T);
         const size_t per_slot = (size_t)F * 4 + (size_t)(F / 32) * 4;
-        int batch = (int)(kDownLdsBudget / per_slot);
+        int batch = kDownStageValues / F;
         if (batch > kDownBatch) batch = kDownBatch;
         if (batch > K + 1) batch = K + 1;
         if (batch < 1) batch = 1;

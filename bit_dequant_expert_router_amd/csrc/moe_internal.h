@@ -22,7 +22,7 @@ struct Workspace {
     int32_t *sel;    // [T][K]   selected experts
     float *coef;     // [T][K+1] combine coefficients (renormalised weights, sigmoid(gs))
     float *act;      // [T][K+1][F] SwiGLU activations of the selected experts and the shared one
-    int8_t *hl;      // [T][4][H]  limbs of the fixed-point normalised tokens
+    int8_t *hl;      // [T][7][H/8] dwords: base-16 limbs of the fixed-point normalised tokens
     float *hs;       // [T][H/64]  group scales (powers of two) of the limbs
     float *hx;       // [T][H/32]  sums of h over each half group
 };
@@ -40,7 +40,7 @@ inline size_t workspace_bytes(const Shape &s, int T) {
     b += align_up((size_t)T * s.K * 4);
     b += align_up((size_t)T * (s.K + 1) * 4);
     b += align_up((size_t)T * (s.K + 1) * s.F * 4);
-    b += align_up((size_t)T * 4 * s.H);
+    b += align_up((size_t)T * 4 * s.H);  // 7 limbs x H/2 bytes fit in 4 H
     b += align_up((size_t)T * (s.H / 64) * 4);
     b += align_up((size_t)T * (s.H / 32) * 4);
     return b;

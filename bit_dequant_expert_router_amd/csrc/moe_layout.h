@@ -9,11 +9,16 @@
 //
 // Codes of a row are stored in 16-byte chunks.  A chunk holds C = 128/bits
 // consecutive codes of the row ("logical chunk" L covers columns
-// [L*C, L*C + C)).  Inside a chunk, code i sits in dword i / D (D = 32/bits
-// codes per dword), byte (i % D) % 4, bits [bits*((i % D) / 4), +bits) of that
-// byte.  So for 4-bit codes the low nibbles of a dword's bytes hold codes
-// 0..3 and the high nibbles codes 4..7: the kernel isolates each half with one
-// mask and converts bytes directly.
+// [L*C, L*C + C)), D = 32/bits codes per dword; code i sits in dword i / D at a
+// bit position t = i % D that depends on the matrix's order:
+//   nibble order (gate, up): 4-bit code t at bits [4t, 4t+4); 2-bit code t < 8
+//     at bits [4t, 4t+2) and code t >= 8 at bits [4(t-8)+2, 4(t-8)+4).  The
+//     dword itself (4-bit) or each of d & 0x33333333 and (d >> 2) & 0x33333333
+//     (2-bit) is then eight 4-bit lanes holding consecutive codes, the operand
+//     form of v_dot8.
+//   byte order (down): code t in byte t % 4 at bits [bits*(t/4), +bits) of
+//     that byte.  One mask per bit slot leaves four codes in bytes, the operand
+//     form of v_cvt_f32_ubyte{0..3}.
 //
 // Chunks are ordered for coalescing: a row of NC chunks is read by LPR =
 // min(NC, 64) lanes, each lane owning CPL = NC/LPR logically consecutive
@@ -39,8 +44,11 @@ constexpr int kMaxTopK = 16;
 constexpr int kMinDim = 128;
 constexpr int kMaxDim = 4096;
 
+enum CodeOrder { kOrderNibble = 0, kOrderByte = 1 };
+
 struct QMat {
     int rows, cols, bits;
+    int order;       // CodeOrder
     int row_bytes;   // cols * bits / 8
     int ngroups;     // cols / 64
     int nchunks;     // chunks per row
@@ -57,11 +65,12 @@ struct ExpertLayout {
 
 MOE_HD int codes_per_chunk(int bits) { return 128 / bits; }
 
-MOE_HD QMat make_qmat(int rows, int cols, int bits) {
+MOE_HD QMat make_qmat(int rows, int cols, int bits, int order) {
     QMat q;
     q.rows = rows;
     q.cols = cols;
     q.bits = bits;
+    q.order = order;
     q.row_bytes = cols * bits / 8;
     q.ngroups = cols / kGroup;
     q.nchunks = cols / codes_per_chunk(bits);
@@ -74,9 +83,9 @@ MOE_HD QMat make_qmat(int rows, int cols, int bits) {
 
 MOE_HD ExpertLayout make_layout(int H, int F, int bits) {
     ExpertLayout L;
-    L.m[0] = make_qmat(F, H, bits);
-    L.m[1] = make_qmat(F, H, bits);
-    L.m[2] = make_qmat(H, F, bits);
+    L.m[0] = make_qmat(F, H, bits, kOrderNibble);
+    L.m[1] = make_qmat(F, H, bits, kOrderNibble);
+    L.m[2] = make_qmat(H, F, bits, kOrderByte);
     size_t off = 0;
     for (int i = 0; i < 3; ++i) {
         L.m[i].codes_off = off;
@@ -93,12 +102,18 @@ MOE_HD ExpertLayout make_layout(int H, int F, int bits) {
 // physical chunk position of logical chunk L in a row
 MOE_HD int phys_chunk(const QMat &q, int L) { return (L / q.cpl) + q.lpr * (L % q.cpl); }
 
-// position of code i (0 <= i < C) inside a 16-byte chunk: byte index and bit shift
-MOE_HD void code_pos(int bits, int i, int &byte, int &shift) {
+// position of code i (0 <= i < C) inside a 16-byte chunk: dword index and
+// bit shift within that dword
+MOE_HD void code_pos(int bits, int order, int i, int &dword, int &shift) {
     const int D = 32 / bits;
     const int t = i % D;
-    byte = 4 * (i / D) + (t % 4);
-    shift = bits * (t / 4);
+    dword = i / D;
+    if (order == kOrderByte)
+        shift = 8 * (t % 4) + bits * (t / 4);
+    else if (bits == 4)
+        shift = 4 * t;
+    else
+        shift = (t < 8) ? 4 * t : 4 * (t - 8) + 2;
 }
 
 }  // namespace moe

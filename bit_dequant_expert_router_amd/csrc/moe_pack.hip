@@ -51,14 +51,14 @@ __device__ __forceinline__ uint16_t uniform_bf16(uint64_t word, double mul, doub
 
 // Place C codes (provided by `code_of(i)`) into a 16-byte chunk.
 template <typename CodeFn>
-__device__ __forceinline__ uint4 make_chunk(int bits, CodeFn code_of) {
+__device__ __forceinline__ uint4 make_chunk(int bits, int order, CodeFn code_of) {
     uint32_t d[4] = {0u, 0u, 0u, 0u};
     const int C = 128 / bits;
     const uint32_t mask = (1u << bits) - 1u;
     for (int i = 0; i < C; ++i) {
-        int byte, shift;
-        code_pos(bits, i, byte, shift);
-        d[byte >> 2] |= ((uint32_t)code_of(i) & mask) << (8 * (byte & 3) + shift);
+        int dw, shift;
+        code_pos(bits, order, i, dw, shift);
+        d[dw] |= ((uint32_t)code_of(i) & mask) << shift;
     }
     return make_uint4(d[0], d[1], d[2], d[3]);
 }
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs a) {
             const int Lc = (p % q.lpr) * q.cpl + p / q.lpr;  // logical chunk stored at p
             const int C = 128 / q.bits;
             const uint8_t *src = a.codes[m] + (size_t)r * q.cols + (size_t)Lc * C;
-            const uint4 v = make_chunk(q.bits, [&](int c) { return src[c]; });
+            const uint4 v = make_chunk(q.bits, q.order, [&](int c) { return src[c]; });
             *(uint4 *)(a.dst + q.codes_off + (size_t)r * q.row_bytes + (size_t)p * 16) = v;
         } else {
             const size_t j = i - w.chunk_begin[3];
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void k_generate(GenArgs a, size_t expert_bytes
             const uint64_t z0 = mix64(base + (uint64_t)(w0 + 1) * kGamma);
             const uint64_t z1 = mix64(base + (uint64_t)(w0 + 2) * kGamma);
             const int bits = q.bits;
-            const uint4 v = make_chunk(bits, [&](int c) {
+            const uint4 v = make_chunk(bits, q.order, [&](int c) {
                 const uint64_t zz = (c < per_word) ? z0 : z1;
                 return (uint32_t)(zz >> (bits * (c % per_word)));
             });
