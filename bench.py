@@ -16,6 +16,7 @@ Prints one JSON line.  `value` is tokens/s with all inputs resident in HBM.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +27,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_BPS = 8.0e12  # MI355X HBM3E peak
+
+# HBM traffic of k_gateup per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+# (profiles/layer4_kernels_pmc_traffic.md), valid only for the kernel source it
+# was measured on; FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0, the ratios
+# of bytes moved to counts reported for a 256 MiB copy.
+GATEUP_TRAFFIC = {"source_sha256_prefix": "5d1ef4fae1e76c30", "workload": "layer4",
+                  "fetch_kib": 11701.1, "write_kib": 26.8, "fetch_scale": 2.0, "write_scale": 1.0}
 
 
 def parse_args():
@@ -39,6 +47,9 @@ def parse_args():
     p.add_argument("--mode", default="graph", choices=["graph", "api"],
                    help="graph: the timed steps are one captured HIP graph; api: one ABI call per step")
     p.add_argument("--cpu-sample", type=int, default=24, help="tokens for the oracle CPU baseline (0: skip)")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="before timing, copy a buffer of this many MiB 8 times (a kernel of known traffic "
+                        "for scaling profiler byte counters)")
     p.add_argument("--quiet", action="store_true")
     return p.parse_args()
 
@@ -87,6 +98,15 @@ def main():
     def step(i):
         j = i % P
         moe.moe_layer_forward(dims, descs[i % R], pool[j], out[j], T, ridx[j], rw[j], ws, wsb)
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # warmup
     for i in range(args.warmup):
@@ -168,6 +188,13 @@ def main():
     per_matrix = dims.ffn * dims.hidden * dims.bits // 8 + (dims.ffn * dims.hidden // 64) * 4
     gu_bytes = float(np.mean([distinct[j] for j in range(NW)])) * 2 * per_matrix
     achieved = gu_bytes / stage_mean[1]
+    traffic = None
+    src = os.path.join(ROOT, "bit_dequant_expert_router_amd", "csrc", "moe_forward.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    tr = GATEUP_TRAFFIC
+    if sha.startswith(tr["source_sha256_prefix"]) and wl.name == tr["workload"]:
+        traffic = round((tr["fetch_kib"] * tr["fetch_scale"] + tr["write_kib"] * tr["write_scale"]) * 1024)
 
     result = {
         "metric": "MoE-layer decode tokens/s (effective expert-weight HBM GB/s and % of peak alongside)",
@@ -199,7 +226,7 @@ def main():
             "peak": HBM_PEAK_BPS / 1e9,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_BPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "bytes_per_launch": round(gu_bytes),
             "launch_us": round(float(stage_mean[1]) * 1e6, 3),
         },
@@ -243,19 +270,25 @@ def cpu_baseline(args, wl, dims):
             for e in list(idx) + [dims.n_experts]:
                 fetch(l)(int(e))
     log(args, f"[bench] cpu baseline: oracle on {n} steps x {wl.n_tokens} tokens, {oracle.threads()} threads")
+    # passes over the sample until about 1.5 s of wall time (x the oracle's threads of CPU work)
+    done = 0
     t0 = time.perf_counter()
-    for i in range(n):
-        l = i % R % len(dense)
-        for t in range(wl.n_tokens):
-            oracle.layer(dims, xs[i, t], dense[l], fetch(l))
-    el = time.perf_counter() - t0
+    while True:
+        for i in range(n):
+            l = i % R % len(dense)
+            for t in range(wl.n_tokens):
+                oracle.layer(dims, xs[i, t], dense[l], fetch(l))
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= 1.5:
+            break
     return {
-        "value": round(n * wl.n_tokens / el, 3),
+        "value": round(done * n * wl.n_tokens / el, 3),
         "unit": "tokens/s",
         "cores": oracle.threads(),
         "kind": "oracle",
-        "sample": f"{n} steps of the {wl.name} workload ({n * wl.n_tokens} tokens, layers rotating), "
-                  f"fp64 C oracle, {el:.1f} s",
+        "sample": f"{done} passes over {n} steps of the {wl.name} workload ({n * wl.n_tokens} tokens, "
+                  f"layers rotating), fp64 C oracle, {el:.1f} s wall on {oracle.threads()} threads",
     }
 
 
