@@ -63,6 +63,12 @@ size_t workspace_bytes_checked(const moe_dims_t *dims, int32_t n_tokens) {
     return workspace_bytes(shape_of(dims), n_tokens);
 }
 
+// batches of kGroupMinTokens or more tokens are grouped by expert
+hipError_t launch_layer(const FwdArgs &a, hipStream_t stream) {
+    if (a.T >= kGroupMinTokens && a.T * a.s.K <= kGroupMaxAssign) return launch_grouped(a, stream);
+    return launch_forward(a, stream);
+}
+
 bool overlap_not_equal(const void *a, const void *b, size_t bytes) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     if (x == y) return false;
@@ -178,7 +184,7 @@ int moe_layer_forward(const moe_dims_t *dims, const moe_layer_t *layer, const fl
     rc = check_layer(layer);
     if (rc != MOE_OK) return rc;
     const FwdArgs a = make_fwd(dims, layer, x, y, n_tokens, route_idx, route_w, workspace);
-    return hip_status(launch_forward(a, (hipStream_t)stream));
+    return hip_status(launch_layer(a, (hipStream_t)stream));
 }
 
 int moe_layer_forward_stage(const moe_dims_t *dims, const moe_layer_t *layer, const float *x, float *y,
@@ -208,7 +214,7 @@ int moe_stack_forward(const moe_dims_t *dims, const moe_layer_t *layers, int32_t
         const FwdArgs a = make_fwd(dims, &layers[l], l == 0 ? x : y, y, n_tokens,
                                    route_idx ? route_idx + l * per_layer : nullptr,
                                    route_w ? route_w + l * per_layer : nullptr, workspace);
-        if (hip_status(launch_forward(a, (hipStream_t)stream)) != MOE_OK) return MOE_ERR_HIP;
+        if (hip_status(launch_layer(a, (hipStream_t)stream)) != MOE_OK) return MOE_ERR_HIP;
     }
     return MOE_OK;
 }

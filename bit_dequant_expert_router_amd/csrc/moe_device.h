@@ -1,0 +1,389 @@
+// moe_device.h -- device helpers shared by the layer kernels (library-internal).
+//
+// Dequantised dot products.  A lane owns a contiguous slice of the reduction
+// axis and walks rows; a 64-entry group with scale s and bias b contributes
+//     sum_i (q_i s + b) v_i = s * sum_i q_i v_i + b * sum_i v_i,
+// the group-level form of the pages' fma(nibble, scale*x, bias*x) rewrite.
+//
+// Gate/up (activation h, the normalised token): the code products sum_i q_i h_i
+// are taken exactly in integers.  Each group of h is written as V_i * S with S a
+// power of two (max|h| < 2^26 S) and V_i an integer split into seven signed
+// base-16 digits (limbs) V = sum_x L_x 16^x, L_x in [-8, 7].  Eight limbs of
+// consecutive entries are packed per dword, the operand form of v_dot8_i32_i4;
+// the codes q, made signed as q - 8 by one XOR per 8 codes (4-bit), are the other
+// operand, so one instruction accumulates 8 exact code x limb products.  Per group
+// and limb the sums stay below 2^12; one fp32 combination restores
+// s*S*sum_x D_x 16^x, and the -8 folds into the bias term, (b + 8 s) * sum h.
+// Values within a factor 4 of their group's maximum are represented exactly
+// (a float has 24 significant bits), smaller ones with an absolute error below
+// 2^-27 of it, so the result matches an fp32 dot product; the VALU does 1.0
+// instruction per weight against ~2.3 for convert-and-FMA.
+//
+// Down (activation a = SwiGLU output, widely spread magnitudes): fp32, codes
+// converted with v_cvt_f32_ubyte (byte code order) and folded per group.
+#pragma once
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+
+__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------
+// cross-lane reductions on the VALU: DPP quad permutations and row mirrors
+// inside 16-lane rows, then v_permlane16_swap / v_permlane32_swap across rows.
+// Each step is one VALU instruction (no LDS round trip).  Callers keep every
+// lane of a reduced group active.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside each half row
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i inside each row
+
+struct SumOp {
+    __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct MaxOp {  // keeps a NaN (fmaxf would drop it)
+    __device__ __forceinline__ float operator()(float a, float b) const {
+        return (a != a || b != b) ? (a + b) : fmaxf(a, b);
+    }
+};
+
+// reduce over aligned groups of W lanes (W a power of two <= 64); every lane
+// of a group receives the result
+template <int W, typename Op>
+__device__ __forceinline__ float lane_reduce(float v, Op op) {
+    if constexpr (W >= 2) v = op(v, __uint_as_float(dpp_u<kDppXor1>(__float_as_uint(v))));
+    if constexpr (W >= 4) v = op(v, __uint_as_float(dpp_u<kDppXor2>(__float_as_uint(v))));
+    if constexpr (W >= 8) v = op(v, __uint_as_float(dpp_u<kDppHalfMirror>(__float_as_uint(v))));
+    if constexpr (W >= 16) v = op(v, __uint_as_float(dpp_u<kDppMirror>(__float_as_uint(v))));
+    if constexpr (W >= 32) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = op(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    }
+    if constexpr (W >= 64) {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = op(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    }
+    return v;
+}
+
+template <int W>
+__device__ __forceinline__ float lane_sum(float v) { return lane_reduce<W>(v, SumOp()); }
+template <int W>
+__device__ __forceinline__ float lane_max(float v) { return lane_reduce<W>(v, MaxOp()); }
+
+// sum over aligned groups of a runtime width (uniform across the wave)
+__device__ __forceinline__ float lane_group_sum(float v, int width) {
+    switch (width) {
+        case 1: return v;
+        case 2: return lane_sum<2>(v);
+        case 4: return lane_sum<4>(v);
+        case 8: return lane_sum<8>(v);
+        case 16: return lane_sum<16>(v);
+        case 32: return lane_sum<32>(v);
+        default: return lane_sum<64>(v);
+    }
+}
+
+// value of a wave-uniform lane index
+__device__ __forceinline__ int lane_bcast(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+__device__ __forceinline__ float lane_bcast(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
+__device__ __forceinline__ float sigmoidf_(float t) { return 1.0f / (1.0f + expf(-t)); }
+
+__device__ __forceinline__ float nan_max(float a, float b) { return MaxOp()(a, b); }
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// streaming 16-byte load of weights that are read once per call
+__device__ __forceinline__ uint4 ld_stream16(const void *p) {
+    const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_stream4(const uint32_t *p) { return __builtin_nontemporal_load(p); }
+
+// ---------------------------------------------------------------------------
+// fixed-point limbs
+// ---------------------------------------------------------------------------
+constexpr int kLimbs = 7;                  // signed base-16 digits
+constexpr int kFixBits = 4 * kLimbs - 2;   // |V| <= 2^26
+
+// Exponent e with max|v| < 2^e, clamped so that 2^(e-26) and 2^(26-e) are
+// normal floats.  NaN / inf maxima are flagged by limb_scale.
+__device__ __forceinline__ int limb_exponent(float m) {
+    const uint32_t E = (__float_as_uint(m) >> 23) & 0xFFu;
+    int e = (E == 0 ? 1 : (int)E) - 126;  // m < 2^e
+    return e < -90 ? -90 : e;
+}
+__device__ __forceinline__ float pow2f(int p) { return __uint_as_float((uint32_t)(p + 127) << 23); }
+// scale S of a group: 2^(e-26), or NaN when the group holds a NaN or an inf
+__device__ __forceinline__ float limb_scale(float m) {
+    return (m <= 3.4028234663852886e38f) ? pow2f(limb_exponent(m) - kFixBits) : __uint_as_float(0x7FC00000u);
+}
+// integer V = rint(v / S) for finite groups (|V| <= 2^26), 0 otherwise
+__device__ __forceinline__ int limb_value(float v, float m) {
+    if (!(m <= 3.4028234663852886e38f)) return 0;
+    return (int)rintf(v * pow2f(kFixBits - limb_exponent(m)));
+}
+// balanced base-16 digits: V = sum_x l[x] 16^x, l[0..5] in [-8, 7], l[6] in [-4, 4]
+__device__ __forceinline__ void limb_split(int V, int (&l)[kLimbs]) {
+#pragma unroll
+    for (int x = 0; x < kLimbs - 1; ++x) {
+        l[x] = ((V + 8) & 15) - 8;
+        V = (V - l[x]) >> 4;
+    }
+    l[kLimbs - 1] = V;
+}
+
+// OR over aligned groups of 8 lanes (every lane receives the result)
+__device__ __forceinline__ uint32_t lane_or8(uint32_t v) {
+    v |= dpp_u<kDppXor1>(v);
+    v |= dpp_u<kDppXor2>(v);
+    v |= dpp_u<kDppHalfMirror>(v);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// routing: softmax -> top-K -> renormalise, by one wave.  Lane k < K ends up
+// holding the k-th selected expert and its renormalised weight.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t route_key(float z, int e) {
+    uint32_t u = (z == 0.0f) ? 0u : __float_as_uint(z);  // -0 and +0 are one key
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)e);
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint32_t blo, uint32_t bhi) {
+    const uint64_t b = ((uint64_t)bhi << 32) | blo;
+    return b > a ? b : a;
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+    return max_u64(v, dpp_u<CTRL>((uint32_t)v), dpp_u<CTRL>((uint32_t)(v >> 32)));
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = dpp_max_u64<kDppXor1>(v);
+    v = dpp_max_u64<kDppXor2>(v);
+    v = dpp_max_u64<kDppHalfMirror>(v);
+    v = dpp_max_u64<kDppMirror>(v);
+    {
+        const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+        v = max_u64(((uint64_t)hi[0] << 32) | lo[0], lo[1], hi[1]);
+    }
+    {
+        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+        v = max_u64(((uint64_t)hi[0] << 32) | lo[0], lo[1], hi[1]);
+    }
+    return v;
+}
+
+__device__ __forceinline__ float route_key_value(uint64_t key) {
+    const uint32_t u = (uint32_t)(key >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// the router logits of one token, EPL per lane (clamped index: all loads in flight at once)
+template <int EPL>
+__device__ __forceinline__ void load_logits(const float *__restrict__ z, int E, float (&zv)[EPL]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        zv[i] = z[e < E ? e : E - 1];
+    }
+}
+
+// bitonic sort of n = EPL keys, descending
+template <int EPL>
+__device__ __forceinline__ void sort_desc(uint64_t (&key)[EPL]) {
+#pragma unroll
+    for (int k = 2; k <= EPL; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const bool desc = (i & k) == 0;
+                    const uint64_t a = key[i], b = key[l];
+                    const bool swap = desc ? (a < b) : (a > b);
+                    key[i] = swap ? b : a;
+                    key[l] = swap ? a : b;
+                }
+            }
+}
+
+// Softmax -> top-K -> renormalise by one wave.  Each lane sorts its EPL keys;
+// every round takes the wave maximum of the list heads and the winning lane
+// pops its head.  Lane k < K ends with the k-th selected expert and weight.
+template <int EPL>
+__device__ __forceinline__ void route_wave(const float (&zv)[EPL], int E, int K, int &my_sel, float &my_w) {
+    const int lane = threadIdx.x & 63;
+    uint64_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = (e < E) ? route_key(zv[i], e) : 0ull;
+    }
+    sort_desc<EPL>(key);
+    my_sel = 0;
+    float my_z = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        const uint64_t best = wave_max_u64(key[0]);
+        const bool win = key[0] == best;  // keys are unique: the index is part of the key
+#pragma unroll
+        for (int i = 0; i < EPL - 1; ++i) key[i] = win ? key[i + 1] : key[i];
+        key[EPL - 1] = win ? 0ull : key[EPL - 1];
+        if (lane == k) {
+            my_sel = (int)(~(uint32_t)best);
+            my_z = route_key_value(best);
+        }
+    }
+    // softmax restricted to the selection == renormalised full softmax
+    const float z0 = lane_bcast(my_z, 0);
+    const float p = (lane < K) ? expf(my_z - z0) : 0.0f;
+    const float denom = lane_sum<64>(p);
+    my_w = p / denom;
+}
+
+// ---------------------------------------------------------------------------
+// dequantised dot product of one row slice with a lane's limb slice
+// ---------------------------------------------------------------------------
+template <int BITS, int CPL>
+struct QSlice {
+    static constexpr int C = 128 / BITS;          // codes per 16-byte chunk
+    static constexpr int D = 32 / BITS;           // codes per dword
+    static constexpr int NV = CPL * C;            // codes per lane per row
+    static constexpr int NL = NV / 8;             // limb dwords per limb (8 nibbles each)
+    static constexpr int GL = NV < 64 ? NV : 64;  // codes of one group inside the slice
+    static constexpr int NGL = NV / GL;           // groups touched by the slice
+    static constexpr uint32_t kByteMask = BITS == 4 ? 0x0F0F0F0Fu : 0x03030303u;
+    static constexpr float kCodeOffset = BITS == 4 ? 8.0f : 0.0f;  // signed code = q - offset
+};
+
+template <int BITS, int CPL>
+struct LimbSlice {
+    using Q = QSlice<BITS, CPL>;
+    int L[kLimbs][Q::NL];
+    float S[Q::NGL];  // group scale (power of two)
+    float X[Q::NGL];  // sum of the activations of the slice within the group
+};
+
+// nibble-order codes (gate, up) against the lane's limb slice
+template <int BITS, int CPL>
+__device__ __forceinline__ float qdot(const uint4 (&c)[CPL], const uint32_t (&sb)[QSlice<BITS, CPL>::NGL],
+                                      const LimbSlice<BITS, CPL> &v) {
+    using Q = QSlice<BITS, CPL>;
+    int acc[Q::NGL][kLimbs];
+#pragma unroll
+    for (int g = 0; g < Q::NGL; ++g)
+#pragma unroll
+        for (int x = 0; x < kLimbs; ++x) acc[g][x] = 0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const uint32_t d[4] = {c[j].x, c[j].y, c[j].z, c[j].w};
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+            if constexpr (BITS == 4) {
+                const int q = (int)(d[w4] ^ 0x88888888u);  // eight signed codes q - 8
+                const int li = j * 4 + w4;
+                const int g = (8 * li) / Q::GL;
+#pragma unroll
+                for (int x = 0; x < kLimbs; ++x) acc[g][x] = __builtin_amdgcn_sdot8(q, v.L[x][li], acc[g][x], false);
+            } else {
+                const int qa = (int)(d[w4] & 0x33333333u);         // codes 0..7 of the dword
+                const int qb = (int)((d[w4] >> 2) & 0x33333333u);  // codes 8..15
+                const int li = j * 8 + 2 * w4;
+                const int g = (8 * li) / Q::GL;
+#pragma unroll
+                for (int x = 0; x < kLimbs; ++x) {
+                    acc[g][x] = __builtin_amdgcn_sdot8(qa, v.L[x][li], acc[g][x], false);
+                    acc[g][x] = __builtin_amdgcn_sdot8(qb, v.L[x][li + 1], acc[g][x], false);
+                }
+            }
+        }
+    }
+    float total = 0.0f;
+#pragma unroll
+    for (int g = 0; g < Q::NGL; ++g) {
+        float f = (float)acc[g][kLimbs - 1];
+#pragma unroll
+        for (int x = kLimbs - 2; x >= 0; --x) f = fmaf(f, 16.0f, (float)acc[g][x]);
+        const float s = bf16_lo(sb[g]);
+        total = fmaf(s * v.S[g], f, total);
+        total = fmaf(fmaf(Q::kCodeOffset, s, bf16_hi(sb[g])), v.X[g], total);
+    }
+    return total;
+}
+
+template <int BITS, int CPL>
+__device__ __forceinline__ void load_row(const uint8_t *__restrict__ ex, const QMat &q, int r, int lr,
+                                         uint4 (&c)[CPL], uint32_t (&sb)[QSlice<BITS, CPL>::NGL]) {
+    using Q = QSlice<BITS, CPL>;
+    const uint8_t *row = ex + q.codes_off + (size_t)r * q.row_bytes;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) c[j] = ld_stream16(row + 16 * (lr + q.lpr * j));
+    const uint32_t *sbr = (const uint32_t *)(ex + q.sb_off) + (size_t)r * q.ngroups + (lr * Q::NV) / kGroup;
+#pragma unroll
+    for (int g = 0; g < Q::NGL; ++g) sb[g] = ld_stream4(sbr + g);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 dequantised dot product for byte-order codes (down projection)
+// ---------------------------------------------------------------------------
+template <int BITS, int CPL>
+__device__ __forceinline__ float qdot_f32(const uint4 (&c)[CPL], const uint32_t (&sb)[QSlice<BITS, CPL>::NGL],
+                                          const float (&av)[QSlice<BITS, CPL>::NV],
+                                          const float (&X)[QSlice<BITS, CPL>::NGL]) {
+    using Q = QSlice<BITS, CPL>;
+    constexpr int NS = 8 / BITS;  // code slots per byte
+    // one accumulator per slot: slot n holds q << (BITS n) once masked in place,
+    // and the power of two is removed once per group
+    float acc[Q::NGL][NS];
+#pragma unroll
+    for (int g = 0; g < Q::NGL; ++g)
+#pragma unroll
+        for (int n = 0; n < NS; ++n) acc[g][n] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const uint32_t d[4] = {c[j].x, c[j].y, c[j].z, c[j].w};
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+#pragma unroll
+            for (int n = 0; n < NS; ++n) {
+                const uint32_t m = d[w4] & (Q::kByteMask << (BITS * n));
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int i = j * Q::C + w4 * Q::D + 4 * n + b;
+                    acc[i / Q::GL][n] = fmaf((float)((m >> (8 * b)) & 0xFFu), av[i], acc[i / Q::GL][n]);
+                }
+            }
+        }
+    }
+    float total = 0.0f;
+#pragma unroll
+    for (int g = 0; g < Q::NGL; ++g) {
+        float qa = acc[g][NS - 1];
+#pragma unroll
+        for (int n = NS - 2; n >= 0; --n) qa = fmaf(qa, 1.0f / (float)(1 << BITS), acc[g][n]);
+        total = fmaf(bf16_lo(sb[g]), qa, total);
+        total = fmaf(bf16_hi(sb[g]), X[g], total);
+    }
+    return total;
+}
+
+}  // namespace
+
+}  // namespace moe

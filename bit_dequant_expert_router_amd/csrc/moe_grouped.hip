@@ -1,0 +1,390 @@
+// moe_grouped.hip -- the expert layer for a batch of tokens, grouped by expert.
+//
+// A batch of T decode tokens routes T*K (token, slot) assignments over the
+// experts; with T = 32 and K = 10 (the model's native routing, juejin post on
+// Flash-MoE, "为什么 397B 的模型能塞进 48GB") about 240 of 512 experts are
+// touched, most by one or two tokens.  Reading each touched expert once and
+// applying it to all of its tokens is what saves HBM bytes; the per-expert
+// token counts are far too small for a dense tile, so the routed experts stay
+// on the dequant-GEMV kernels with a loop over each expert's tokens.
+//
+//   k_router        (moe_forward.hip) RMSNorm, router logits and the limb form of h
+//   k_route_group   one block: softmax/top-K/renormalise of every token, then a
+//                   histogram of assignments per expert, an exclusive scan and a
+//                   stable scatter (token order kept inside each expert), and the
+//                   compact list of touched experts
+//   k_grouped_gateup  one block per (touched expert, row chunk): gate+up rows read
+//                   once, applied to every token of the expert, SwiGLU; the shared
+//                   expert gets its own blocks over all tokens
+//   k_grouped_down  same for the down projection, writing one output vector per
+//                   (token, slot)
+//   k_combine       out = x + sum_k w_k y_k + sigmoid(g_s) y_shared, in slot order
+#include "moe_device.h"
+
+namespace moe {
+
+namespace {
+
+struct GroupView {
+    int G;  // bound on touched experts
+    const int32_t *n_touched;
+    const int32_t *expert;
+    const int32_t *first;
+    const int32_t *count;
+    const int32_t *perm;
+};
+
+__device__ __forceinline__ GroupView group_view(const FwdArgs &a) {
+    GroupView g;
+    g.G = (a.T * a.s.K < a.s.E) ? a.T * a.s.K : a.s.E;
+    g.n_touched = a.ws.grp;
+    g.expert = a.ws.grp + 4;
+    g.first = g.expert + (g.G + 1);
+    g.count = g.first + (g.G + 1);
+    g.perm = g.count + (g.G + 1);
+    return g;
+}
+
+// exclusive prefix sum over the 64 lanes of a wave (small, one-time use)
+__device__ __forceinline__ int wave_excl_scan(int v) {
+    const int lane = threadIdx.x & 63;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+    }
+    return incl - v;
+}
+
+// ---------------------------------------------------------------------------
+// k_route_group: routing of every token and grouping of assignments by expert
+// ---------------------------------------------------------------------------
+template <int EPL>
+__global__ __launch_bounds__(1024) void k_route_group(FwdArgs a) {
+    const int T = a.T, E = a.s.E, K = a.s.K;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int TK = T * K;
+    GroupView gv = group_view(a);
+    int32_t *expert = (int32_t *)gv.expert;
+    int32_t *first = (int32_t *)gv.first;
+    int32_t *count = (int32_t *)gv.count;
+    int32_t *perm = (int32_t *)gv.perm;
+
+    __shared__ int s_sel[kGroupMaxAssign];
+    __shared__ int s_cnt[kMaxExperts];
+    __shared__ int s_off[kMaxExperts];
+    __shared__ int s_tch[kMaxExperts];
+
+    for (int i = threadIdx.x; i < E; i += 1024) s_cnt[i] = 0;
+    // routing, one token per wave
+    for (int t = wave; t < T; t += 16) {
+        float zv[EPL];
+        load_logits<EPL>(a.ws.z + (size_t)t * E, E, zv);
+        int my_sel;
+        float my_w;
+        route_wave<EPL>(zv, E, K, my_sel, my_w);
+        if (lane < K) {
+            s_sel[t * K + lane] = my_sel;
+            a.ws.sel[t * K + lane] = my_sel;
+            a.ws.coef[t * (K + 1) + lane] = my_w;
+            if (a.route_idx) a.route_idx[t * K + lane] = my_sel;
+            if (a.route_w) a.route_w[t * K + lane] = my_w;
+        } else if (lane == K) {
+            a.ws.coef[t * (K + 1) + K] = sigmoidf_(a.ws.gs[t]);
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < TK; i += 1024) atomicAdd(&s_cnt[s_sel[i]], 1);
+    __syncthreads();
+    // exclusive scans of the counts and of the touched flags (E <= 1024: 16 per lane)
+    if (wave == 0) {
+        constexpr int kPer = kMaxExperts / 64;
+        int c[kPer];
+        int sc = 0, sf = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = lane * kPer + i;
+            c[i] = (e < E) ? s_cnt[e] : 0;
+            sc += c[i];
+            sf += c[i] > 0 ? 1 : 0;
+        }
+        int pc = wave_excl_scan(sc), pf = wave_excl_scan(sf);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = lane * kPer + i;
+            if (e < E) {
+                s_off[e] = pc;
+                s_tch[e] = pf;
+            }
+            pc += c[i];
+            pf += c[i] > 0 ? 1 : 0;
+        }
+        if (lane == 63) a.ws.grp[0] = pf;  // number of touched experts
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 1024) {
+        if (s_cnt[e] > 0) {
+            const int u = s_tch[e];
+            expert[u] = e;
+            first[u] = s_off[e];
+            count[u] = s_cnt[e];
+        }
+    }
+    // stable scatter: rank of an assignment among the earlier ones of its expert
+    for (int i = threadIdx.x; i < TK; i += 1024) {
+        const int e = s_sel[i];
+        int r = 0;
+        for (int j = 0; j < i; ++j) r += (s_sel[j] == e) ? 1 : 0;
+        perm[s_off[e] + r] = i;
+    }
+}
+
+// unit of work of the grouped kernels: a touched expert (or the shared expert
+// and a chunk of the batch's tokens) and a chunk of rows
+struct Unit {
+    bool live;
+    bool shared;
+    int expert;
+    int first;   // first assignment in perm (routed) or first token (shared)
+    int count;   // assignments (routed) or tokens (shared)
+};
+
+__device__ __forceinline__ Unit decode_unit(const FwdArgs &a, const GroupView &gv, int ui, int shared_tok_chunk) {
+    Unit u;
+    u.live = false;
+    u.shared = false;
+    if (ui < gv.G) {
+        if (ui < *gv.n_touched) {
+            u.live = true;
+            u.expert = gv.expert[ui];
+            u.first = gv.first[ui];
+            u.count = gv.count[ui];
+        }
+    } else {
+        const int tc = ui - gv.G;  // shared expert, token chunk tc
+        u.shared = true;
+        u.expert = a.s.E;
+        u.first = tc * shared_tok_chunk;
+        u.count = (a.T - u.first) < shared_tok_chunk ? (a.T - u.first) : shared_tok_chunk;
+        u.live = u.count > 0;
+    }
+    return u;
+}
+
+// (token, slot) of the i-th assignment of a unit
+__device__ __forceinline__ void unit_item(const FwdArgs &a, const GroupView &gv, const Unit &u, int i, int &t,
+                                          int &slot) {
+    const int K = a.s.K;
+    if (u.shared) {
+        t = u.first + i;
+        slot = K;
+    } else {
+        const int asg = gv.perm[u.first + i];
+        t = asg / K;
+        slot = asg % K;
+    }
+}
+
+template <int BITS, int CPL>
+__device__ __forceinline__ void load_limb_slice(const FwdArgs &a, int t, int k0, LimbSlice<BITS, CPL> &hv) {
+    using Q = QSlice<BITS, CPL>;
+    const int H = a.s.H;
+    const uint32_t *hl = (const uint32_t *)a.ws.hl + (size_t)t * kLimbs * (H / 8) + k0 / 8;
+#pragma unroll
+    for (int x = 0; x < kLimbs; ++x)
+#pragma unroll
+        for (int i = 0; i < Q::NL / 4; ++i) {
+            const int4 v = *(const int4 *)(hl + (size_t)x * (H / 8) + 4 * i);
+            hv.L[x][4 * i + 0] = v.x; hv.L[x][4 * i + 1] = v.y;
+            hv.L[x][4 * i + 2] = v.z; hv.L[x][4 * i + 3] = v.w;
+        }
+#pragma unroll
+    for (int g = 0; g < Q::NGL; ++g) {
+        hv.S[g] = a.ws.hs[(size_t)t * (H / 64) + k0 / 64 + g];
+        float xs = 0.0f;
+#pragma unroll
+        for (int hh = 0; hh < Q::GL / 32; ++hh) xs += a.ws.hx[(size_t)t * (H / 32) + (k0 + g * 64) / 32 + hh];
+        hv.X[g] = xs;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_grouped_gateup
+// ---------------------------------------------------------------------------
+template <int BITS, int CPL, int RPW>
+__global__ __launch_bounds__(256) void k_grouped_gateup(FwdArgs a, int chunks, int shared_tok_chunk) {
+    using Q = QSlice<BITS, CPL>;
+    const int F = a.s.F, K = a.s.K;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const GroupView gv = group_view(a);
+    const Unit u = decode_unit(a, gv, blockIdx.x / chunks, shared_tok_chunk);
+    if (!u.live) return;
+    const QMat &G = a.L.m[0];
+    const QMat &U = a.L.m[1];
+    const int lpr = G.lpr, rpi = 64 / lpr;
+    const int lr = lane % lpr, rsub = lane / lpr;
+    const int nrs = F / rpi;
+    const int rs0 = ((blockIdx.x % chunks) * 4 + wave) * RPW;
+    if (rs0 >= nrs) return;
+    const uint8_t *ex = u.shared ? a.shared : a.experts + (size_t)u.expert * a.L.bytes;
+
+    uint4 gc[RPW][CPL], uc[RPW][CPL];
+    uint32_t gsb[RPW][Q::NGL], usb[RPW][Q::NGL];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int rs = rs0 + i;
+        if (rs < nrs) {
+            load_row<BITS, CPL>(ex, G, rs * rpi + rsub, lr, gc[i], gsb[i]);
+            load_row<BITS, CPL>(ex, U, rs * rpi + rsub, lr, uc[i], usb[i]);
+        }
+    }
+    const int k0 = lr * Q::NV;
+    for (int it = 0; it < u.count; ++it) {
+        int t, slot;
+        unit_item(a, gv, u, it, t, slot);
+        LimbSlice<BITS, CPL> hv;
+        load_limb_slice<BITS, CPL>(a, t, k0, hv);
+        float *act = a.ws.act + ((size_t)t * (K + 1) + slot) * F;
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int rs = rs0 + i;
+            if (rs < nrs) {
+                float g = qdot<BITS, CPL>(gc[i], gsb[i], hv);
+                float v = qdot<BITS, CPL>(uc[i], usb[i], hv);
+                g = lane_group_sum(g, lpr);
+                v = lane_group_sum(v, lpr);
+                if (lr == 0) act[rs * rpi + rsub] = g * sigmoidf_(g) * v;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_grouped_down
+// ---------------------------------------------------------------------------
+template <int BITS, int CPL, int RPW>
+__global__ __launch_bounds__(256) void k_grouped_down(FwdArgs a, int chunks, int shared_tok_chunk) {
+    using Q = QSlice<BITS, CPL>;
+    const int H = a.s.H, F = a.s.F, K = a.s.K;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const GroupView gv = group_view(a);
+    const Unit u = decode_unit(a, gv, blockIdx.x / chunks, shared_tok_chunk);
+    if (!u.live) return;
+    const QMat &Dm = a.L.m[2];
+    const int lpr = Dm.lpr, rpi = 64 / lpr;
+    const int lr = lane % lpr, rsub = lane / lpr;
+    const int nrs = H / rpi;
+    const int rs0 = ((blockIdx.x % chunks) * 4 + wave) * RPW;
+    if (rs0 >= nrs) return;
+    const uint8_t *ex = u.shared ? a.shared : a.experts + (size_t)u.expert * a.L.bytes;
+
+    uint4 wc[RPW][CPL];
+    uint32_t wsb[RPW][Q::NGL];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int rs = rs0 + i;
+        if (rs < nrs) load_row<BITS, CPL>(ex, Dm, rs * rpi + rsub, lr, wc[i], wsb[i]);
+    }
+    const int k0 = lr * Q::NV;
+    for (int it = 0; it < u.count; ++it) {
+        int t, slot;
+        unit_item(a, gv, u, it, t, slot);
+        const float *ap = a.ws.act + ((size_t)t * (K + 1) + slot) * F + k0;
+        float av[Q::NV];
+#pragma unroll
+        for (int i = 0; i < Q::NV / 4; ++i) {
+            const float4 v = *(const float4 *)(ap + 4 * i);
+            av[4 * i] = v.x; av[4 * i + 1] = v.y; av[4 * i + 2] = v.z; av[4 * i + 3] = v.w;
+        }
+        float X[Q::NGL];
+#pragma unroll
+        for (int g = 0; g < Q::NGL; ++g) {
+            float x = 0.0f;
+#pragma unroll
+            for (int i = 0; i < Q::GL; ++i) x += av[g * Q::GL + i];
+            X[g] = x;
+        }
+        float *ys = a.ws.ys + ((size_t)t * (K + 1) + slot) * H;
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int rs = rs0 + i;
+            if (rs < nrs) {
+                const float v = lane_group_sum(qdot_f32<BITS, CPL>(wc[i], wsb[i], av, X), lpr);
+                if (lr == 0) ys[rs * rpi + rsub] = v;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_combine: out = x + sum_k w_k y_k + sigmoid(g_s) y_shared (slot order)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_combine(FwdArgs a) {
+    const int H = a.s.H, K = a.s.K;
+    const int t = blockIdx.y;
+    const int o = blockIdx.x * 256 + threadIdx.x;
+    if (o >= H) return;
+    const float *c = a.ws.coef + (size_t)t * (K + 1);
+    const float *ys = a.ws.ys + (size_t)t * (K + 1) * H + o;
+    float acc = a.x[(size_t)t * H + o];
+    for (int k = 0; k <= K; ++k) acc = fmaf(c[k], ys[(size_t)k * H], acc);
+    a.y[(size_t)t * H + o] = acc;
+}
+
+constexpr int kGroupRpwGateUp = 4;
+constexpr int kGroupRpwDown = 4;
+constexpr int kSharedTokChunk = 8;
+
+template <int BITS>
+hipError_t launch_grouped_bits(const FwdArgs &a, hipStream_t st) {
+    const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K, T = a.T;
+    const int G = (T * K < E) ? T * K : E;
+    const int shared_units = (T + kSharedTokChunk - 1) / kSharedTokChunk;
+    {
+        const bool wide = E > 512;
+        if (wide)
+            hipLaunchKernelGGL(k_route_group<16>, dim3(1), dim3(1024), 0, st, a);
+        else
+            hipLaunchKernelGGL(k_route_group<8>, dim3(1), dim3(1024), 0, st, a);
+    }
+    {
+        const QMat &Gm = a.L.m[0];
+        const int rpi = 64 / Gm.lpr;
+        const int nrs = F / rpi;
+        const int chunks = (nrs + 4 * kGroupRpwGateUp - 1) / (4 * kGroupRpwGateUp);
+        const dim3 grid((unsigned)((G + shared_units) * chunks));
+        switch (Gm.cpl) {
+            case 1: hipLaunchKernelGGL((k_grouped_gateup<BITS, 1, kGroupRpwGateUp>), grid, dim3(256), 0, st, a, chunks, kSharedTokChunk); break;
+            case 2: hipLaunchKernelGGL((k_grouped_gateup<BITS, 2, kGroupRpwGateUp>), grid, dim3(256), 0, st, a, chunks, kSharedTokChunk); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+    {
+        const QMat &Dm = a.L.m[2];
+        const int rpi = 64 / Dm.lpr;
+        const int nrs = H / rpi;
+        const int chunks = (nrs + 4 * kGroupRpwDown - 1) / (4 * kGroupRpwDown);
+        const dim3 grid((unsigned)((G + shared_units) * chunks));
+        switch (Dm.cpl) {
+            case 1: hipLaunchKernelGGL((k_grouped_down<BITS, 1, kGroupRpwDown>), grid, dim3(256), 0, st, a, chunks, kSharedTokChunk); break;
+            case 2: hipLaunchKernelGGL((k_grouped_down<BITS, 2, kGroupRpwDown>), grid, dim3(256), 0, st, a, chunks, kSharedTokChunk); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((H + 255) / 256), (unsigned)T), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_grouped(const FwdArgs &a, hipStream_t stream) {
+    (void)hipGetLastError();
+    const hipError_t e = launch_forward_stage(a, 0, stream);  // RMSNorm + router + limbs of h
+    if (e != hipSuccess) return e;
+    if (a.s.bits == 4) return launch_grouped_bits<4>(a, stream);
+    if (a.s.bits == 2) return launch_grouped_bits<2>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -25,12 +25,22 @@ struct Workspace {
     int8_t *hl;      // [T][7][H/8] dwords: base-16 limbs of the fixed-point normalised tokens
     float *hs;       // [T][H/64]  group scales (powers of two) of the limbs
     float *hx;       // [T][H/32]  sums of h over each half group
+    // batched (grouped-by-expert) path
+    int32_t *grp;    // [4 + 3 * (G + 1) + T*K]: n_touched, then expert, first slot and count of
+                     // each touched expert, then the assignments t*K+k sorted by (expert, token)
+    float *ys;       // [T][K+1][H] per-slot expert outputs
 };
 
 struct Shape {
     int H, F, E, K, bits;
     float eps;
 };
+
+// touched-expert bound of a batch and the integers of the grouping table
+inline int touched_bound(const Shape &s, int T) { return (T * s.K < s.E) ? T * s.K : s.E; }
+inline size_t grouped_ints(const Shape &s, int T) {
+    return 4 + 3 * ((size_t)touched_bound(s, T) + 1) + (size_t)T * s.K;
+}
 
 inline size_t workspace_bytes(const Shape &s, int T) {
     size_t b = kCtrlBytes;
@@ -43,6 +53,8 @@ inline size_t workspace_bytes(const Shape &s, int T) {
     b += align_up((size_t)T * 4 * s.H);  // 7 limbs x H/2 bytes fit in 4 H
     b += align_up((size_t)T * (s.H / 64) * 4);
     b += align_up((size_t)T * (s.H / 32) * 4);
+    b += align_up(grouped_ints(s, T) * 4);
+    b += align_up((size_t)T * (s.K + 1) * s.H * 4);
     return b;
 }
 
@@ -68,6 +80,10 @@ inline Workspace carve_workspace(void *base, const Shape &s, int T) {
     w.hs = (float *)p;
     p += align_up((size_t)T * (s.H / 64) * 4);
     w.hx = (float *)p;
+    p += align_up((size_t)T * (s.H / 32) * 4);
+    w.grp = (int32_t *)p;
+    p += align_up(grouped_ints(s, T) * 4);
+    w.ys = (float *)p;
     return w;
 }
 
@@ -89,6 +105,11 @@ struct FwdArgs {
 };
 
 constexpr int kForwardStages = 3;
+// batches of at least this many tokens (and at most kGroupMaxAssign assignments)
+// take the grouped-by-expert path
+constexpr int kGroupMinTokens = 4;
+constexpr int kGroupMaxAssign = 4096;
+hipError_t launch_grouped(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_forward_stage(const FwdArgs &a, int stage, hipStream_t stream);
 

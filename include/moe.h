@@ -149,7 +149,10 @@ int moe_generate_layer(const moe_dims_t *dims, uint64_t seed, uint32_t layer, vo
                        void *shared_expert, void *stream);
 
 /*
- * One MoE layer for n_tokens tokens.
+ * One MoE layer for n_tokens tokens.  A single token (or up to 3) runs three
+ * kernels per layer; batches of 4 or more tokens (with n_tokens * top_k <= 4096)
+ * are grouped by expert so that every selected expert's weights are read once
+ * for all of its tokens.  Both give the same results up to fp32 rounding order.
  *   x          fp32 [n_tokens][H] device, 16-B aligned (may equal y: in place)
  *   y          fp32 [n_tokens][H] device, 16-B aligned: x + routed combine + gated shared
  *   route_idx  int32 [n_tokens][K] device or NULL: selected experts, ordered by
@@ -165,14 +168,15 @@ int moe_layer_forward(const moe_dims_t *dims, const moe_layer_t *layer, const fl
                       size_t workspace_bytes, void *stream);
 
 /*
- * Enqueue one stage of moe_layer_forward, for profiling or for interleaving
- * other work between stages.  Stage 0: RMSNorm, router GEMV and shared-gate
- * logit; stage 1: softmax/top-K/renormalise and the fused gate+up dequant GEMV
- * with SwiGLU for the selected and the shared experts; stage 2: down-projection
- * with the weighted combine, sigmoid-gated shared expert and residual.
- * Stages 0, 1, 2 enqueued in this order with identical arguments (same
- * workspace, stream order) produce exactly what moe_layer_forward produces.
- * Arguments as for moe_layer_forward; stage outside 0..2 is MOE_ERR_INVALID_ARG.
+ * Enqueue one stage of the per-token (ungrouped) layer, for profiling or for
+ * interleaving other work between stages.  Stage 0: RMSNorm, router GEMV and
+ * shared-gate logit; stage 1: softmax/top-K/renormalise and the fused gate+up
+ * dequant GEMV with SwiGLU for the selected and the shared experts; stage 2:
+ * down-projection with the weighted combine, sigmoid-gated shared expert and
+ * residual.  Stages 0, 1, 2 enqueued in this order with identical arguments
+ * (same workspace, stream order) produce exactly what moe_layer_forward produces
+ * for fewer than 4 tokens.  Arguments as for moe_layer_forward; stage outside
+ * 0..2 is MOE_ERR_INVALID_ARG.
  */
 int moe_layer_forward_stage(const moe_dims_t *dims, const moe_layer_t *layer, const float *x, float *y,
                             int32_t n_tokens, int32_t *route_idx, float *route_w, void *workspace,
