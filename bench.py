@@ -28,12 +28,23 @@ if ROOT not in sys.path:
 
 HBM_PEAK_BPS = 8.0e12  # MI355X HBM3E peak
 
-# HBM traffic of k_gateup per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
-# (profiles/layer4_kernels_pmc_traffic.md), valid only for the kernel source it
-# was measured on; FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0, the ratios
+# HBM traffic per launch of the dominant expert kernel, keyed by (workload,
+# kernel), from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (summaries under
+# profiles/); an entry holds only while the kernel sources hash to the prefix it
+# was measured on.  FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0, the ratios
 # of bytes moved to counts reported for a 256 MiB copy.
-GATEUP_TRAFFIC = {"source_sha256_prefix": "5d1ef4fae1e76c30", "workload": "layer4",
-                  "fetch_kib": 11701.1, "write_kib": 26.8, "fetch_scale": 2.0, "write_scale": 1.0}
+KERNEL_TRAFFIC = {}
+
+
+def kernel_source_hash(grouped):
+    """sha256 of the sources the expert kernels are built from."""
+    h = hashlib.sha256()
+    names = ["moe_device.h", "moe_internal.h", "moe_layout.h",
+             "moe_grouped.hip" if grouped else "moe_forward.hip"]
+    for n in names:
+        with open(os.path.join(ROOT, "bit_dequant_expert_router_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def parse_args():
@@ -160,9 +171,18 @@ def main():
     for j in range(NW):
         moe.moe_layer_forward(dims, descs[j % R], pool[j], out[j], T, ridx[j], rw[j], wss[j], wsb)
     torch.cuda.synchronize()
-    M = 512
+    n_stages = moe.moe_forward_stage_count(dims, T)
+    grouped = n_stages == 6
+    if grouped:
+        names = ["k_router", "k_route_group", "k_grouped_gateup", "k_encode_act", "k_grouped_down", "k_combine"]
+        gu_stage, down_stage = 2, 4
+        M = 64
+    else:
+        names = ["k_router", "k_gateup", "k_down"]
+        gu_stage, down_stage = 1, 2
+        M = 512
     stage_s = []
-    for st in range(3):
+    for st in range(n_stages):
         sg = torch.cuda.Stream()
         sg.wait_stream(torch.cuda.current_stream())
         g = torch.cuda.CUDAGraph()
@@ -176,6 +196,7 @@ def main():
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        # replay() launches the graph on the current stream: the events bracket it there
         e0.record()
         g.replay()
         e1.record()
@@ -183,17 +204,16 @@ def main():
         stage_s.append(e0.elapsed_time(e1) * 1e-3 / M)
         del g
     stage_mean = np.array(stage_s)
-    # algorithmic bytes of the gate/up kernel: gate + up codes and scale/bias of
-    # the distinct selected experts and the shared one
+    # algorithmic bytes of the expert kernels: gate + up (or down) codes and
+    # scale/bias of the distinct selected experts and the shared one
     per_matrix = dims.ffn * dims.hidden * dims.bits // 8 + (dims.ffn * dims.hidden // 64) * 4
-    gu_bytes = float(np.mean([distinct[j] for j in range(NW)])) * 2 * per_matrix
-    achieved = gu_bytes / stage_mean[1]
+    n_distinct = float(np.mean([distinct[j] for j in range(NW)]))
+    kbytes = {gu_stage: n_distinct * 2 * per_matrix, down_stage: n_distinct * per_matrix}
+    dom = max(kbytes, key=lambda k: stage_mean[k])
+    achieved = kbytes[dom] / stage_mean[dom]
     traffic = None
-    src = os.path.join(ROOT, "bit_dequant_expert_router_amd", "csrc", "moe_forward.hip")
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    tr = GATEUP_TRAFFIC
-    if sha.startswith(tr["source_sha256_prefix"]) and wl.name == tr["workload"]:
+    tr = KERNEL_TRAFFIC.get((wl.name, names[dom]))
+    if tr is not None and tr["source_sha256_prefix"] == kernel_source_hash(grouped)[:16]:
         traffic = round((tr["fetch_kib"] * tr["fetch_scale"] + tr["write_kib"] * tr["write_scale"]) * 1024)
 
     result = {
@@ -220,19 +240,17 @@ def main():
         "effective_expert_GBps": round(bytes_per_step * nsteps / elapsed / 1e9, 1),
         "pct_of_hbm_peak": round(100.0 * bytes_per_step * nsteps / elapsed / HBM_PEAK_BPS, 2),
         "roofline": {
-            "kernel": "k_gateup (routing + fused gate/up dequant GEMV + SwiGLU)",
+            "kernel": names[dom],
             "bound": "hbm",
             "achieved": round(achieved / 1e9, 1),
             "peak": HBM_PEAK_BPS / 1e9,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_BPS, 4),
             "traffic": traffic,
-            "bytes_per_launch": round(gu_bytes),
-            "launch_us": round(float(stage_mean[1]) * 1e6, 3),
+            "bytes_per_launch": round(kbytes[dom]),
+            "launch_us": round(float(stage_mean[dom]) * 1e6, 3),
         },
-        "stage_us": {"k_router": round(float(stage_mean[0]) * 1e6, 3),
-                     "k_gateup": round(float(stage_mean[1]) * 1e6, 3),
-                     "k_down": round(float(stage_mean[2]) * 1e6, 3)},
+        "stage_us": {n: round(float(v) * 1e6, 3) for n, v in zip(names, stage_mean)},
     }
 
     if args.cpu_sample > 0:

@@ -63,6 +63,7 @@ _SIGS = {
     "moe_generate_layer": (ctypes.c_int, [_dimsp, ctypes.c_uint64, ctypes.c_uint32, _vp, _vp, _vp]),
     "moe_layer_forward": (ctypes.c_int, [_dimsp, _layerp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "moe_layer_forward_stage": (ctypes.c_int, [_dimsp, _layerp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _i32, _vp]),
+    "moe_forward_stage_count": (ctypes.c_int, [_dimsp, _i32]),
     "moe_stack_forward": (ctypes.c_int, [_dimsp, _layerp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -186,6 +187,13 @@ def moe_layer_forward_stage(dims, layer: moe_layer_t, x, y, n_tokens: int, route
                   _lib.moe_layer_forward_stage(ctypes.byref(dims_of(dims)), ctypes.byref(layer), _addr(x),
                                                _addr(y), int(n_tokens), _addr(route_idx), _addr(route_w),
                                                _addr(workspace), nbytes, int(stage), _stream(stream)))
+
+
+def moe_forward_stage_count(dims, n_tokens: int) -> int:
+    rc = int(_lib.moe_forward_stage_count(ctypes.byref(dims_of(dims)), int(n_tokens)))
+    if rc < 0:
+        raise MoeError("moe_forward_stage_count", rc)
+    return rc
 
 
 def moe_stack_forward(dims, layers: Sequence[moe_layer_t], x, y, n_tokens: int, route_idx, route_w,

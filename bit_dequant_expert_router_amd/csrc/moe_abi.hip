@@ -65,7 +65,7 @@ size_t workspace_bytes_checked(const moe_dims_t *dims, int32_t n_tokens) {
 
 // batches of kGroupMinTokens or more tokens are grouped by expert
 hipError_t launch_layer(const FwdArgs &a, hipStream_t stream) {
-    if (a.T >= kGroupMinTokens && a.T * a.s.K <= kGroupMaxAssign) return launch_grouped(a, stream);
+    if (uses_grouped(a.s, a.T)) return launch_grouped(a, stream);
     return launch_forward(a, stream);
 }
 
@@ -194,9 +194,18 @@ int moe_layer_forward_stage(const moe_dims_t *dims, const moe_layer_t *layer, co
     if (rc != MOE_OK) return rc;
     rc = check_layer(layer);
     if (rc != MOE_OK) return rc;
-    if (stage < 0 || stage >= kForwardStages) return MOE_ERR_INVALID_ARG;
+    const bool grouped = uses_grouped(shape_of(dims), n_tokens);
+    if (stage < 0 || stage >= (grouped ? kGroupedStages : kForwardStages)) return MOE_ERR_INVALID_ARG;
     const FwdArgs a = make_fwd(dims, layer, x, y, n_tokens, route_idx, route_w, workspace);
+    if (grouped) return hip_status(launch_grouped_stage(a, stage, (hipStream_t)stream));
     return hip_status(launch_forward_stage(a, stage, (hipStream_t)stream));
+}
+
+int moe_forward_stage_count(const moe_dims_t *dims, int32_t n_tokens) {
+    const int rc = check_dims_impl(dims);
+    if (rc != MOE_OK) return rc;
+    if (n_tokens < 1 || n_tokens > 65535) return MOE_ERR_INVALID_ARG;
+    return uses_grouped(shape_of(dims), n_tokens) ? kGroupedStages : kForwardStages;
 }
 
 int moe_stack_forward(const moe_dims_t *dims, const moe_layer_t *layers, int32_t n_layers, const float *x,

@@ -150,24 +150,27 @@ struct Unit {
     int count;   // assignments (routed) or tokens (shared)
 };
 
+// units 0 .. n_shared-1: the shared expert over token chunks (the heaviest units
+// are dispatched first); then one unit per touched routed expert
 __device__ __forceinline__ Unit decode_unit(const FwdArgs &a, const GroupView &gv, int ui, int shared_tok_chunk) {
     Unit u;
     u.live = false;
     u.shared = false;
-    if (ui < gv.G) {
-        if (ui < *gv.n_touched) {
-            u.live = true;
-            u.expert = gv.expert[ui];
-            u.first = gv.first[ui];
-            u.count = gv.count[ui];
-        }
-    } else {
-        const int tc = ui - gv.G;  // shared expert, token chunk tc
+    const int n_shared = (a.T + shared_tok_chunk - 1) / shared_tok_chunk;
+    if (ui < n_shared) {
         u.shared = true;
         u.expert = a.s.E;
-        u.first = tc * shared_tok_chunk;
+        u.first = ui * shared_tok_chunk;
         u.count = (a.T - u.first) < shared_tok_chunk ? (a.T - u.first) : shared_tok_chunk;
         u.live = u.count > 0;
+    } else {
+        const int r = ui - n_shared;
+        if (r < *gv.n_touched) {
+            u.live = true;
+            u.expert = gv.expert[r];
+            u.first = gv.first[r];
+            u.count = gv.count[r];
+        }
     }
     return u;
 }
@@ -186,27 +189,45 @@ __device__ __forceinline__ void unit_item(const FwdArgs &a, const GroupView &gv,
     }
 }
 
+// lane slice [k0, k0 + NV) of one vector in limb form: limbs [7][n/8] dwords,
+// group scales [n/64], half-group sums [n/32]
 template <int BITS, int CPL>
-__device__ __forceinline__ void load_limb_slice(const FwdArgs &a, int t, int k0, LimbSlice<BITS, CPL> &hv) {
+__device__ __forceinline__ void load_limb_slice(const uint32_t *hl, const float *hs, const float *hx, int n, int k0,
+                                                LimbSlice<BITS, CPL> &hv) {
     using Q = QSlice<BITS, CPL>;
-    const int H = a.s.H;
-    const uint32_t *hl = (const uint32_t *)a.ws.hl + (size_t)t * kLimbs * (H / 8) + k0 / 8;
+    hl += k0 / 8;
 #pragma unroll
     for (int x = 0; x < kLimbs; ++x)
 #pragma unroll
         for (int i = 0; i < Q::NL / 4; ++i) {
-            const int4 v = *(const int4 *)(hl + (size_t)x * (H / 8) + 4 * i);
+            const int4 v = *(const int4 *)(hl + (size_t)x * (n / 8) + 4 * i);
             hv.L[x][4 * i + 0] = v.x; hv.L[x][4 * i + 1] = v.y;
             hv.L[x][4 * i + 2] = v.z; hv.L[x][4 * i + 3] = v.w;
         }
 #pragma unroll
     for (int g = 0; g < Q::NGL; ++g) {
-        hv.S[g] = a.ws.hs[(size_t)t * (H / 64) + k0 / 64 + g];
+        hv.S[g] = hs[k0 / 64 + g];
         float xs = 0.0f;
 #pragma unroll
-        for (int hh = 0; hh < Q::GL / 32; ++hh) xs += a.ws.hx[(size_t)t * (H / 32) + (k0 + g * 64) / 32 + hh];
+        for (int hh = 0; hh < Q::GL / 32; ++hh) xs += hx[(k0 + g * 64) / 32 + hh];
         hv.X[g] = xs;
     }
+}
+
+// the normalised token t
+template <int BITS, int CPL>
+__device__ __forceinline__ void load_token_limbs(const FwdArgs &a, int t, int k0, LimbSlice<BITS, CPL> &hv) {
+    const int H = a.s.H;
+    load_limb_slice<BITS, CPL>((const uint32_t *)a.ws.hl + (size_t)t * kLimbs * (H / 8), a.ws.hs + (size_t)t * (H / 64),
+                               a.ws.hx + (size_t)t * (H / 32), H, k0, hv);
+}
+
+// the activation vector of (token, slot) pair p
+template <int BITS, int CPL>
+__device__ __forceinline__ void load_act_limbs(const FwdArgs &a, int p, int k0, LimbSlice<BITS, CPL> &hv) {
+    const int F = a.s.F;
+    load_limb_slice<BITS, CPL>((const uint32_t *)a.ws.al + (size_t)p * kLimbs * (F / 8), a.ws.as + (size_t)p * (F / 64),
+                               a.ws.ax + (size_t)p * (F / 32), F, k0, hv);
 }
 
 // ---------------------------------------------------------------------------
@@ -240,11 +261,18 @@ __global__ __launch_bounds__(256) void k_grouped_gateup(FwdArgs a, int chunks, i
         }
     }
     const int k0 = lr * Q::NV;
+    int t, slot;
+    unit_item(a, gv, u, 0, t, slot);
+    LimbSlice<BITS, CPL> hv;
+    load_token_limbs<BITS, CPL>(a, t, k0, hv);
     for (int it = 0; it < u.count; ++it) {
-        int t, slot;
-        unit_item(a, gv, u, it, t, slot);
-        LimbSlice<BITS, CPL> hv;
-        load_limb_slice<BITS, CPL>(a, t, k0, hv);
+        // the next token's limbs are loaded while this token is computed
+        int tn = t, sn = slot;
+        LimbSlice<BITS, CPL> hn;
+        if (it + 1 < u.count) {
+            unit_item(a, gv, u, it + 1, tn, sn);
+            load_token_limbs<BITS, CPL>(a, tn, k0, hn);
+        }
         float *act = a.ws.act + ((size_t)t * (K + 1) + slot) * F;
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
@@ -257,16 +285,83 @@ __global__ __launch_bounds__(256) void k_grouped_gateup(FwdArgs a, int chunks, i
                 if (lr == 0) act[rs * rpi + rsub] = g * sigmoidf_(g) * v;
             }
         }
+        t = tn;
+        slot = sn;
+        hv = hn;
     }
 }
 
 // ---------------------------------------------------------------------------
-// k_grouped_down
+// k_encode_act: limb form of every (token, slot) activation vector, in the
+// order of the down projection's byte-order codes.  A thread takes 16
+// consecutive activations, four threads one group of 64.
+//   4-bit: the code dword covering k = 8w .. 8w+7 holds k = 8w + m in nibble
+//          2 (m % 4) + m / 4, so the limb dword w puts k = 8w + (n >> 1) + 4 (n & 1)
+//          in nibble n.
+//   2-bit: the code dword covering k = 16w .. 16w+15 holds k = 16w + m in byte
+//          m % 4 at bit 2 (m / 4); its two masked halves (bits 0-1, bits 2-3 of
+//          each nibble) are dotted with limb dwords 2w and 2w+1, which put
+//          k = 16w + (n >> 1) + 4 p + 8 (n & 1) in nibble n (p = 0, 1).
+// ---------------------------------------------------------------------------
+template <int BITS>
+__global__ __launch_bounds__(256) void k_encode_act(FwdArgs a, int n_pairs) {
+    const int F = a.s.F;
+    const int tpp = F / 16;  // threads per pair (a multiple of 8)
+    const int p = blockIdx.x * (256 / tpp) + threadIdx.x / tpp;
+    const int u = threadIdx.x % tpp;
+    const bool live = p < n_pairs;
+    float v[16];
+    const float *src = a.ws.act + (size_t)(live ? p : 0) * F + 16 * u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float4 q = *(const float4 *)(src + 4 * i);
+        v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+    }
+    float m = 0.0f, sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        m = nan_max(m, fabsf(v[i]));
+        sum += v[i];
+    }
+    sum += __shfl_xor(sum, 1, 64);  // half group (32 values)
+    m = nan_max(m, __shfl_xor(m, 1, 64));
+    m = nan_max(m, __shfl_xor(m, 2, 64));  // group of 64
+    uint32_t pk[kLimbs][2];
+#pragma unroll
+    for (int x = 0; x < kLimbs; ++x) pk[x][0] = pk[x][1] = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        int l[kLimbs];
+        limb_split(limb_value(v[i], m), l);
+        int dw, nib;
+        if constexpr (BITS == 4) {
+            const int mm = i % 8;
+            dw = i / 8;
+            nib = 2 * (mm % 4) + mm / 4;
+        } else {
+            dw = (i / 4) % 2;
+            nib = 2 * (i % 4) + i / 8;
+        }
+#pragma unroll
+        for (int x = 0; x < kLimbs; ++x) pk[x][dw] |= (uint32_t)(l[x] & 15) << (4 * nib);
+    }
+    if (live) {
+        uint32_t *al = (uint32_t *)a.ws.al + (size_t)p * kLimbs * (F / 8) + 2 * u;
+#pragma unroll
+        for (int x = 0; x < kLimbs; ++x) *(uint2 *)(al + (size_t)x * (F / 8)) = make_uint2(pk[x][0], pk[x][1]);
+        if ((u & 1) == 0) a.ws.ax[(size_t)p * (F / 32) + u / 2] = sum;
+        if ((u & 3) == 0) a.ws.as[(size_t)p * (F / 64) + u / 4] = limb_scale(m);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_grouped_down: one block per (unit, chunk of rows); exact code x limb
+// products as in gate/up, activations taken from k_encode_act's limbs
 // ---------------------------------------------------------------------------
 template <int BITS, int CPL, int RPW>
 __global__ __launch_bounds__(256) void k_grouped_down(FwdArgs a, int chunks, int shared_tok_chunk) {
     using Q = QSlice<BITS, CPL>;
-    const int H = a.s.H, F = a.s.F, K = a.s.K;
+    const int H = a.s.H, K = a.s.K;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const GroupView gv = group_view(a);
     const Unit u = decode_unit(a, gv, blockIdx.x / chunks, shared_tok_chunk);
@@ -287,33 +382,30 @@ __global__ __launch_bounds__(256) void k_grouped_down(FwdArgs a, int chunks, int
         if (rs < nrs) load_row<BITS, CPL>(ex, Dm, rs * rpi + rsub, lr, wc[i], wsb[i]);
     }
     const int k0 = lr * Q::NV;
+    int t, slot;
+    unit_item(a, gv, u, 0, t, slot);
+    LimbSlice<BITS, CPL> av;
+    load_act_limbs<BITS, CPL>(a, t * (K + 1) + slot, k0, av);
     for (int it = 0; it < u.count; ++it) {
-        int t, slot;
-        unit_item(a, gv, u, it, t, slot);
-        const float *ap = a.ws.act + ((size_t)t * (K + 1) + slot) * F + k0;
-        float av[Q::NV];
-#pragma unroll
-        for (int i = 0; i < Q::NV / 4; ++i) {
-            const float4 v = *(const float4 *)(ap + 4 * i);
-            av[4 * i] = v.x; av[4 * i + 1] = v.y; av[4 * i + 2] = v.z; av[4 * i + 3] = v.w;
-        }
-        float X[Q::NGL];
-#pragma unroll
-        for (int g = 0; g < Q::NGL; ++g) {
-            float x = 0.0f;
-#pragma unroll
-            for (int i = 0; i < Q::GL; ++i) x += av[g * Q::GL + i];
-            X[g] = x;
+        // the next pair's limbs are loaded while this one is computed
+        int tn = t, sn = slot;
+        LimbSlice<BITS, CPL> an;
+        if (it + 1 < u.count) {
+            unit_item(a, gv, u, it + 1, tn, sn);
+            load_act_limbs<BITS, CPL>(a, tn * (K + 1) + sn, k0, an);
         }
         float *ys = a.ws.ys + ((size_t)t * (K + 1) + slot) * H;
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const int rs = rs0 + i;
             if (rs < nrs) {
-                const float v = lane_group_sum(qdot_f32<BITS, CPL>(wc[i], wsb[i], av, X), lpr);
+                const float v = lane_group_sum(qdot<BITS, CPL>(wc[i], wsb[i], av), lpr);
                 if (lr == 0) ys[rs * rpi + rsub] = v;
             }
         }
+        t = tn;
+        slot = sn;
+        av = an;
     }
 }
 
@@ -332,59 +424,85 @@ __global__ __launch_bounds__(256) void k_combine(FwdArgs a) {
     a.y[(size_t)t * H + o] = acc;
 }
 
-constexpr int kGroupRpwGateUp = 4;
-constexpr int kGroupRpwDown = 4;
+// rows per wave of the grouped kernels, sized so that the weights, the current
+// and the prefetched limb slices stay in registers (NL = limb dwords per limb)
+constexpr int grouped_rpw(int bits, int cpl, bool down) {
+    const int nl = cpl * 16 / bits;
+    if (down) return nl <= 4 ? 8 : (nl <= 8 ? 4 : 2);
+    return nl <= 8 ? 4 : 2;
+}
 constexpr int kSharedTokChunk = 8;
 
+template <int BITS, int CPL>
+void launch_grouped_mats(const FwdArgs &a, int units, hipStream_t st, bool down) {
+    const QMat &M = a.L.m[down ? 2 : 0];
+    const int rpi = 64 / M.lpr;
+    const int nrs = M.rows / rpi;
+    const int rpw = grouped_rpw(BITS, CPL, down);
+    const int chunks = (nrs + 4 * rpw - 1) / (4 * rpw);
+    const dim3 grid((unsigned)(units * chunks));
+    if (down)
+        hipLaunchKernelGGL((k_grouped_down<BITS, CPL, grouped_rpw(BITS, CPL, true)>), grid, dim3(256), 0, st, a, chunks,
+                           kSharedTokChunk);
+    else
+        hipLaunchKernelGGL((k_grouped_gateup<BITS, CPL, grouped_rpw(BITS, CPL, false)>), grid, dim3(256), 0, st, a,
+                           chunks, kSharedTokChunk);
+}
+
 template <int BITS>
-hipError_t launch_grouped_bits(const FwdArgs &a, hipStream_t st) {
+hipError_t launch_grouped_bits(const FwdArgs &a, int stage, hipStream_t st) {
     const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K, T = a.T;
     const int G = (T * K < E) ? T * K : E;
-    const int shared_units = (T + kSharedTokChunk - 1) / kSharedTokChunk;
-    {
-        const bool wide = E > 512;
-        if (wide)
-            hipLaunchKernelGGL(k_route_group<16>, dim3(1), dim3(1024), 0, st, a);
-        else
-            hipLaunchKernelGGL(k_route_group<8>, dim3(1), dim3(1024), 0, st, a);
-    }
-    {
-        const QMat &Gm = a.L.m[0];
-        const int rpi = 64 / Gm.lpr;
-        const int nrs = F / rpi;
-        const int chunks = (nrs + 4 * kGroupRpwGateUp - 1) / (4 * kGroupRpwGateUp);
-        const dim3 grid((unsigned)((G + shared_units) * chunks));
-        switch (Gm.cpl) {
-            case 1: hipLaunchKernelGGL((k_grouped_gateup<BITS, 1, kGroupRpwGateUp>), grid, dim3(256), 0, st, a, chunks, kSharedTokChunk); break;
-            case 2: hipLaunchKernelGGL((k_grouped_gateup<BITS, 2, kGroupRpwGateUp>), grid, dim3(256), 0, st, a, chunks, kSharedTokChunk); break;
-            default: return hipErrorInvalidValue;
+    const int units = G + (T + kSharedTokChunk - 1) / kSharedTokChunk;
+    switch (stage) {
+        case 1:
+            if (E > 512)
+                hipLaunchKernelGGL(k_route_group<16>, dim3(1), dim3(1024), 0, st, a);
+            else
+                hipLaunchKernelGGL(k_route_group<8>, dim3(1), dim3(1024), 0, st, a);
+            break;
+        case 2:
+        case 4: {
+            const bool down = stage == 4;
+            switch (a.L.m[down ? 2 : 0].cpl) {
+                case 1: launch_grouped_mats<BITS, 1>(a, units, st, down); break;
+                case 2: launch_grouped_mats<BITS, 2>(a, units, st, down); break;
+                default: return hipErrorInvalidValue;
+            }
+            break;
         }
-    }
-    {
-        const QMat &Dm = a.L.m[2];
-        const int rpi = 64 / Dm.lpr;
-        const int nrs = H / rpi;
-        const int chunks = (nrs + 4 * kGroupRpwDown - 1) / (4 * kGroupRpwDown);
-        const dim3 grid((unsigned)((G + shared_units) * chunks));
-        switch (Dm.cpl) {
-            case 1: hipLaunchKernelGGL((k_grouped_down<BITS, 1, kGroupRpwDown>), grid, dim3(256), 0, st, a, chunks, kSharedTokChunk); break;
-            case 2: hipLaunchKernelGGL((k_grouped_down<BITS, 2, kGroupRpwDown>), grid, dim3(256), 0, st, a, chunks, kSharedTokChunk); break;
-            default: return hipErrorInvalidValue;
+        case 3: {
+            const int n_pairs = T * (K + 1);
+            const int ppb = 256 / (F / 16);
+            hipLaunchKernelGGL(k_encode_act<BITS>, dim3((unsigned)((n_pairs + ppb - 1) / ppb)), dim3(256), 0, st, a,
+                               n_pairs);
+            break;
         }
+        case 5:
+            hipLaunchKernelGGL(k_combine, dim3((unsigned)((H + 255) / 256), (unsigned)T), dim3(256), 0, st, a);
+            break;
+        default: return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)((H + 255) / 256), (unsigned)T), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_grouped(const FwdArgs &a, hipStream_t stream) {
+// stage 0 is the per-token path's RMSNorm + router + limbs of h
+hipError_t launch_grouped_stage(const FwdArgs &a, int stage, hipStream_t stream) {
     (void)hipGetLastError();
-    const hipError_t e = launch_forward_stage(a, 0, stream);  // RMSNorm + router + limbs of h
-    if (e != hipSuccess) return e;
-    if (a.s.bits == 4) return launch_grouped_bits<4>(a, stream);
-    if (a.s.bits == 2) return launch_grouped_bits<2>(a, stream);
+    if (stage == 0) return launch_forward_stage(a, 0, stream);
+    if (a.s.bits == 4) return launch_grouped_bits<4>(a, stage, stream);
+    if (a.s.bits == 2) return launch_grouped_bits<2>(a, stage, stream);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_grouped(const FwdArgs &a, hipStream_t stream) {
+    for (int stage = 0; stage < kGroupedStages; ++stage) {
+        const hipError_t e = launch_grouped_stage(a, stage, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace moe

@@ -29,6 +29,9 @@ struct Workspace {
     int32_t *grp;    // [4 + 3 * (G + 1) + T*K]: n_touched, then expert, first slot and count of
                      // each touched expert, then the assignments t*K+k sorted by (expert, token)
     float *ys;       // [T][K+1][H] per-slot expert outputs
+    int8_t *al;      // [T][K+1][7][F/8] dwords: limbs of the activations, in the down codes' order
+    float *as;       // [T][K+1][F/64] group scales of those limbs
+    float *ax;       // [T][K+1][F/32] sums of the activations over each half group
 };
 
 struct Shape {
@@ -55,6 +58,9 @@ inline size_t workspace_bytes(const Shape &s, int T) {
     b += align_up((size_t)T * (s.H / 32) * 4);
     b += align_up(grouped_ints(s, T) * 4);
     b += align_up((size_t)T * (s.K + 1) * s.H * 4);
+    b += align_up((size_t)T * (s.K + 1) * 4 * s.F);  // 7 limbs x F/2 bytes fit in 4 F
+    b += align_up((size_t)T * (s.K + 1) * (s.F / 64) * 4);
+    b += align_up((size_t)T * (s.K + 1) * (s.F / 32) * 4);
     return b;
 }
 
@@ -84,6 +90,12 @@ inline Workspace carve_workspace(void *base, const Shape &s, int T) {
     w.grp = (int32_t *)p;
     p += align_up(grouped_ints(s, T) * 4);
     w.ys = (float *)p;
+    p += align_up((size_t)T * (s.K + 1) * s.H * 4);
+    w.al = (int8_t *)p;
+    p += align_up((size_t)T * (s.K + 1) * 4 * s.F);
+    w.as = (float *)p;
+    p += align_up((size_t)T * (s.K + 1) * (s.F / 64) * 4);
+    w.ax = (float *)p;
     return w;
 }
 
@@ -109,7 +121,10 @@ constexpr int kForwardStages = 3;
 // take the grouped-by-expert path
 constexpr int kGroupMinTokens = 4;
 constexpr int kGroupMaxAssign = 4096;
+constexpr int kGroupedStages = 6;
+inline bool uses_grouped(const Shape &s, int T) { return T >= kGroupMinTokens && T * s.K <= kGroupMaxAssign; }
 hipError_t launch_grouped(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_grouped_stage(const FwdArgs &a, int stage, hipStream_t stream);
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_forward_stage(const FwdArgs &a, int stage, hipStream_t stream);
 

@@ -168,19 +168,30 @@ int moe_layer_forward(const moe_dims_t *dims, const moe_layer_t *layer, const fl
                       size_t workspace_bytes, void *stream);
 
 /*
- * Enqueue one stage of the per-token (ungrouped) layer, for profiling or for
- * interleaving other work between stages.  Stage 0: RMSNorm, router GEMV and
- * shared-gate logit; stage 1: softmax/top-K/renormalise and the fused gate+up
- * dequant GEMV with SwiGLU for the selected and the shared experts; stage 2:
- * down-projection with the weighted combine, sigmoid-gated shared expert and
- * residual.  Stages 0, 1, 2 enqueued in this order with identical arguments
- * (same workspace, stream order) produce exactly what moe_layer_forward produces
- * for fewer than 4 tokens.  Arguments as for moe_layer_forward; stage outside
- * 0..2 is MOE_ERR_INVALID_ARG.
+ * Enqueue one stage of the layer, for profiling or for interleaving other work
+ * between stages.  The stages are those of the path moe_layer_forward takes for
+ * n_tokens (moe_forward_stage_count gives their number); enqueued in order
+ * 0, 1, ... with identical arguments (same workspace, stream order) they
+ * produce exactly what moe_layer_forward produces.
+ * Per-token path (fewer than 4 tokens, 3 stages): 0 RMSNorm, router GEMV and
+ * shared-gate logit; 1 softmax/top-K/renormalise and the fused gate+up dequant
+ * GEMV with SwiGLU for the selected and the shared experts; 2 down projection
+ * with the weighted combine, sigmoid-gated shared expert and residual.
+ * Grouped path (6 stages): 0 as above; 1 routing of every token and grouping
+ * of the assignments by expert; 2 gate+up with SwiGLU per touched expert over
+ * its tokens (and the shared expert over all tokens); 3 limb encoding of the
+ * activations; 4 down projection per touched expert; 5 weighted combine,
+ * sigmoid-gated shared expert and residual.
+ * Arguments as for moe_layer_forward; a stage outside 0 .. count-1 is
+ * MOE_ERR_INVALID_ARG.
  */
 int moe_layer_forward_stage(const moe_dims_t *dims, const moe_layer_t *layer, const float *x, float *y,
                             int32_t n_tokens, int32_t *route_idx, float *route_w, void *workspace,
                             size_t workspace_bytes, int32_t stage, void *stream);
+
+/* Number of stages of moe_layer_forward_stage for this batch size (3 or 6), or
+ * a negative status for invalid dims or n_tokens outside 1 .. 65535. */
+int moe_forward_stage_count(const moe_dims_t *dims, int32_t n_tokens);
 
 /*
  * n_layers layers chained: x_{l+1} = layer_l(x_l), x_0 = x, y = x_{n_layers}

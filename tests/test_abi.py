@@ -168,6 +168,33 @@ def test_stage_rejects():
              wsb, 0, None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_stage_count():
+    dims = d()
+    K = dims.top_k
+    assert moe.moe_forward_stage_count(dims, 1) == 3
+    assert moe.moe_forward_stage_count(dims, 3) == 3
+    assert moe.moe_forward_stage_count(dims, 4) == 6
+    assert moe.moe_forward_stage_count(dims, 4096 // K) == 6
+    assert moe.moe_forward_stage_count(dims, 4096 // K + 1) == 3
+    f = moe._lib.moe_forward_stage_count
+    assert f(ctypes.byref(dims), 0) == moe.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(dims), 65536) == moe.MOE_ERR_INVALID_ARG
+    bad = d()
+    bad.bits = 3
+    assert f(ctypes.byref(bad), 1) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_grouped_stage_rejects():
+    dims = d()
+    T = 6
+    wsb = moe.moe_workspace_bytes(dims, T)
+    f = moe._lib.moe_layer_forward_stage
+    lay = _layer()
+    for stage in (-1, 6, 100):
+        assert f(ctypes.byref(dims), ctypes.byref(lay), A + 0x300000, A + 0x400000, T, None, None, A + 0x500000,
+                 wsb, stage, None) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_stack_rejects():
     dims = d()
     lay = (moe.moe_layer_t * 2)(_layer(), _layer(experts=None))

@@ -63,6 +63,7 @@ SMALL_SHAPES = [
     (1024, 2048, 7, 7, 2),
     (2048, 512, 33, 5, 4),
     (256, 256, 1, 1, 2),
+    (256, 4096, 6, 2, 4),
 ]
 
 
@@ -95,34 +96,39 @@ def test_inplace_determinism_and_optional_outputs(moe, n_tokens):
         check_token(a[t], ia[t], wa[t], oracle.layer_all(dims, x[t], dense, experts), dims.top_k, f"token {t}")
 
 
-def test_stages_equal_full_forward(moe):
-    """Stages 0, 1, 2 enqueued one by one give exactly the one-call result."""
+@pytest.mark.parametrize("T", [3, 6])
+def test_stages_equal_full_forward(moe, T):
+    """The stages enqueued one by one give exactly the one-call result, on the
+    per-token path (3 tokens, 3 stages) and the grouped path (6 tokens, 6 stages)."""
     dims = syn.WORKLOADS["tiny"].dims
     dense, experts, lw = _canonical_layer(dims)
-    x = syn.tokens(4, 3, dims.hidden)  # fewer than 4 tokens: the ungrouped kernels
+    x = syn.tokens(4, T, dims.hidden)
     full, fidx, fw = run_layer(dims, lw, x)
     xt = torch.from_numpy(x).cuda()
     yt = torch.empty_like(xt)
-    ridx = torch.empty((3, dims.top_k), dtype=torch.int32, device="cuda")
-    rw = torch.empty((3, dims.top_k), dtype=torch.float32, device="cuda")
-    ws = torch.empty(moe.moe_workspace_bytes(dims, 3), dtype=torch.uint8, device="cuda")
+    ridx = torch.empty((T, dims.top_k), dtype=torch.int32, device="cuda")
+    rw = torch.empty((T, dims.top_k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_workspace_bytes(dims, T), dtype=torch.uint8, device="cuda")
     moe.moe_workspace_init(ws)
-    for stage in range(3):
-        moe.moe_layer_forward_stage(dims, lw.descriptor(), xt, yt, 3, ridx, rw, ws, None, stage)
+    n_stages = moe.moe_forward_stage_count(dims, T)
+    assert n_stages == (3 if T < 4 else 6)
+    for stage in range(n_stages):
+        moe.moe_layer_forward_stage(dims, lw.descriptor(), xt, yt, T, ridx, rw, ws, None, stage)
     torch.cuda.synchronize()
     assert np.array_equal(yt.cpu().numpy(), full) and np.array_equal(ridx.cpu().numpy(), fidx)
     assert np.array_equal(rw.cpu().numpy(), fw)
 
 
-def test_nan_propagates(moe):
+@pytest.mark.parametrize("T", [3, 6])
+def test_nan_propagates(moe, T):
     """A NaN in x reaches every output of its token and no other token."""
     dims = syn.WORKLOADS["tiny"].dims
     dense, experts, lw = _canonical_layer(dims)
-    x = syn.tokens(5, 3, dims.hidden)
+    x = syn.tokens(5, T, dims.hidden)
     x[1, 17] = np.nan
     out, idx, wt = run_layer(dims, lw, x)
     assert np.all(np.isnan(out[1]))
-    assert np.all(np.isfinite(out[0])) and np.all(np.isfinite(out[2]))
+    assert np.all(np.isfinite(np.delete(out, 1, axis=0)))
 
 
 def test_zero_router_selects_first_experts(moe):
