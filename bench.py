@@ -172,10 +172,11 @@ def main():
         moe.moe_layer_forward(dims, descs[j % R], pool[j], out[j], T, ridx[j], rw[j], wss[j], wsb)
     torch.cuda.synchronize()
     n_stages = moe.moe_forward_stage_count(dims, T)
-    grouped = n_stages == 6
+    grouped = n_stages == 7
     if grouped:
-        names = ["k_router", "k_route_group", "k_grouped_gateup", "k_encode_act", "k_grouped_down", "k_combine"]
-        gu_stage, down_stage = 2, 4
+        names = ["k_norm_batch", "k_router_mfma", "k_route_tokens", "k_grouped_gateup", "k_encode_act",
+                 "k_grouped_down", "k_combine"]
+        gu_stage, down_stage = 3, 5
         M = 64
     else:
         names = ["k_router", "k_gateup", "k_down"]

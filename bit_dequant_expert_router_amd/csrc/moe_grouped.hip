@@ -8,11 +8,13 @@
 // token counts are far too small for a dense tile, so the routed experts stay
 // on the dequant-GEMV kernels with a loop over each expert's tokens.
 //
-//   k_router        (moe_forward.hip) RMSNorm, router logits and the limb form of h
-//   k_route_group   one block: softmax/top-K/renormalise of every token, then a
-//                   histogram of assignments per expert, an exclusive scan and a
-//                   stable scatter (token order kept inside each expert), and the
-//                   compact list of touched experts
+//   k_norm_batch, k_router_mfma (moe_batch_router.hip) RMSNorm, limb and bf16
+//                   forms of h, router logits on the matrix cores
+//   k_route_tokens  one block per token: softmax/top-K/renormalise; the last
+//                   block to finish builds a histogram of assignments per
+//                   expert, an exclusive scan, a stable scatter (token order
+//                   kept inside each expert) and the compact list of touched
+//                   experts
 //   k_grouped_gateup  one block per (touched expert, row chunk): gate+up rows read
 //                   once, applied to every token of the expert, SwiGLU; the shared
 //                   expert gets its own blocks over all tokens
@@ -58,10 +60,45 @@ __device__ __forceinline__ int wave_excl_scan(int v) {
 }
 
 // ---------------------------------------------------------------------------
-// k_route_group: routing of every token and grouping of assignments by expert
+// routing of every token and grouping of assignments by expert
 // ---------------------------------------------------------------------------
+// logits of token t: the KS partial sums of the router GEMM, every load issued
+// at once, added in a fixed order
 template <int EPL>
-__global__ __launch_bounds__(1024) void k_route_group(FwdArgs a) {
+__device__ __forceinline__ void token_logits(const FwdArgs &a, int t, float (&zv)[EPL], float &gs) {
+    const int E = a.s.E, T = a.T, ksn = router_ksplit(a.s.H);
+    const int lane = threadIdx.x & 63;
+    const float *zt = a.ws.zp + (size_t)t * (E + 1);
+    const size_t kstride = (size_t)T * (E + 1);
+    float z[kMaxKsplit][EPL], g[kMaxKsplit];
+#pragma unroll
+    for (int ks = 0; ks < kMaxKsplit; ++ks) {
+        const float *zk = zt + (size_t)(ks < ksn ? ks : 0) * kstride;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            z[ks][i] = zk[e < E ? e : E - 1];
+        }
+        g[ks] = zk[E];
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) zv[i] = z[0][i];
+    gs = g[0];
+#pragma unroll
+    for (int ks = 1; ks < kMaxKsplit; ++ks) {
+        if (ks < ksn) {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) zv[i] += z[ks][i];
+            gs += g[ks];
+        }
+    }
+}
+
+// grouping of all T*K assignments by expert, by one block of 256 threads:
+// histogram, exclusive scans, the compact list of touched experts, and a
+// stable scatter (token order kept inside each expert)
+__device__ void group_assignments(const FwdArgs &a) {
+    constexpr int NT = 256;
     const int T = a.T, E = a.s.E, K = a.s.K;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int TK = T * K;
@@ -75,27 +112,12 @@ __global__ __launch_bounds__(1024) void k_route_group(FwdArgs a) {
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_off[kMaxExperts];
     __shared__ int s_tch[kMaxExperts];
+    __shared__ uint32_t s_mask[kMaxExperts];
 
-    for (int i = threadIdx.x; i < E; i += 1024) s_cnt[i] = 0;
-    // routing, one token per wave
-    for (int t = wave; t < T; t += 16) {
-        float zv[EPL];
-        load_logits<EPL>(a.ws.z + (size_t)t * E, E, zv);
-        int my_sel;
-        float my_w;
-        route_wave<EPL>(zv, E, K, my_sel, my_w);
-        if (lane < K) {
-            s_sel[t * K + lane] = my_sel;
-            a.ws.sel[t * K + lane] = my_sel;
-            a.ws.coef[t * (K + 1) + lane] = my_w;
-            if (a.route_idx) a.route_idx[t * K + lane] = my_sel;
-            if (a.route_w) a.route_w[t * K + lane] = my_w;
-        } else if (lane == K) {
-            a.ws.coef[t * (K + 1) + K] = sigmoidf_(a.ws.gs[t]);
-        }
-    }
+    for (int i = threadIdx.x; i < E; i += NT) s_cnt[i] = 0;
+    for (int i = threadIdx.x; i < TK; i += NT) s_sel[i] = a.ws.sel[i];
     __syncthreads();
-    for (int i = threadIdx.x; i < TK; i += 1024) atomicAdd(&s_cnt[s_sel[i]], 1);
+    for (int i = threadIdx.x; i < TK; i += NT) atomicAdd(&s_cnt[s_sel[i]], 1);
     __syncthreads();
     // exclusive scans of the counts and of the touched flags (E <= 1024: 16 per lane)
     if (wave == 0) {
@@ -123,7 +145,7 @@ __global__ __launch_bounds__(1024) void k_route_group(FwdArgs a) {
         if (lane == 63) a.ws.grp[0] = pf;  // number of touched experts
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 1024) {
+    for (int e = threadIdx.x; e < E; e += NT) {
         if (s_cnt[e] > 0) {
             const int u = s_tch[e];
             expert[u] = e;
@@ -131,13 +153,61 @@ __global__ __launch_bounds__(1024) void k_route_group(FwdArgs a) {
             count[u] = s_cnt[e];
         }
     }
-    // stable scatter: rank of an assignment among the earlier ones of its expert
-    for (int i = threadIdx.x; i < TK; i += 1024) {
-        const int e = s_sel[i];
-        int r = 0;
-        for (int j = 0; j < i; ++j) r += (s_sel[j] == e) ? 1 : 0;
-        perm[s_off[e] + r] = i;
+    // stable scatter, 32 tokens at a time: bit t - c0 of s_mask[e] marks token t
+    // as a user of expert e (the K experts of a token are distinct), so the rank
+    // of (t, e) among e's assignments is the users before c0 (s_off advanced
+    // chunk by chunk) plus the bits below t - c0
+    for (int c0 = 0; c0 < T; c0 += 32) {
+        for (int e = threadIdx.x; e < E; e += NT) s_mask[e] = 0u;
+        __syncthreads();
+        const int i0 = c0 * K, i1 = min(T, c0 + 32) * K;
+        for (int i = i0 + threadIdx.x; i < i1; i += NT) atomicOr(&s_mask[s_sel[i]], 1u << (i / K - c0));
+        __syncthreads();
+        for (int i = i0 + threadIdx.x; i < i1; i += NT) {
+            const int e = s_sel[i];
+            const uint32_t below = s_mask[e] & ((1u << (i / K - c0)) - 1u);
+            perm[s_off[e] + __popc(below)] = i;
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < E; e += NT) s_off[e] += __popc(s_mask[e]);
+        __syncthreads();
     }
+}
+
+// ---------------------------------------------------------------------------
+// k_route_tokens: one block per token; wave 0 sums the partial logits and
+// routes (softmax -> top-K -> renormalise).  The block that finishes last
+// (a counter in the workspace's control block, reset by that block) groups
+// the assignments of the whole batch.
+// ---------------------------------------------------------------------------
+template <int EPL>
+__global__ __launch_bounds__(256) void k_route_tokens(FwdArgs a) {
+    const int t = blockIdx.x, K = a.s.K, E = a.s.E;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (wave == 0) {
+        float zv[EPL], gs;
+        token_logits<EPL>(a, t, zv, gs);
+        int my_sel;
+        float my_w;
+        route_wave<EPL>(zv, E, K, my_sel, my_w);
+        if (lane < K) {
+            a.ws.sel[t * K + lane] = my_sel;
+            a.ws.coef[t * (K + 1) + lane] = my_w;
+            if (a.route_idx) a.route_idx[t * K + lane] = my_sel;
+            if (a.route_w) a.route_w[t * K + lane] = my_w;
+        } else if (lane == K) {
+            a.ws.coef[t * (K + 1) + K] = sigmoidf_(gs);
+        }
+        __threadfence();  // this token's routing visible to every block
+    }
+    __syncthreads();
+    __shared__ int s_last;
+    if (threadIdx.x == 0) s_last = atomicAdd(&a.ws.ctrl[0], 1u) == (unsigned)(a.T - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();  // every other token's routing is visible from here on
+    group_assignments(a);
+    if (threadIdx.x == 0) a.ws.ctrl[0] = 0u;
 }
 
 // unit of work of the grouped kernels: a touched expert (or the shared expert
@@ -164,13 +234,13 @@ __device__ __forceinline__ Unit decode_unit(const FwdArgs &a, const GroupView &g
         u.count = (a.T - u.first) < shared_tok_chunk ? (a.T - u.first) : shared_tok_chunk;
         u.live = u.count > 0;
     } else {
+        // r < G always: the four loads go out together
         const int r = ui - n_shared;
-        if (r < *gv.n_touched) {
-            u.live = true;
-            u.expert = gv.expert[r];
-            u.first = gv.first[r];
-            u.count = gv.count[r];
-        }
+        const int nt = *gv.n_touched;
+        u.expert = gv.expert[r];
+        u.first = gv.first[r];
+        u.count = gv.count[r];
+        u.live = r < nt;
     }
     return u;
 }
@@ -455,15 +525,15 @@ hipError_t launch_grouped_bits(const FwdArgs &a, int stage, hipStream_t st) {
     const int G = (T * K < E) ? T * K : E;
     const int units = G + (T + kSharedTokChunk - 1) / kSharedTokChunk;
     switch (stage) {
-        case 1:
-            if (E > 512)
-                hipLaunchKernelGGL(k_route_group<16>, dim3(1), dim3(1024), 0, st, a);
-            else
-                hipLaunchKernelGGL(k_route_group<8>, dim3(1), dim3(1024), 0, st, a);
-            break;
         case 2:
-        case 4: {
-            const bool down = stage == 4;
+            if (E > 512)
+                hipLaunchKernelGGL(k_route_tokens<16>, dim3((unsigned)T), dim3(256), 0, st, a);
+            else
+                hipLaunchKernelGGL(k_route_tokens<8>, dim3((unsigned)T), dim3(256), 0, st, a);
+            break;
+        case 3:
+        case 5: {
+            const bool down = stage == 5;
             switch (a.L.m[down ? 2 : 0].cpl) {
                 case 1: launch_grouped_mats<BITS, 1>(a, units, st, down); break;
                 case 2: launch_grouped_mats<BITS, 2>(a, units, st, down); break;
@@ -471,14 +541,14 @@ hipError_t launch_grouped_bits(const FwdArgs &a, int stage, hipStream_t st) {
             }
             break;
         }
-        case 3: {
+        case 4: {
             const int n_pairs = T * (K + 1);
             const int ppb = 256 / (F / 16);
             hipLaunchKernelGGL(k_encode_act<BITS>, dim3((unsigned)((n_pairs + ppb - 1) / ppb)), dim3(256), 0, st, a,
                                n_pairs);
             break;
         }
-        case 5:
+        case 6:
             hipLaunchKernelGGL(k_combine, dim3((unsigned)((H + 255) / 256), (unsigned)T), dim3(256), 0, st, a);
             break;
         default: return hipErrorInvalidValue;
@@ -488,10 +558,10 @@ hipError_t launch_grouped_bits(const FwdArgs &a, int stage, hipStream_t st) {
 
 }  // namespace
 
-// stage 0 is the per-token path's RMSNorm + router + limbs of h
+// stages 0 and 1: batched RMSNorm and router GEMM
 hipError_t launch_grouped_stage(const FwdArgs &a, int stage, hipStream_t stream) {
     (void)hipGetLastError();
-    if (stage == 0) return launch_forward_stage(a, 0, stream);
+    if (stage < 2) return launch_batch_router(a, stage, stream);
     if (a.s.bits == 4) return launch_grouped_bits<4>(a, stage, stream);
     if (a.s.bits == 2) return launch_grouped_bits<2>(a, stage, stream);
     return hipErrorInvalidValue;

@@ -15,7 +15,8 @@ MOE_HD size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 // Workspace of one forward call, carved from the caller's buffer.
 struct Workspace {
-    uint32_t *ctrl;  // control block (barrier counters), kCtrlBytes, zero between calls
+    uint32_t *ctrl;  // control block, kCtrlBytes, zero between calls: [0] tokens routed so far
+                     // (the grouped path's last routing block resets it)
     float *h;        // [T][H]   normalised tokens
     float *z;        // [T][E]   router logits
     float *gs;       // [T]      shared-gate logits
@@ -32,7 +33,15 @@ struct Workspace {
     int8_t *al;      // [T][K+1][7][F/8] dwords: limbs of the activations, in the down codes' order
     float *as;       // [T][K+1][F/64] group scales of those limbs
     float *ax;       // [T][K+1][F/32] sums of the activations over each half group
+    uint16_t *hb;    // h = hi + mid + lo in bf16, the router GEMM's operand, in fragment order:
+                     // [ceil(T/32)][H/16][3][64 lanes][8] (see k_norm_batch)
+    float *zp;       // [KS][T][E+1] partial router logits (column E: shared gate), KS = router_ksplit(H)
 };
+
+// k-splits of the batched router GEMM: 512 reduction entries per block when H >= 512
+constexpr int kMaxKsplit = kMaxDim / 512;
+MOE_HD int router_ksplit(int H) { return H >= 512 ? H / 512 : 1; }
+MOE_HD int token_tiles(int T) { return (T + 31) / 32; }
 
 struct Shape {
     int H, F, E, K, bits;
@@ -61,6 +70,8 @@ inline size_t workspace_bytes(const Shape &s, int T) {
     b += align_up((size_t)T * (s.K + 1) * 4 * s.F);  // 7 limbs x F/2 bytes fit in 4 F
     b += align_up((size_t)T * (s.K + 1) * (s.F / 64) * 4);
     b += align_up((size_t)T * (s.K + 1) * (s.F / 32) * 4);
+    b += align_up((size_t)token_tiles(T) * 32 * 3 * s.H * 2);
+    b += align_up((size_t)router_ksplit(s.H) * T * (s.E + 1) * 4);
     return b;
 }
 
@@ -96,6 +107,10 @@ inline Workspace carve_workspace(void *base, const Shape &s, int T) {
     w.as = (float *)p;
     p += align_up((size_t)T * (s.K + 1) * (s.F / 64) * 4);
     w.ax = (float *)p;
+    p += align_up((size_t)T * (s.K + 1) * (s.F / 32) * 4);
+    w.hb = (uint16_t *)p;
+    p += align_up((size_t)token_tiles(T) * 32 * 3 * s.H * 2);
+    w.zp = (float *)p;
     return w;
 }
 
@@ -121,10 +136,12 @@ constexpr int kForwardStages = 3;
 // take the grouped-by-expert path
 constexpr int kGroupMinTokens = 4;
 constexpr int kGroupMaxAssign = 4096;
-constexpr int kGroupedStages = 6;
+constexpr int kGroupedStages = 7;
 inline bool uses_grouped(const Shape &s, int T) { return T >= kGroupMinTokens && T * s.K <= kGroupMaxAssign; }
 hipError_t launch_grouped(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_grouped_stage(const FwdArgs &a, int stage, hipStream_t stream);
+// batched RMSNorm (stage 0) and router GEMM (stage 1) of the grouped path
+hipError_t launch_batch_router(const FwdArgs &a, int stage, hipStream_t stream);
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_forward_stage(const FwdArgs &a, int stage, hipStream_t stream);
 

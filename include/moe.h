@@ -177,10 +177,11 @@ int moe_layer_forward(const moe_dims_t *dims, const moe_layer_t *layer, const fl
  * shared-gate logit; 1 softmax/top-K/renormalise and the fused gate+up dequant
  * GEMV with SwiGLU for the selected and the shared experts; 2 down projection
  * with the weighted combine, sigmoid-gated shared expert and residual.
- * Grouped path (6 stages): 0 as above; 1 routing of every token and grouping
- * of the assignments by expert; 2 gate+up with SwiGLU per touched expert over
- * its tokens (and the shared expert over all tokens); 3 limb encoding of the
- * activations; 4 down projection per touched expert; 5 weighted combine,
+ * Grouped path (7 stages): 0 RMSNorm of every token; 1 router GEMM and
+ * shared-gate logits; 2 softmax/top-K/renormalise of every token and grouping
+ * of the assignments by expert; 3 gate+up with SwiGLU per touched expert over
+ * its tokens (and the shared expert over all tokens); 4 limb encoding of the
+ * activations; 5 down projection per touched expert; 6 weighted combine,
  * sigmoid-gated shared expert and residual.
  * Arguments as for moe_layer_forward; a stage outside 0 .. count-1 is
  * MOE_ERR_INVALID_ARG.
@@ -189,7 +190,7 @@ int moe_layer_forward_stage(const moe_dims_t *dims, const moe_layer_t *layer, co
                             int32_t n_tokens, int32_t *route_idx, float *route_w, void *workspace,
                             size_t workspace_bytes, int32_t stage, void *stream);
 
-/* Number of stages of moe_layer_forward_stage for this batch size (3 or 6), or
+/* Number of stages of moe_layer_forward_stage for this batch size (3 or 7), or
  * a negative status for invalid dims or n_tokens outside 1 .. 65535. */
 int moe_forward_stage_count(const moe_dims_t *dims, int32_t n_tokens);
 

@@ -173,8 +173,8 @@ def test_stage_count():
     K = dims.top_k
     assert moe.moe_forward_stage_count(dims, 1) == 3
     assert moe.moe_forward_stage_count(dims, 3) == 3
-    assert moe.moe_forward_stage_count(dims, 4) == 6
-    assert moe.moe_forward_stage_count(dims, 4096 // K) == 6
+    assert moe.moe_forward_stage_count(dims, 4) == 7
+    assert moe.moe_forward_stage_count(dims, 4096 // K) == 7
     assert moe.moe_forward_stage_count(dims, 4096 // K + 1) == 3
     f = moe._lib.moe_forward_stage_count
     assert f(ctypes.byref(dims), 0) == moe.MOE_ERR_INVALID_ARG
@@ -190,7 +190,7 @@ def test_grouped_stage_rejects():
     wsb = moe.moe_workspace_bytes(dims, T)
     f = moe._lib.moe_layer_forward_stage
     lay = _layer()
-    for stage in (-1, 6, 100):
+    for stage in (-1, 7, 100):
         assert f(ctypes.byref(dims), ctypes.byref(lay), A + 0x300000, A + 0x400000, T, None, None, A + 0x500000,
                  wsb, stage, None) == moe.MOE_ERR_INVALID_ARG
 

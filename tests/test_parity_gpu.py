@@ -99,7 +99,7 @@ def test_inplace_determinism_and_optional_outputs(moe, n_tokens):
 @pytest.mark.parametrize("T", [3, 6])
 def test_stages_equal_full_forward(moe, T):
     """The stages enqueued one by one give exactly the one-call result, on the
-    per-token path (3 tokens, 3 stages) and the grouped path (6 tokens, 6 stages)."""
+    per-token path (3 tokens, 3 stages) and the grouped path (6 tokens, 7 stages)."""
     dims = syn.WORKLOADS["tiny"].dims
     dense, experts, lw = _canonical_layer(dims)
     x = syn.tokens(4, T, dims.hidden)
@@ -111,7 +111,7 @@ def test_stages_equal_full_forward(moe, T):
     ws = torch.empty(moe.moe_workspace_bytes(dims, T), dtype=torch.uint8, device="cuda")
     moe.moe_workspace_init(ws)
     n_stages = moe.moe_forward_stage_count(dims, T)
-    assert n_stages == (3 if T < 4 else 6)
+    assert n_stages == (3 if T < 4 else 7)
     for stage in range(n_stages):
         moe.moe_layer_forward_stage(dims, lw.descriptor(), xt, yt, T, ridx, rw, ws, None, stage)
     torch.cuda.synchronize()
