@@ -328,6 +328,141 @@ __device__ __forceinline__ float qdot(const uint4 (&c)[CPL], const uint32_t (&sb
     return total;
 }
 
+// Variant for weights reused across several activation vectors: the codes are
+// prepared once per row (4-bit: made signed by the XOR), the group scale s and
+// offset o = b + off * s are unpacked once, and the seven limb sums are
+// combined in integers by Horner steps (limbs 4-6 and 0-3: |sum| < 2^25),
+// then in fp32: f = hi * 2^16 + lo.
+template <int BITS, int CPL>
+struct RowPrep {
+    using Q = QSlice<BITS, CPL>;
+    uint4 q[CPL];
+    float s[Q::NGL], o[Q::NGL];
+};
+
+template <int BITS, int CPL>
+__device__ __forceinline__ void prep_row(const uint4 (&c)[CPL], const uint32_t (&sb)[QSlice<BITS, CPL>::NGL],
+                                         RowPrep<BITS, CPL> &r) {
+    using Q = QSlice<BITS, CPL>;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        if constexpr (BITS == 4)
+            r.q[j] = make_uint4(c[j].x ^ 0x88888888u, c[j].y ^ 0x88888888u, c[j].z ^ 0x88888888u, c[j].w ^ 0x88888888u);
+        else
+            r.q[j] = c[j];
+    }
+#pragma unroll
+    for (int g = 0; g < Q::NGL; ++g) {
+        r.s[g] = bf16_lo(sb[g]);
+        r.o[g] = fmaf(Q::kCodeOffset, r.s[g], bf16_hi(sb[g]));
+    }
+}
+
+template <int BITS, int CPL>
+__device__ __forceinline__ float qdot_prep(const RowPrep<BITS, CPL> &r, const LimbSlice<BITS, CPL> &v) {
+    using Q = QSlice<BITS, CPL>;
+    // dword list of the slice: (operand, limb dword index, group)
+    constexpr int ND = BITS == 4 ? CPL * 4 : CPL * 8;
+    int op[ND];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const uint32_t d[4] = {r.q[j].x, r.q[j].y, r.q[j].z, r.q[j].w};
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+            if constexpr (BITS == 4) {
+                op[j * 4 + w4] = (int)d[w4];
+            } else {
+                op[j * 8 + 2 * w4] = (int)(d[w4] & 0x33333333u);
+                op[j * 8 + 2 * w4 + 1] = (int)((d[w4] >> 2) & 0x33333333u);
+            }
+        }
+    }
+    constexpr int DPG = ND / Q::NGL;  // limb dwords per group
+    float total = 0.0f;
+#pragma unroll
+    for (int g = 0; g < Q::NGL; ++g) {
+        int hi = 0, lo = 0;
+#pragma unroll
+        for (int x = kLimbs - 1; x >= 4; --x) {
+            if (x != kLimbs - 1) hi <<= 4;
+#pragma unroll
+            for (int i = 0; i < DPG; ++i) hi = __builtin_amdgcn_sdot8(op[g * DPG + i], v.L[x][g * DPG + i], hi, false);
+        }
+#pragma unroll
+        for (int x = 3; x >= 0; --x) {
+            if (x != 3) lo <<= 4;
+#pragma unroll
+            for (int i = 0; i < DPG; ++i) lo = __builtin_amdgcn_sdot8(op[g * DPG + i], v.L[x][g * DPG + i], lo, false);
+        }
+        const float f = fmaf((float)hi, 65536.0f, (float)lo);
+        total = fmaf(r.s[g] * v.S[g], f, total);
+        total = fmaf(r.o[g], v.X[g], total);
+    }
+    return total;
+}
+
+// ---------------------------------------------------------------------------
+// several partial sums reduced at once over aligned groups of W lanes
+// (N <= W, both powers of two).  The first log2(N) exchange steps halve the
+// list (a lane keeps the half its lane bit selects and adds its partner's copy
+// of that half), the remaining steps are plain sums.  Lane l ends with list
+// entry j = sum over the halving steps s of bit b_s(l) * N / 2^(s+1), where
+// b_s = log2(W) - 1 - s; every lane of the sub-group W / N shares it.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ float xchg(float v) {  // partner's copy of v across lane bit log2(D)
+    if constexpr (D == 32) {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return __uint_as_float((threadIdx.x & 32) ? p[0] : p[1]);
+    } else if constexpr (D == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return __uint_as_float((threadIdx.x & 16) ? p[0] : p[1]);
+    } else {
+        constexpr int C = D == 8 ? kDppMirror : D == 4 ? kDppHalfMirror : D == 2 ? kDppXor2 : kDppXor1;
+        return __uint_as_float(dpp_u<C>(__float_as_uint(v)));
+    }
+}
+
+template <int D>
+__device__ __forceinline__ float halve(float a, float b) {  // keep a (lane bit clear) or b (set), plus partner's
+    if constexpr (D == 32) {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    } else if constexpr (D == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    } else {
+        const bool hi = (threadIdx.x & D) != 0;
+        return (hi ? b : a) + xchg<D>(hi ? a : b);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ float plain_reduce(float x) {
+    if constexpr (D >= 1) return plain_reduce<D / 2>(x + xchg<D>(x));
+    else return x;
+}
+
+template <int N, int W, int D = W / 2>
+__device__ __forceinline__ float multi_reduce(float (&v)[N]) {
+    static_assert(N <= W, "one list entry per lane at least");
+    if constexpr (N == 1) {
+        return plain_reduce<D>(v[0]);
+    } else {
+        float h[N / 2];
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) h[i] = halve<D>(v[i], v[i + N / 2]);
+        return multi_reduce<N / 2, W, D / 2>(h);
+    }
+}
+
+// list index held by the lane after multi_reduce<N, W>
+template <int N, int W>
+__device__ __forceinline__ int multi_index(int lane) {
+    if constexpr (N == 1) return 0;
+    else return ((lane & (W / 2)) ? N / 2 : 0) + multi_index<N / 2, W / 2>(lane);
+}
+
 template <int BITS, int CPL>
 __device__ __forceinline__ void load_row(const uint8_t *__restrict__ ex, const QMat &q, int r, int lr,
                                          uint4 (&c)[CPL], uint32_t (&sb)[QSlice<BITS, CPL>::NGL]) {

@@ -284,83 +284,6 @@ __device__ __forceinline__ void load_limb_slice(const uint32_t *hl, const float 
     }
 }
 
-// the normalised token t
-template <int BITS, int CPL>
-__device__ __forceinline__ void load_token_limbs(const FwdArgs &a, int t, int k0, LimbSlice<BITS, CPL> &hv) {
-    const int H = a.s.H;
-    load_limb_slice<BITS, CPL>((const uint32_t *)a.ws.hl + (size_t)t * kLimbs * (H / 8), a.ws.hs + (size_t)t * (H / 64),
-                               a.ws.hx + (size_t)t * (H / 32), H, k0, hv);
-}
-
-// the activation vector of (token, slot) pair p
-template <int BITS, int CPL>
-__device__ __forceinline__ void load_act_limbs(const FwdArgs &a, int p, int k0, LimbSlice<BITS, CPL> &hv) {
-    const int F = a.s.F;
-    load_limb_slice<BITS, CPL>((const uint32_t *)a.ws.al + (size_t)p * kLimbs * (F / 8), a.ws.as + (size_t)p * (F / 64),
-                               a.ws.ax + (size_t)p * (F / 32), F, k0, hv);
-}
-
-// ---------------------------------------------------------------------------
-// k_grouped_gateup
-// ---------------------------------------------------------------------------
-template <int BITS, int CPL, int RPW>
-__global__ __launch_bounds__(256) void k_grouped_gateup(FwdArgs a, int chunks, int shared_tok_chunk) {
-    using Q = QSlice<BITS, CPL>;
-    const int F = a.s.F, K = a.s.K;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const GroupView gv = group_view(a);
-    const Unit u = decode_unit(a, gv, blockIdx.x / chunks, shared_tok_chunk);
-    if (!u.live) return;
-    const QMat &G = a.L.m[0];
-    const QMat &U = a.L.m[1];
-    const int lpr = G.lpr, rpi = 64 / lpr;
-    const int lr = lane % lpr, rsub = lane / lpr;
-    const int nrs = F / rpi;
-    const int rs0 = ((blockIdx.x % chunks) * 4 + wave) * RPW;
-    if (rs0 >= nrs) return;
-    const uint8_t *ex = u.shared ? a.shared : a.experts + (size_t)u.expert * a.L.bytes;
-
-    uint4 gc[RPW][CPL], uc[RPW][CPL];
-    uint32_t gsb[RPW][Q::NGL], usb[RPW][Q::NGL];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int rs = rs0 + i;
-        if (rs < nrs) {
-            load_row<BITS, CPL>(ex, G, rs * rpi + rsub, lr, gc[i], gsb[i]);
-            load_row<BITS, CPL>(ex, U, rs * rpi + rsub, lr, uc[i], usb[i]);
-        }
-    }
-    const int k0 = lr * Q::NV;
-    int t, slot;
-    unit_item(a, gv, u, 0, t, slot);
-    LimbSlice<BITS, CPL> hv;
-    load_token_limbs<BITS, CPL>(a, t, k0, hv);
-    for (int it = 0; it < u.count; ++it) {
-        // the next token's limbs are loaded while this token is computed
-        int tn = t, sn = slot;
-        LimbSlice<BITS, CPL> hn;
-        if (it + 1 < u.count) {
-            unit_item(a, gv, u, it + 1, tn, sn);
-            load_token_limbs<BITS, CPL>(a, tn, k0, hn);
-        }
-        float *act = a.ws.act + ((size_t)t * (K + 1) + slot) * F;
-#pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-            const int rs = rs0 + i;
-            if (rs < nrs) {
-                float g = qdot<BITS, CPL>(gc[i], gsb[i], hv);
-                float v = qdot<BITS, CPL>(uc[i], usb[i], hv);
-                g = lane_group_sum(g, lpr);
-                v = lane_group_sum(v, lpr);
-                if (lr == 0) act[rs * rpi + rsub] = g * sigmoidf_(g) * v;
-            }
-        }
-        t = tn;
-        slot = sn;
-        hv = hn;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // k_encode_act: limb form of every (token, slot) activation vector, in the
 // order of the down projection's byte-order codes.  A thread takes 16
@@ -425,57 +348,150 @@ __global__ __launch_bounds__(256) void k_encode_act(FwdArgs a, int n_pairs) {
 }
 
 // ---------------------------------------------------------------------------
-// k_grouped_down: one block per (unit, chunk of rows); exact code x limb
-// products as in gate/up, activations taken from k_encode_act's limbs
+// k_grouped_stream: the dequant GEMV of one expert matrix pair (gate + up, with
+// SwiGLU) or of the down matrix, for the tokens of one unit and a range of rows.
+//
+// A block takes one unit (a touched expert, or the shared expert and a chunk of
+// tokens) and a range of row-steps.  It stages the limb form of up to TP
+// vectors of the unit (tokens h for gate/up, (token, slot) activations for
+// down) in LDS once, then every wave streams its row-steps: the weights of
+// step s+1 are loaded into one register set while step s is computed from the
+// other, so HBM requests stay in flight through the compute.  Each step's
+// rows are applied to every staged vector (weights read from HBM once per
+// pass; a unit with more than TP vectors takes several passes).
 // ---------------------------------------------------------------------------
-template <int BITS, int CPL, int RPW>
-__global__ __launch_bounds__(256) void k_grouped_down(FwdArgs a, int chunks, int shared_tok_chunk) {
+// words of one staged vector of length n: limbs [7][n/8], scales [n/64], half
+// sums [n/32], rounded up to 16 bytes
+MOE_HD int stage_words(int n) { return (kLimbs * (n / 8) + n / 64 + n / 32 + 3) & ~3; }
+
+template <int BITS, int CPL, int NM, int RPW>
+struct StepWeights {
     using Q = QSlice<BITS, CPL>;
-    const int H = a.s.H, K = a.s.K;
+    uint4 c[NM][RPW][CPL];
+    uint32_t sb[NM][RPW][Q::NGL];
+};
+
+// LPR: lanes per row when the partial sums of a step are reduced together
+// (16, 32 or 64); 0: any other width, one reduction per row
+template <int BITS, int CPL, int RPW, bool DOWN, int LPR>
+__global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, int chunks, int shared_tok_chunk, int tp) {
+    using Q = QSlice<BITS, CPL>;
+    constexpr int NM = DOWN ? 1 : 2;
+    constexpr int NV = NM * RPW;  // partial sums per lane per step and vector
+    extern __shared__ uint4 s_dyn[];
+    uint32_t *s_vec = (uint32_t *)s_dyn;
+    __shared__ int s_out[16];  // output vector index (t * (K+1) + slot) per staged vector
+    const int H = a.s.H, F = a.s.F, K = a.s.K;
+    const int n = DOWN ? F : H;  // reduction length
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const GroupView gv = group_view(a);
     const Unit u = decode_unit(a, gv, blockIdx.x / chunks, shared_tok_chunk);
     if (!u.live) return;
-    const QMat &Dm = a.L.m[2];
-    const int lpr = Dm.lpr, rpi = 64 / lpr;
+    const QMat &M0 = a.L.m[DOWN ? 2 : 0];
+    const QMat &M1 = a.L.m[1];
+    const int lpr = LPR ? LPR : M0.lpr, rpi = 64 / lpr;
     const int lr = lane % lpr, rsub = lane / lpr;
-    const int nrs = H / rpi;
-    const int rs0 = ((blockIdx.x % chunks) * 4 + wave) * RPW;
-    if (rs0 >= nrs) return;
+    const int nrs = M0.rows / rpi;
+    const int per_block = (nrs + chunks - 1) / chunks;
+    const int rs_lo = (blockIdx.x % chunks) * per_block;
+    const int rs_hi = min(nrs, rs_lo + per_block);
+    const int nsteps = (rs_hi - rs_lo + 4 * RPW - 1) / (4 * RPW);
     const uint8_t *ex = u.shared ? a.shared : a.experts + (size_t)u.expert * a.L.bytes;
-
-    uint4 wc[RPW][CPL];
-    uint32_t wsb[RPW][Q::NGL];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int rs = rs0 + i;
-        if (rs < nrs) load_row<BITS, CPL>(ex, Dm, rs * rpi + rsub, lr, wc[i], wsb[i]);
-    }
+    const int words = stage_words(n);
     const int k0 = lr * Q::NV;
-    int t, slot;
-    unit_item(a, gv, u, 0, t, slot);
-    LimbSlice<BITS, CPL> av;
-    load_act_limbs<BITS, CPL>(a, t * (K + 1) + slot, k0, av);
-    for (int it = 0; it < u.count; ++it) {
-        // the next pair's limbs are loaded while this one is computed
-        int tn = t, sn = slot;
-        LimbSlice<BITS, CPL> an;
-        if (it + 1 < u.count) {
-            unit_item(a, gv, u, it + 1, tn, sn);
-            load_act_limbs<BITS, CPL>(a, tn * (K + 1) + sn, k0, an);
-        }
-        float *ys = a.ws.ys + ((size_t)t * (K + 1) + slot) * H;
+    const int out_len = DOWN ? H : F;
+    float *out_base = DOWN ? a.ws.ys : a.ws.act;
+
+    auto load_step = [&](int s, StepWeights<BITS, CPL, NM, RPW> &w) {
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
-            const int rs = rs0 + i;
-            if (rs < nrs) {
-                const float v = lane_group_sum(qdot<BITS, CPL>(wc[i], wsb[i], av), lpr);
-                if (lr == 0) ys[rs * rpi + rsub] = v;
+            const int rs = rs_lo + (s * 4 + wave) * RPW + i;
+            if (rs < rs_hi) {
+                load_row<BITS, CPL>(ex, M0, rs * rpi + rsub, lr, w.c[0][i], w.sb[0][i]);
+                if constexpr (NM == 2) load_row<BITS, CPL>(ex, M1, rs * rpi + rsub, lr, w.c[1][i], w.sb[1][i]);
             }
         }
-        t = tn;
-        slot = sn;
-        av = an;
+    };
+    auto compute_step = [&](int s, const StepWeights<BITS, CPL, NM, RPW> &w, int np) {
+        const int rs0 = rs_lo + (s * 4 + wave) * RPW;
+        RowPrep<BITS, CPL> rp[NM][RPW];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i)
+#pragma unroll
+            for (int m = 0; m < NM; ++m) prep_row<BITS, CPL>(w.c[m][i], w.sb[m][i], rp[m][i]);
+        for (int v = 0; v < np; ++v) {
+            const uint32_t *vec = s_vec + (size_t)v * words;
+            LimbSlice<BITS, CPL> hv;
+            load_limb_slice<BITS, CPL>(vec, (const float *)(vec + kLimbs * (n / 8)),
+                                       (const float *)(vec + kLimbs * (n / 8) + n / 64), n, k0, hv);
+            float *out = out_base + (size_t)s_out[v] * out_len;
+            if constexpr (LPR != 0) {
+                // every row of the step at once; rows past the block's range
+                // are computed on stale registers and not written
+                float part[NV];
+#pragma unroll
+                for (int i = 0; i < RPW; ++i)
+#pragma unroll
+                    for (int m = 0; m < NM; ++m) part[NM * i + m] = qdot_prep<BITS, CPL>(rp[m][i], hv);
+                const float r = multi_reduce<NV, LPR>(part);
+                constexpr int DL = LPR / NV;  // lanes sharing one reduced entry
+                const int j = multi_index<NV, LPR>(lane);
+                const int rs = rs0 + j / NM;
+                if constexpr (DOWN) {
+                    if ((lane & (DL - 1)) == 0 && rs < rs_hi) out[rs * rpi + rsub] = r;
+                } else {
+                    const float up = xchg<DL>(r);  // the up sum sits across the last halving bit
+                    const float act = r * up * __builtin_amdgcn_rcpf(1.0f + __expf(-r));
+                    if ((lane & (2 * DL - 1)) == 0 && rs < rs_hi) out[rs * rpi + rsub] = act;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < RPW; ++i) {
+                    const int rs = rs0 + i;
+                    if (rs < rs_hi) {
+                        if constexpr (DOWN) {
+                            const float y = lane_group_sum(qdot_prep<BITS, CPL>(rp[0][i], hv), lpr);
+                            if (lr == 0) out[rs * rpi + rsub] = y;
+                        } else {
+                            const float g = lane_group_sum(qdot_prep<BITS, CPL>(rp[0][i], hv), lpr);
+                            const float up = lane_group_sum(qdot_prep<BITS, CPL>(rp[1][i], hv), lpr);
+                            if (lr == 0) out[rs * rpi + rsub] = g * up * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    for (int p0 = 0; p0 < u.count; p0 += tp) {
+        const int np = min(tp, u.count - p0);
+        StepWeights<BITS, CPL, NM, RPW> wa, wb;
+        load_step(0, wa);  // in flight while the vectors are staged
+        if (p0 > 0) __syncthreads();  // the previous pass is done with LDS
+        // stage the np vectors: limbs as 16-byte pieces, then scales and half sums
+        for (int v = 0; v < np; ++v) {
+            int t, slot;
+            unit_item(a, gv, u, p0 + v, t, slot);
+            const int pv = t * (K + 1) + slot;
+            if (threadIdx.x == 0) s_out[v] = pv;
+            const uint32_t *hl = DOWN ? (const uint32_t *)a.ws.al + (size_t)pv * kLimbs * (F / 8)
+                                      : (const uint32_t *)a.ws.hl + (size_t)t * kLimbs * (H / 8);
+            const float *hs = DOWN ? a.ws.as + (size_t)pv * (F / 64) : a.ws.hs + (size_t)t * (H / 64);
+            const float *hx = DOWN ? a.ws.ax + (size_t)pv * (F / 32) : a.ws.hx + (size_t)t * (H / 32);
+            uint32_t *dst = s_vec + (size_t)v * words;
+            for (int i = threadIdx.x; i < kLimbs * n / 32; i += 256) ((uint4 *)dst)[i] = ((const uint4 *)hl)[i];
+            for (int i = threadIdx.x; i < n / 64; i += 256) dst[kLimbs * (n / 8) + i] = __float_as_uint(hs[i]);
+            for (int i = threadIdx.x; i < n / 32; i += 256) dst[kLimbs * (n / 8) + n / 64 + i] = __float_as_uint(hx[i]);
+        }
+        __syncthreads();
+        for (int s = 0; s < nsteps; s += 2) {
+            if (s + 1 < nsteps) load_step(s + 1, wb);
+            compute_step(s, wa, np);
+            if (s + 1 < nsteps) {
+                if (s + 2 < nsteps) load_step(s + 2, wa);
+                compute_step(s + 1, wb, np);
+            }
+        }
     }
 }
 
@@ -494,36 +510,50 @@ __global__ __launch_bounds__(256) void k_combine(FwdArgs a) {
     a.y[(size_t)t * H + o] = acc;
 }
 
-// rows per wave of the grouped kernels, sized so that the weights, the current
-// and the prefetched limb slices stay in registers (NL = limb dwords per limb)
-constexpr int grouped_rpw(int bits, int cpl, bool down) {
-    const int nl = cpl * 16 / bits;
-    if (down) return nl <= 4 ? 8 : (nl <= 8 ? 4 : 2);
-    return nl <= 8 ? 4 : 2;
-}
-constexpr int kSharedTokChunk = 8;
+// row-slots per wave and step of k_grouped_stream: two register sets of
+// weights stay within ~80 VGPRs
+constexpr int stream_rpw(int cpl) { return cpl == 1 ? 4 : 2; }
+constexpr int kStreamStepsPerWave = 8;  // row-steps a wave streams per block
+constexpr int kStreamLdsBytes = 48 * 1024;
+constexpr int kStreamMaxVectors = 16;
 
-template <int BITS, int CPL>
-void launch_grouped_mats(const FwdArgs &a, int units, hipStream_t st, bool down) {
-    const QMat &M = a.L.m[down ? 2 : 0];
+// vectors staged per pass: as many as fit the LDS budget, at most 16
+inline int stream_vectors(int n) {
+    const int v = kStreamLdsBytes / (stage_words(n) * 4);
+    return v < kStreamMaxVectors ? v : kStreamMaxVectors;
+}
+
+template <int BITS, int CPL, bool DOWN, int LPR>
+void launch_stream(const FwdArgs &a, hipStream_t st) {
+    const QMat &M = a.L.m[DOWN ? 2 : 0];
     const int rpi = 64 / M.lpr;
     const int nrs = M.rows / rpi;
-    const int rpw = grouped_rpw(BITS, CPL, down);
-    const int chunks = (nrs + 4 * rpw - 1) / (4 * rpw);
-    const dim3 grid((unsigned)(units * chunks));
-    if (down)
-        hipLaunchKernelGGL((k_grouped_down<BITS, CPL, grouped_rpw(BITS, CPL, true)>), grid, dim3(256), 0, st, a, chunks,
-                           kSharedTokChunk);
-    else
-        hipLaunchKernelGGL((k_grouped_gateup<BITS, CPL, grouped_rpw(BITS, CPL, false)>), grid, dim3(256), 0, st, a,
-                           chunks, kSharedTokChunk);
+    constexpr int rpw = stream_rpw(CPL);
+    const int chunks = (nrs + 4 * rpw * kStreamStepsPerWave - 1) / (4 * rpw * kStreamStepsPerWave);
+    const int n = DOWN ? a.s.F : a.s.H;
+    const int tp = stream_vectors(n);
+    // shared-expert units of tp tokens: one pass each
+    const int units = touched_bound(a.s, a.T) + (a.T + tp - 1) / tp;
+    const size_t lds = (size_t)tp * stage_words(n) * 4;
+    hipLaunchKernelGGL((k_grouped_stream<BITS, CPL, rpw, DOWN, LPR>), dim3((unsigned)(units * chunks)), dim3(256), lds, st,
+                       a, chunks, tp, tp);
+}
+
+// the butterfly reduction needs lanes per row >= partial sums per lane
+template <int BITS, int CPL, bool DOWN>
+void launch_grouped_mats(const FwdArgs &a, hipStream_t st) {
+    constexpr int nv = (DOWN ? 1 : 2) * stream_rpw(CPL);
+    switch (a.L.m[DOWN ? 2 : 0].lpr) {
+        case 64: launch_stream<BITS, CPL, DOWN, 64>(a, st); break;
+        case 32: launch_stream<BITS, CPL, DOWN, (nv <= 32 ? 32 : 0)>(a, st); break;
+        case 16: launch_stream<BITS, CPL, DOWN, (nv <= 16 ? 16 : 0)>(a, st); break;
+        default: launch_stream<BITS, CPL, DOWN, 0>(a, st); break;
+    }
 }
 
 template <int BITS>
 hipError_t launch_grouped_bits(const FwdArgs &a, int stage, hipStream_t st) {
     const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K, T = a.T;
-    const int G = (T * K < E) ? T * K : E;
-    const int units = G + (T + kSharedTokChunk - 1) / kSharedTokChunk;
     switch (stage) {
         case 2:
             if (E > 512)
@@ -534,10 +564,15 @@ hipError_t launch_grouped_bits(const FwdArgs &a, int stage, hipStream_t st) {
         case 3:
         case 5: {
             const bool down = stage == 5;
-            switch (a.L.m[down ? 2 : 0].cpl) {
-                case 1: launch_grouped_mats<BITS, 1>(a, units, st, down); break;
-                case 2: launch_grouped_mats<BITS, 2>(a, units, st, down); break;
-                default: return hipErrorInvalidValue;
+            const int cpl = a.L.m[down ? 2 : 0].cpl;
+            if (cpl == 1) {
+                if (down) launch_grouped_mats<BITS, 1, true>(a, st);
+                else launch_grouped_mats<BITS, 1, false>(a, st);
+            } else if (BITS == 4 && cpl == 2) {  // 2-bit rows of 4096 or fewer codes take one chunk per lane
+                if (down) launch_grouped_mats<4, 2, true>(a, st);
+                else launch_grouped_mats<4, 2, false>(a, st);
+            } else {
+                return hipErrorInvalidValue;
             }
             break;
         }
