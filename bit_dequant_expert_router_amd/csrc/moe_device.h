@@ -401,6 +401,79 @@ __device__ __forceinline__ float qdot_prep(const RowPrep<BITS, CPL> &r, const Li
     return total;
 }
 
+// NR prepared rows against one vector's lane slice held in LDS (limbs
+// [7][n/8] words, then scales [n/64] and half-group sums [n/32]).  The limb
+// words are read one limb at a time, limb-major, so that only 8 of them are
+// live; each row keeps two integer Horner accumulators (limbs 6-4, 3-0).
+// Codes must be prepared (prep_codes) and s, o unpacked (prep_scales).
+template <int BITS, int CPL>
+__device__ __forceinline__ void prep_codes(uint4 (&c)[CPL]) {
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+            c[j] = make_uint4(c[j].x ^ 0x88888888u, c[j].y ^ 0x88888888u, c[j].z ^ 0x88888888u, c[j].w ^ 0x88888888u);
+    }
+}
+
+template <int BITS, int CPL, int NR>
+__device__ __forceinline__ void rows_dot_lds(const uint4 (&c)[NR][CPL], const float (&s)[NR][QSlice<BITS, CPL>::NGL],
+                                             const float (&o)[NR][QSlice<BITS, CPL>::NGL], const uint32_t *vec, int n,
+                                             int k0, float (&out)[NR]) {
+    using Q = QSlice<BITS, CPL>;
+    constexpr int ND = BITS == 4 ? CPL * 4 : CPL * 8;  // limb words per limb in the slice
+    constexpr int DPG = ND / Q::NGL;                    // ... per group
+    const uint32_t *lw = vec + k0 / 8;
+    const float *S = (const float *)(vec + kLimbs * (n / 8)) + k0 / 64;
+    const float *Xh = (const float *)(vec + kLimbs * (n / 8) + n / 64) + k0 / 32;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) out[r] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < Q::NGL; ++g) {
+        int hi[NR], lo[NR];
+#pragma unroll
+        for (int x = kLimbs - 1; x >= 0; --x) {
+            int L[DPG];
+#pragma unroll
+            for (int i = 0; i < DPG / 4; ++i) {
+                const int4 v = *(const int4 *)(lw + x * (n / 8) + g * DPG + 4 * i);
+                L[4 * i] = v.x; L[4 * i + 1] = v.y; L[4 * i + 2] = v.z; L[4 * i + 3] = v.w;
+            }
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                int acc = (x == kLimbs - 1 || x == 3) ? 0 : ((x >= 4 ? hi[r] : lo[r]) << 4);
+#pragma unroll
+                for (int i = 0; i < DPG; ++i) {
+                    const int di = g * DPG + i;  // limb word of the slice
+                    int op;
+                    if constexpr (BITS == 4) {
+                        const uint4 cj = c[r][di / 4];
+                        const uint32_t w[4] = {cj.x, cj.y, cj.z, cj.w};
+                        op = (int)w[di % 4];
+                    } else {
+                        const uint4 cj = c[r][di / 8];
+                        const uint32_t w[4] = {cj.x, cj.y, cj.z, cj.w};
+                        const uint32_t d = w[(di % 8) / 2];
+                        op = (int)((di & 1) ? ((d >> 2) & 0x33333333u) : (d & 0x33333333u));
+                    }
+                    acc = __builtin_amdgcn_sdot8(op, L[i], acc, false);
+                }
+                if (x >= 4) hi[r] = acc;
+                else lo[r] = acc;
+            }
+        }
+        float xs = 0.0f;
+#pragma unroll
+        for (int hh = 0; hh < Q::GL / 32; ++hh) xs += Xh[g * 2 + hh];
+        const float Sg = S[g];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const float f = fmaf((float)hi[r], 65536.0f, (float)lo[r]);
+            out[r] = fmaf(s[r][g] * Sg, f, out[r]);
+            out[r] = fmaf(o[r][g], xs, out[r]);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // several partial sums reduced at once over aligned groups of W lanes
 // (N <= W, both powers of two).  The first log2(N) exchange steps halve the

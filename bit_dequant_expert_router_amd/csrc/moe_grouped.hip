@@ -412,27 +412,38 @@ __global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, int chunks, i
             }
         }
     };
-    auto compute_step = [&](int s, const StepWeights<BITS, CPL, NM, RPW> &w, int np) {
+    auto compute_step = [&](int s, StepWeights<BITS, CPL, NM, RPW> &w, int np) {
         const int rs0 = rs_lo + (s * 4 + wave) * RPW;
-        RowPrep<BITS, CPL> rp[NM][RPW];
+        // row-major list of the step's rows: entry NM * i + m
+        uint4 (&c)[NV][CPL] = *reinterpret_cast<uint4 (*)[NV][CPL]>(&w.c[0][0][0]);
+        float sc[NV][Q::NGL], of[NV][Q::NGL];
 #pragma unroll
         for (int i = 0; i < RPW; ++i)
 #pragma unroll
-            for (int m = 0; m < NM; ++m) prep_row<BITS, CPL>(w.c[m][i], w.sb[m][i], rp[m][i]);
+            for (int m = 0; m < NM; ++m) {
+                prep_codes<BITS, CPL>(w.c[m][i]);
+#pragma unroll
+                for (int g = 0; g < Q::NGL; ++g) {
+                    sc[NM * i + m][g] = bf16_lo(w.sb[m][i][g]);
+                    of[NM * i + m][g] = fmaf(Q::kCodeOffset, sc[NM * i + m][g], bf16_hi(w.sb[m][i][g]));
+                }
+            }
+        uint4 cl[NV][CPL];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i)
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) cl[NM * i + m][j] = w.c[m][i][j];
+        (void)c;
         for (int v = 0; v < np; ++v) {
             const uint32_t *vec = s_vec + (size_t)v * words;
-            LimbSlice<BITS, CPL> hv;
-            load_limb_slice<BITS, CPL>(vec, (const float *)(vec + kLimbs * (n / 8)),
-                                       (const float *)(vec + kLimbs * (n / 8) + n / 64), n, k0, hv);
             float *out = out_base + (size_t)s_out[v] * out_len;
+            float part[NV];
+            rows_dot_lds<BITS, CPL, NV>(cl, sc, of, vec, n, k0, part);
             if constexpr (LPR != 0) {
                 // every row of the step at once; rows past the block's range
                 // are computed on stale registers and not written
-                float part[NV];
-#pragma unroll
-                for (int i = 0; i < RPW; ++i)
-#pragma unroll
-                    for (int m = 0; m < NM; ++m) part[NM * i + m] = qdot_prep<BITS, CPL>(rp[m][i], hv);
                 const float r = multi_reduce<NV, LPR>(part);
                 constexpr int DL = LPR / NV;  // lanes sharing one reduced entry
                 const int j = multi_index<NV, LPR>(lane);
@@ -450,11 +461,11 @@ __global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, int chunks, i
                     const int rs = rs0 + i;
                     if (rs < rs_hi) {
                         if constexpr (DOWN) {
-                            const float y = lane_group_sum(qdot_prep<BITS, CPL>(rp[0][i], hv), lpr);
+                            const float y = lane_group_sum(part[i], lpr);
                             if (lr == 0) out[rs * rpi + rsub] = y;
                         } else {
-                            const float g = lane_group_sum(qdot_prep<BITS, CPL>(rp[0][i], hv), lpr);
-                            const float up = lane_group_sum(qdot_prep<BITS, CPL>(rp[1][i], hv), lpr);
+                            const float g = lane_group_sum(part[2 * i], lpr);
+                            const float up = lane_group_sum(part[2 * i + 1], lpr);
                             if (lr == 0) out[rs * rpi + rsub] = g * up * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
                         }
                     }
