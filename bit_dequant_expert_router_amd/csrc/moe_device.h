@@ -430,8 +430,7 @@ __device__ __forceinline__ void rows_dot_lds(const uint4 (&c)[NR][CPL], const fl
 #pragma unroll
     for (int g = 0; g < Q::NGL; ++g) {
         int hi[NR], lo[NR];
-#pragma unroll
-        for (int x = kLimbs - 1; x >= 0; --x) {
+        auto limb = [&](int x, int (&acc)[NR], bool first) {
             int L[DPG];
 #pragma unroll
             for (int i = 0; i < DPG / 4; ++i) {
@@ -440,7 +439,7 @@ __device__ __forceinline__ void rows_dot_lds(const uint4 (&c)[NR][CPL], const fl
             }
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
-                int acc = (x == kLimbs - 1 || x == 3) ? 0 : ((x >= 4 ? hi[r] : lo[r]) << 4);
+                int a = first ? 0 : (acc[r] << 4);
 #pragma unroll
                 for (int i = 0; i < DPG; ++i) {
                     const int di = g * DPG + i;  // limb word of the slice
@@ -455,12 +454,19 @@ __device__ __forceinline__ void rows_dot_lds(const uint4 (&c)[NR][CPL], const fl
                         const uint32_t d = w[(di % 8) / 2];
                         op = (int)((di & 1) ? ((d >> 2) & 0x33333333u) : (d & 0x33333333u));
                     }
-                    acc = __builtin_amdgcn_sdot8(op, L[i], acc, false);
+                    a = __builtin_amdgcn_sdot8(op, L[i], a, false);
                 }
-                if (x >= 4) hi[r] = acc;
-                else lo[r] = acc;
+                acc[r] = a;
             }
-        }
+        };
+        // limbs one at a time (the loops are kept rolled so that the limb
+        // words of only one limb are live)
+        limb(kLimbs - 1, hi, true);
+#pragma unroll 1
+        for (int x = kLimbs - 2; x >= 4; --x) limb(x, hi, false);
+        limb(3, lo, true);
+#pragma unroll 1
+        for (int x = 2; x >= 0; --x) limb(x, lo, false);
         float xs = 0.0f;
 #pragma unroll
         for (int hh = 0; hh < Q::GL / 32; ++hh) xs += Xh[g * 2 + hh];

@@ -525,12 +525,14 @@ __global__ __launch_bounds__(256) void k_combine(FwdArgs a) {
 // weights stay within ~80 VGPRs
 constexpr int stream_rpw(int cpl) { return cpl == 1 ? 4 : 2; }
 constexpr int kStreamStepsPerWave = 8;  // row-steps a wave streams per block
-constexpr int kStreamLdsBytes = 48 * 1024;
 constexpr int kStreamMaxVectors = 16;
 
-// vectors staged per pass: as many as fit the LDS budget, at most 16
-inline int stream_vectors(int n) {
-    const int v = kStreamLdsBytes / (stage_words(n) * 4);
+// vectors staged per pass: as many as fit the block's LDS budget (48 KiB for
+// gate/up: three blocks per CU; 40 KiB for down, whose registers allow four),
+// at most 16
+inline int stream_vectors(int n, bool down) {
+    const int budget = (down ? 40 : 48) * 1024;
+    const int v = budget / (stage_words(n) * 4);
     return v < kStreamMaxVectors ? v : kStreamMaxVectors;
 }
 
@@ -542,7 +544,7 @@ void launch_stream(const FwdArgs &a, hipStream_t st) {
     constexpr int rpw = stream_rpw(CPL);
     const int chunks = (nrs + 4 * rpw * kStreamStepsPerWave - 1) / (4 * rpw * kStreamStepsPerWave);
     const int n = DOWN ? a.s.F : a.s.H;
-    const int tp = stream_vectors(n);
+    const int tp = stream_vectors(n, DOWN);
     // shared-expert units of tp tokens: one pass each
     const int units = touched_bound(a.s, a.T) + (a.T + tp - 1) / tp;
     const size_t lds = (size_t)tp * stage_words(n) * 4;
