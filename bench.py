@@ -53,7 +53,7 @@ def parse_args():
     p.add_argument("--steps", type=int, default=2048)
     p.add_argument("--warmup", type=int, default=64)
     p.add_argument("--workload", default="layer4", choices=["layer4", "layer2", "batch32", "tiny"])
-    p.add_argument("--layers", type=int, default=8, help="resident layers the steps rotate over")
+    p.add_argument("--layers", type=int, default=32, help="resident layers the steps rotate over")
     p.add_argument("--pool", type=int, default=1024, help="distinct tokens the steps rotate over")
     p.add_argument("--mode", default="graph", choices=["graph", "api"],
                    help="graph: the timed steps are one captured HIP graph; api: one ABI call per step")

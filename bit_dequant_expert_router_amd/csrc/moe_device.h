@@ -401,8 +401,7 @@ __device__ __forceinline__ float qdot_prep(const RowPrep<BITS, CPL> &r, const Li
     return total;
 }
 
-// NR prepared rows against one vector's lane slice held in LDS (limbs
-// [7][n/8] words, then scales [n/64] and half-group sums [n/32]).  The limb
+// NR prepared rows against one vector's lane slice held in LDS.  The limb
 // words are read one limb at a time, limb-major, so that only 8 of them are
 // live; each row keeps two integer Horner accumulators (limbs 6-4, 3-0).
 // Codes must be prepared (prep_codes) and s, o unpacked (prep_scales).
@@ -415,16 +414,17 @@ __device__ __forceinline__ void prep_codes(uint4 (&c)[CPL]) {
     }
 }
 
+// limbs: [7][n/8] words; S: [n/64] group scales; Xh: [n/32] half-group sums
 template <int BITS, int CPL, int NR>
 __device__ __forceinline__ void rows_dot_lds(const uint4 (&c)[NR][CPL], const float (&s)[NR][QSlice<BITS, CPL>::NGL],
-                                             const float (&o)[NR][QSlice<BITS, CPL>::NGL], const uint32_t *vec, int n,
-                                             int k0, float (&out)[NR]) {
+                                             const float (&o)[NR][QSlice<BITS, CPL>::NGL], const uint32_t *limbs,
+                                             const float *S_all, const float *Xh_all, int n, int k0, float (&out)[NR]) {
     using Q = QSlice<BITS, CPL>;
     constexpr int ND = BITS == 4 ? CPL * 4 : CPL * 8;  // limb words per limb in the slice
     constexpr int DPG = ND / Q::NGL;                    // ... per group
-    const uint32_t *lw = vec + k0 / 8;
-    const float *S = (const float *)(vec + kLimbs * (n / 8)) + k0 / 64;
-    const float *Xh = (const float *)(vec + kLimbs * (n / 8) + n / 64) + k0 / 32;
+    const uint32_t *lw = limbs + k0 / 8;
+    const float *S = S_all + k0 / 64;
+    const float *Xh = Xh_all + k0 / 32;
 #pragma unroll
     for (int r = 0; r < NR; ++r) out[r] = 0.0f;
 #pragma unroll

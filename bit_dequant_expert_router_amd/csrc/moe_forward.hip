@@ -116,7 +116,9 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // k_gateup: RPW row-steps per wave over the (K+1) x F gate/up row pairs
 // ---------------------------------------------------------------------------
-template <int BITS, int CPL, int RPW, int EPL>
+// LPR: lanes per row when the step's partial sums are reduced together (64);
+// 0: one reduction per row
+template <int BITS, int CPL, int RPW, int EPL, int LPR>
 __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
     using Q = QSlice<BITS, CPL>;
     const int t = blockIdx.y;
@@ -212,36 +214,49 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
     if (!active) return;
     if (!wave_shared_only) issue_loads();
 
-    // the lane's limb slice of h, from LDS
+    // codes prepared once, then every row against the lane's limb slice of h
+    // in LDS, limb-major
+    constexpr int NV = 2 * RPW;  // entries 2i (gate) and 2i + 1 (up) of row-step i
     const int k0 = lr * Q::NV;
-    LimbSlice<BITS, CPL> hv;
-#pragma unroll
-    for (int x = 0; x < kLimbs; ++x)
-#pragma unroll
-        for (int i = 0; i < Q::NL / 4; ++i) {
-            const int4 v = *(const int4 *)(s_hl + x * (H / 8) + k0 / 8 + 4 * i);
-            hv.L[x][4 * i + 0] = v.x; hv.L[x][4 * i + 1] = v.y;
-            hv.L[x][4 * i + 2] = v.z; hv.L[x][4 * i + 3] = v.w;
-        }
-#pragma unroll
-    for (int g = 0; g < Q::NGL; ++g) {
-        hv.S[g] = s_hs[k0 / 64 + g];
-        float xs = 0.0f;
-#pragma unroll
-        for (int hh = 0; hh < Q::GL / 32; ++hh) xs += s_hx[(k0 + g * 64) / 32 + hh];
-        hv.X[g] = xs;
-    }
-
-    float *act = a.ws.act + (size_t)t * (K + 1) * F;
+    uint4 cl[NV][CPL];
+    float sc[NV][Q::NGL], of[NV][Q::NGL];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-        const int rs = rs0 + i;
-        if (rs < nrs) {
-            float g = qdot<BITS, CPL>(gc[i], gsb[i], hv);
-            float u = qdot<BITS, CPL>(uc[i], usb[i], hv);
-            g = lane_group_sum(g, lpr);
-            u = lane_group_sum(u, lpr);
-            if (lr == 0) act[rs * rpi + rsub] = g * sigmoidf_(g) * u;
+        prep_codes<BITS, CPL>(gc[i]);
+        prep_codes<BITS, CPL>(uc[i]);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            cl[2 * i][j] = gc[i][j];
+            cl[2 * i + 1][j] = uc[i][j];
+        }
+#pragma unroll
+        for (int g = 0; g < Q::NGL; ++g) {
+            sc[2 * i][g] = bf16_lo(gsb[i][g]);
+            of[2 * i][g] = fmaf(Q::kCodeOffset, sc[2 * i][g], bf16_hi(gsb[i][g]));
+            sc[2 * i + 1][g] = bf16_lo(usb[i][g]);
+            of[2 * i + 1][g] = fmaf(Q::kCodeOffset, sc[2 * i + 1][g], bf16_hi(usb[i][g]));
+        }
+    }
+    float part[NV];
+    rows_dot_lds<BITS, CPL, NV>(cl, sc, of, s_hl, s_hs, s_hx, H, k0, part);
+
+    float *act = a.ws.act + (size_t)t * (K + 1) * F;
+    if constexpr (LPR != 0) {
+        // rows past the end are computed on unloaded registers and not written
+        const float r = multi_reduce<NV, LPR>(part);
+        constexpr int DL = LPR / NV;  // lanes sharing one reduced entry
+        const int rs = rs0 + multi_index<NV, LPR>(lane) / 2;
+        const float up = xchg<DL>(r);  // the up sum sits across the last halving bit
+        if ((lane & (2 * DL - 1)) == 0 && rs < nrs) act[rs * rpi + rsub] = r * sigmoidf_(r) * up;
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int rs = rs0 + i;
+            if (rs < nrs) {
+                const float g = lane_group_sum(part[2 * i], lpr);
+                const float u = lane_group_sum(part[2 * i + 1], lpr);
+                if (lr == 0) act[rs * rpi + rsub] = g * sigmoidf_(g) * u;
+            }
         }
     }
 }
@@ -370,7 +385,7 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
     }
 }
 
-constexpr int kRpwGateUp = 3;
+constexpr int kRpwGateUp = 2;
 constexpr int kRpwDown = 2;
 
 template <int BITS>
@@ -398,11 +413,14 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
         const int blocks = (nrs + 4 * kRpwGateUp - 1) / (4 * kRpwGateUp);
         dim3 grid(blocks, T);
         const bool wide = E > 512;
-        switch (G.cpl * 2 + (wide ? 1 : 0)) {
-            case 2: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8>), grid, dim3(256), 0, st, a); break;
-            case 3: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16>), grid, dim3(256), 0, st, a); break;
-            case 4: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 8>), grid, dim3(256), 0, st, a); break;
-            case 5: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 16>), grid, dim3(256), 0, st, a); break;
+        const bool full = G.lpr == 64;  // rows of 64 lanes: one butterfly for the whole step
+        switch (G.cpl * 4 + (wide ? 2 : 0) + (full ? 1 : 0)) {
+            case 4: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 0>), grid, dim3(256), 0, st, a); break;
+            case 5: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 64>), grid, dim3(256), 0, st, a); break;
+            case 6: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 0>), grid, dim3(256), 0, st, a); break;
+            case 7: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 64>), grid, dim3(256), 0, st, a); break;
+            case 9: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 8, 64>), grid, dim3(256), 0, st, a); break;
+            case 11: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 16, 64>), grid, dim3(256), 0, st, a); break;
             default: return hipErrorInvalidValue;
         }
     } else if (stage == 2) {  // down + combine + residual

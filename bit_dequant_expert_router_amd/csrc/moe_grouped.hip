@@ -440,7 +440,8 @@ __global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, int chunks, i
             const uint32_t *vec = s_vec + (size_t)v * words;
             float *out = out_base + (size_t)s_out[v] * out_len;
             float part[NV];
-            rows_dot_lds<BITS, CPL, NV>(cl, sc, of, vec, n, k0, part);
+            rows_dot_lds<BITS, CPL, NV>(cl, sc, of, vec, (const float *)(vec + kLimbs * (n / 8)),
+                                        (const float *)(vec + kLimbs * (n / 8) + n / 64), n, k0, part);
             if constexpr (LPR != 0) {
                 // every row of the step at once; rows past the block's range
                 // are computed on stale registers and not written
