@@ -196,18 +196,27 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
     // weight loads: shared-only waves issue theirs before the routing is known
     uint4 gc[RPW][CPL], uc[RPW][CPL];
     uint32_t gsb[RPW][Q::NGL], usb[RPW][Q::NGL];
+    // every row's loads unconditional (rows past the end re-read the last
+    // row), so that they are all in flight before the first wait
+    // (addresses first, then every load back to back)
     auto issue_loads = [&]() {
+        const uint8_t *exr[RPW];
+        int jr[RPW];
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
-            const int rs = rs0 + i;
-            if (rs < nrs) {
-                const int p = rs * rpi + rsub;
-                const int s = p / F, j = p % F;
-                const uint8_t *ex = (s < K) ? a.experts + (size_t)s_sel[s] * a.L.bytes : a.shared;
-                load_row<BITS, CPL>(ex, G, j, lr, gc[i], gsb[i]);
-                load_row<BITS, CPL>(ex, U, j, lr, uc[i], usb[i]);
-            }
+            const int rs = rs0 + i < nrs ? rs0 + i : nrs - 1;
+            const int p = rs * rpi + rsub;
+            const int s = p / F;
+            jr[i] = p - s * F;
+            exr[i] = (s < K) ? a.experts + (size_t)s_sel[s < K ? s : 0] * a.L.bytes : a.shared;
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            load_row<BITS, CPL>(exr[i], G, jr[i], lr, gc[i], gsb[i]);
+            load_row<BITS, CPL>(exr[i], U, jr[i], lr, uc[i], usb[i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
     if (active && wave_shared_only) issue_loads();
     __syncthreads();
@@ -273,27 +282,41 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
 constexpr int kDownBatch = 5;
 constexpr int kDownStageValues = 5120;  // activations staged per batch (batch * F <= this)
 
-template <int BITS, int CPL, int RPW>
+// LPR: lanes per row for one butterfly over the wave's RPW rows (16, 32, 64);
+// 0: one reduction per row
+// ONE: all K+1 slots in a single batch (straight-line code: no loop-header
+// wait holds back the first loads)
+template <int BITS, int CPL, int RPW, int LPR, bool ONE>
 __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
     using Q = QSlice<BITS, CPL>;
     const int t = blockIdx.y;
     const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const QMat &Dm = a.L.m[2];
-    const int lpr = Dm.lpr, rpi = 64 / lpr;
+    const int lpr = LPR ? LPR : Dm.lpr, rpi = 64 / lpr;
     const int lr = lane % lpr, rsub = lane / lpr;
     const int nrs = H / rpi;
     const int rs0 = (blockIdx.x * 4 + wave) * RPW;
     const bool active = rs0 < nrs;
     const int k0 = lr * Q::NV;
 
+    // the residual of the rows this lane may write, fetched now
+    float xres[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int rs = rs0 + i < nrs ? rs0 + i : nrs - 1;
+        xres[i] = a.x[(size_t)t * H + rs * rpi + rsub];
+    }
+
     extern __shared__ __align__(16) unsigned char smem[];
     float *s_act = (float *)smem;              // [batch][F]
     float *s_half = s_act + (size_t)batch * F;  // [batch][F/32]
 
-    // lane s (s <= K) holds slot s: expert index and combine coefficient
-    const int my_e = (lane < K) ? a.ws.sel[t * K + lane] : E;
-    const float my_c = (lane <= K) ? a.ws.coef[t * (K + 1) + lane] : 0.0f;
+    // lane s (s <= K) holds slot s: expert index (s < K) and combine
+    // coefficient; only those lanes are ever read (unconditional loads, lanes
+    // past the end read a valid entry)
+    const int my_e = a.ws.sel[t * K + (lane < K ? lane : K - 1)];
+    const float my_c = a.ws.coef[t * (K + 1) + (lane <= K ? lane : K)];
 
     float acc[RPW];
 #pragma unroll
@@ -301,35 +324,35 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
 
     // slot positions run shared, 0, 1, ..., K-1: the shared expert's loads need no routing
     constexpr int kStageMax = kDownStageValues / 1024;  // float4 pieces per thread and batch
-    for (int b0 = 0; b0 <= K; b0 += batch) {
+    auto run_batch = [&](int b0) {
         const int nb = (K + 1 - b0) < batch ? (K + 1 - b0) : batch;
         // this batch's activations first: the staging then waits on them only
         // (loads complete in order), while the weight loads stay in flight
+        // every load below is unconditional (indices past the end are
+        // clamped to valid ones and their results unused), so that all of
+        // them are in flight before the first wait
         float4 stv[kStageMax];
 #pragma unroll
         for (int r = 0; r < kStageMax; ++r) {
             const int v0 = threadIdx.x * 4 + 1024 * r;
-            stv[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (v0 < nb * F) {
-                const int si = v0 / F, j = v0 % F;
-                const int s = (b0 + si == 0) ? K : b0 + si - 1;
-                stv[r] = *(const float4 *)(a.ws.act + ((size_t)t * (K + 1) + s) * F + j);
-            }
+            const int vc = v0 < nb * F ? v0 : 0;
+            const int si = vc / F, j = vc % F;
+            const int s = (b0 + si == 0) ? K : b0 + si - 1;
+            stv[r] = *(const float4 *)(a.ws.act + ((size_t)t * (K + 1) + s) * F + j);
         }
         // weights of up to kDownBatch slots of this batch, all in flight together
         uint4 wc[kDownBatch][RPW][CPL];
         uint32_t wsb[kDownBatch][RPW][Q::NGL];
 #pragma unroll
         for (int si = 0; si < kDownBatch; ++si) {
-            if (si < nb && active) {
-                const int s = (b0 + si == 0) ? K : b0 + si - 1;
-                const int e = (s == K) ? E : lane_bcast(my_e, s);
-                const uint8_t *ex = (e < E) ? a.experts + (size_t)e * a.L.bytes : a.shared;
+            const int sc = si < nb ? si : nb - 1;
+            const int s = (b0 + sc == 0) ? K : b0 + sc - 1;
+            const int e = (s == K) ? E : lane_bcast(my_e, s);
+            const uint8_t *ex = (e < E) ? a.experts + (size_t)e * a.L.bytes : a.shared;
 #pragma unroll
-                for (int i = 0; i < RPW; ++i) {
-                    const int rs = rs0 + i;
-                    if (rs < nrs) load_row<BITS, CPL>(ex, Dm, rs * rpi + rsub, lr, wc[si][i], wsb[si][i]);
-                }
+            for (int i = 0; i < RPW; ++i) {
+                const int rs = rs0 + i < nrs ? rs0 + i : nrs - 1;
+                load_row<BITS, CPL>(ex, Dm, rs * rpi + rsub, lr, wc[si][i], wsb[si][i]);
             }
         }
         // stage this batch's activations and half-group sums
@@ -372,15 +395,27 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
                 }
             }
         }
+    };
+    if constexpr (ONE) {
+        run_batch(0);
+    } else {
+        for (int b0 = 0; b0 <= K; b0 += batch) run_batch(b0);
     }
     if (!active) return;
+    if constexpr (LPR != 0 && RPW <= LPR) {
+        const float v = multi_reduce<RPW, LPR>(acc);
+        const int i = multi_index<RPW, LPR>(lane);
+        constexpr int DL = LPR / RPW;  // lanes sharing one reduced row
+        float xr = xres[0];
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int rs = rs0 + i;
-        const float v = lane_group_sum(acc[i], lpr);
-        if (rs < nrs && lr == 0) {
-            const size_t o = (size_t)t * H + rs * rpi + rsub;
-            a.y[o] = a.x[o] + v;
+        for (int q = 1; q < RPW; ++q) xr = (i == q) ? xres[q] : xr;
+        if ((lane & (DL - 1)) == 0 && rs0 + i < nrs) a.y[(size_t)t * H + (rs0 + i) * rpi + rsub] = xr + v;
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int rs = rs0 + i;
+            const float v = lane_group_sum(acc[i], lpr);
+            if (rs < nrs && lr == 0) a.y[(size_t)t * H + rs * rpi + rsub] = xres[i] + v;
         }
     }
 }
@@ -435,10 +470,24 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
         if (batch > K + 1) batch = K + 1;
         if (batch < 1) batch = 1;
         const size_t lds = per_slot * batch;
-        switch (Dm.cpl) {
-            case 1: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown>), grid, dim3(256), lds, st, a, batch); break;
-            case 2: hipLaunchKernelGGL((k_down<BITS, 2, kRpwDown>), grid, dim3(256), lds, st, a, batch); break;
-            default: return hipErrorInvalidValue;
+        const bool one = K + 1 <= batch;
+        if (Dm.cpl == 2) {
+            if (one) hipLaunchKernelGGL((k_down<BITS, 2, kRpwDown, 64, true>), grid, dim3(256), lds, st, a, batch);
+            else hipLaunchKernelGGL((k_down<BITS, 2, kRpwDown, 64, false>), grid, dim3(256), lds, st, a, batch);
+        } else if (Dm.cpl == 1) {
+            const int key = (Dm.lpr == 64 ? 0 : Dm.lpr == 32 ? 1 : Dm.lpr == 16 ? 2 : 3) * 2 + (one ? 1 : 0);
+            switch (key) {
+                case 0: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 64, false>), grid, dim3(256), lds, st, a, batch); break;
+                case 1: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 64, true>), grid, dim3(256), lds, st, a, batch); break;
+                case 2: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 32, false>), grid, dim3(256), lds, st, a, batch); break;
+                case 3: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 32, true>), grid, dim3(256), lds, st, a, batch); break;
+                case 4: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 16, false>), grid, dim3(256), lds, st, a, batch); break;
+                case 5: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 16, true>), grid, dim3(256), lds, st, a, batch); break;
+                case 6: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 0, false>), grid, dim3(256), lds, st, a, batch); break;
+                default: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 0, true>), grid, dim3(256), lds, st, a, batch); break;
+            }
+        } else {
+            return hipErrorInvalidValue;
         }
     } else {
         return hipErrorInvalidValue;

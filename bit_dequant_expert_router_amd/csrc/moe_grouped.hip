@@ -402,14 +402,15 @@ __global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, int chunks, i
     const int out_len = DOWN ? H : F;
     float *out_base = DOWN ? a.ws.ys : a.ws.act;
 
+    // unconditional loads (rows past the range re-read its last row, unused)
+    // so that no wait separates them
     auto load_step = [&](int s, StepWeights<BITS, CPL, NM, RPW> &w) {
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
-            const int rs = rs_lo + (s * 4 + wave) * RPW + i;
-            if (rs < rs_hi) {
-                load_row<BITS, CPL>(ex, M0, rs * rpi + rsub, lr, w.c[0][i], w.sb[0][i]);
-                if constexpr (NM == 2) load_row<BITS, CPL>(ex, M1, rs * rpi + rsub, lr, w.c[1][i], w.sb[1][i]);
-            }
+            const int r0 = rs_lo + (s * 4 + wave) * RPW + i;
+            const int rs = r0 < rs_hi ? r0 : rs_hi - 1;
+            load_row<BITS, CPL>(ex, M0, rs * rpi + rsub, lr, w.c[0][i], w.sb[0][i]);
+            if constexpr (NM == 2) load_row<BITS, CPL>(ex, M1, rs * rpi + rsub, lr, w.c[1][i], w.sb[1][i]);
         }
     };
     auto compute_step = [&](int s, StepWeights<BITS, CPL, NM, RPW> &w, int np) {
@@ -496,13 +497,15 @@ __global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, int chunks, i
             for (int i = threadIdx.x; i < n / 32; i += 256) dst[kLimbs * (n / 8) + n / 64 + i] = __float_as_uint(hx[i]);
         }
         __syncthreads();
+        // the prefetches are unconditional (past the last step they re-read
+        // it, from cache): a load issued on one path only would make the
+        // waits after the join count for the path without it, i.e. wait for
+        // the prefetch itself
         for (int s = 0; s < nsteps; s += 2) {
-            if (s + 1 < nsteps) load_step(s + 1, wb);
+            load_step(s + 1 < nsteps ? s + 1 : nsteps - 1, wb);
             compute_step(s, wa, np);
-            if (s + 1 < nsteps) {
-                if (s + 2 < nsteps) load_step(s + 2, wa);
-                compute_step(s + 1, wb, np);
-            }
+            load_step(s + 2 < nsteps ? s + 2 : nsteps - 1, wa);
+            if (s + 1 < nsteps) compute_step(s + 1, wb, np);
         }
     }
 }
