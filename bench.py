@@ -33,7 +33,12 @@ HBM_PEAK_BPS = 8.0e12  # MI355X HBM3E peak
 # profiles/); an entry holds only while the kernel sources hash to the prefix it
 # was measured on.  FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0, the ratios
 # of bytes moved to counts reported for a 256 MiB copy.
-KERNEL_TRAFFIC = {}
+KERNEL_TRAFFIC = {
+    ("layer4", "k_gateup"): {"source_sha256_prefix": "06dafaaf914207ca", "fetch_kib": 11649.2, "write_kib": 20.1,
+                             "fetch_scale": 2.0, "write_scale": 1.0},
+    ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "1bb7768796cf9143", "fetch_kib": 624740.9,
+                                      "write_kib": 1439.9, "fetch_scale": 2.0, "write_scale": 1.0},
+}
 
 
 def kernel_source_hash(grouped):
