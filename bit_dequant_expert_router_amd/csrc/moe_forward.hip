@@ -114,6 +114,119 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// k_router_split (H = 2048 or 4096): the 4 waves of a block split H into
+// quarters of the block's RB router rows (one row per block measures fastest:
+// 513 blocks spread the 4 MiB over the whole chip), so a wave reads 1/4 of x
+// and gamma instead of all of it.  The dot products use x * gamma; the factor
+// 1 / rms(x) is applied to the block's sum (the norm's two passes are the
+// waves' sums of squares, then the scaling).  The first H / 256 blocks also
+// write the limb form of h for k_gateup.
+// ---------------------------------------------------------------------------
+constexpr int kRouterSplitRows = 1;
+
+template <int CPL_R>
+__global__ __launch_bounds__(256) void k_router_split(FwdArgs a) {
+    constexpr int RB = kRouterSplitRows;
+    const int t = blockIdx.y;
+    const int H = a.s.H, E = a.s.E;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const float *x = a.x + (size_t)t * H;
+    const int r0 = blockIdx.x * RB;
+    // lane's chunks of 8 entries: wave quarter + lane + 64 j
+    const int kq = wave * (H / 4);
+    uint4 wv[RB][CPL_R];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        const int row = r0 + r <= E ? r0 + r : E;  // rows past the end re-read the gate row, unused
+        const uint16_t *src = (row < E) ? a.router + (size_t)row * H : a.sgate;
+#pragma unroll
+        for (int j = 0; j < CPL_R; ++j) wv[r][j] = ld_stream16(src + kq + 8 * (lane + 64 * j));
+    }
+    float xv[CPL_R * 8];
+    uint4 gv[CPL_R];
+#pragma unroll
+    for (int j = 0; j < CPL_R; ++j) {
+        const int k0 = kq + 8 * (lane + 64 * j);
+        const float4 x0 = *(const float4 *)(x + k0);
+        const float4 x1 = *(const float4 *)(x + k0 + 4);
+        xv[8 * j + 0] = x0.x; xv[8 * j + 1] = x0.y; xv[8 * j + 2] = x0.z; xv[8 * j + 3] = x0.w;
+        xv[8 * j + 4] = x1.x; xv[8 * j + 5] = x1.y; xv[8 * j + 6] = x1.z; xv[8 * j + 7] = x1.w;
+        gv[j] = *(const uint4 *)(a.gamma + k0);
+    }
+    // this block's share of the limb encoding: entry k of h (x and gamma fetched now)
+    const int ke = blockIdx.x * 256 + threadIdx.x;
+    const bool enc = blockIdx.x * 256 < H;
+    const float xe = x[ke < H ? ke : 0];
+    const float ge = __uint_as_float((uint32_t)a.gamma[ke < H ? ke : 0] << 16);
+
+    float ss = 0.0f;
+    float xg[CPL_R * 8];
+#pragma unroll
+    for (int j = 0; j < CPL_R; ++j) {
+        const uint32_t g[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            xg[8 * j + 2 * q] = xv[8 * j + 2 * q] * bf16_lo(g[q]);
+            xg[8 * j + 2 * q + 1] = xv[8 * j + 2 * q + 1] * bf16_hi(g[q]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < CPL_R * 8; ++i) ss = fmaf(xv[i], xv[i], ss);
+    float acc[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        float v = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL_R; ++j) {
+            const uint32_t w[4] = {wv[r][j].x, wv[r][j].y, wv[r][j].z, wv[r][j].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v = fmaf(bf16_lo(w[q]), xg[8 * j + 2 * q], v);
+                v = fmaf(bf16_hi(w[q]), xg[8 * j + 2 * q + 1], v);
+            }
+        }
+        acc[r] = v;
+    }
+    const float red = multi_reduce<RB, 64>(acc);
+    const int jr = multi_index<RB, 64>(lane);
+    ss = lane_sum<64>(ss);
+    __shared__ float s_part[4][RB];
+    __shared__ float s_ss[4];
+    if ((lane & (64 / RB - 1)) == 0) s_part[wave][jr] = red;
+    if (lane == 0) s_ss[wave] = ss;
+    __syncthreads();
+    const float inv = 1.0f / sqrtf(((s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3])) / (float)H + a.s.eps);
+    if (threadIdx.x < RB) {
+        const int row = r0 + threadIdx.x;
+        const float z = (((s_part[0][threadIdx.x] + s_part[1][threadIdx.x]) + s_part[2][threadIdx.x]) +
+                         s_part[3][threadIdx.x]) * inv;
+        if (row < E)
+            a.ws.z[(size_t)t * E + row] = z;
+        else if (row == E)
+            a.ws.gs[t] = z;
+    }
+    if (enc) {  // one wave = one group of 64
+        const float h = (ke < H) ? xe * inv * ge : 0.0f;
+        const float m = lane_max<64>(fabsf(h));
+        int l[kLimbs];
+        limb_split(limb_value(h, m), l);
+        const float half = lane_sum<32>(h);
+        uint32_t packed[kLimbs];
+#pragma unroll
+        for (int xl = 0; xl < kLimbs; ++xl) packed[xl] = lane_or8((uint32_t)(l[xl] & 15) << (4 * (lane & 7)));
+        if (ke < H) {
+            uint32_t *hl = (uint32_t *)a.ws.hl + (size_t)t * kLimbs * (H / 8);
+            if ((lane & 7) == 0) {
+#pragma unroll
+                for (int xl = 0; xl < kLimbs; ++xl) hl[(size_t)xl * (H / 8) + ke / 8] = packed[xl];
+            }
+            if (lane == 0) a.ws.hs[(size_t)t * (H / 64) + ke / 64] = limb_scale(m);
+            if ((lane & 31) == 0) a.ws.hx[(size_t)t * (H / 32) + ke / 32] = half;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // k_gateup: RPW row-steps per wave over the (K+1) x F gate/up row pairs
 // ---------------------------------------------------------------------------
 // LPR: lanes per row when the step's partial sums are reduced together (64);
@@ -426,7 +539,14 @@ constexpr int kRpwDown = 2;
 template <int BITS>
 hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
     const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K, T = a.T;
-    if (stage == 0) {  // RMSNorm + router + limbs of h
+    if (stage == 0 && (H == 2048 || H == 4096)) {  // RMSNorm + router + limbs of h, H split over 4 waves
+        const int rows = (E + 1 + kRouterSplitRows - 1) / kRouterSplitRows;
+        const int blocks = rows > H / 256 ? rows : H / 256;
+        if (H == 4096)
+            hipLaunchKernelGGL(k_router_split<2>, dim3(blocks, T), dim3(256), 0, st, a);
+        else
+            hipLaunchKernelGGL(k_router_split<1>, dim3(blocks, T), dim3(256), 0, st, a);
+    } else if (stage == 0) {  // RMSNorm + router + limbs of h
         const int nch = H / 8, lpr = nch < 64 ? nch : 64, cplr = nch / lpr, rpi = 64 / lpr;
         const int nrs = (E + 1 + rpi - 1) / rpi;
         int blocks = (nrs + kRouterWaves - 1) / kRouterWaves;
