@@ -96,14 +96,29 @@ def test_inplace_determinism_and_optional_outputs(moe, n_tokens):
         check_token(a[t], ia[t], wa[t], oracle.layer_all(dims, x[t], dense, experts), dims.top_k, f"token {t}")
 
 
-@pytest.mark.parametrize("T", [3, 6])
-def test_stages_equal_full_forward(moe, T):
+@pytest.mark.parametrize("name,T", [("tiny", 3), ("tiny", 6), ("layer4", 1)])
+def test_stages_equal_full_forward(moe, name, T):
     """The stages enqueued one by one give exactly the one-call result, on the
-    per-token path (3 tokens, 3 stages) and the grouped path (6 tokens, 7 stages)."""
-    dims = syn.WORKLOADS["tiny"].dims
+    per-token path (3 tokens, 3 stages), the grouped path (6 tokens, 7 stages)
+    and the full-size single-token layer."""
+    dims = syn.WORKLOADS[name].dims
+    if name != "tiny":
+        from bit_dequant_expert_router_amd.weights import layer_generated
+        lw = layer_generated(dims, dense_layer(0, 3, dims), 0, 3)
+        x = syn.tokens(4, T, dims.hidden)
+        full, fidx, fw = run_layer(dims, lw, x)
+        again, _, _ = run_layer(dims, lw, x)
+        assert np.array_equal(full, again)
+        _check_stages(moe, dims, lw, x, full, fidx, fw)
+        return
     dense, experts, lw = _canonical_layer(dims)
     x = syn.tokens(4, T, dims.hidden)
     full, fidx, fw = run_layer(dims, lw, x)
+    _check_stages(moe, dims, lw, x, full, fidx, fw)
+
+
+def _check_stages(moe, dims, lw, x, full, fidx, fw):
+    T = x.shape[0]
     xt = torch.from_numpy(x).cuda()
     yt = torch.empty_like(xt)
     ridx = torch.empty((T, dims.top_k), dtype=torch.int32, device="cuda")
