@@ -10,11 +10,10 @@
 //
 //   k_norm_batch, k_router_mfma (moe_batch_router.hip) RMSNorm, limb and bf16
 //                   forms of h, router logits on the matrix cores
-//   k_route_tokens  one block per token: softmax/top-K/renormalise; the last
-//                   block to finish builds a histogram of assignments per
-//                   expert, an exclusive scan, a stable scatter (token order
-//                   kept inside each expert) and the compact list of touched
-//                   experts
+//   k_route_tokens  one wave per token: softmax/top-K/renormalise
+//   k_group         one block: histogram of assignments per expert, exclusive
+//                   scan, stable scatter (token order kept inside each expert)
+//                   and the compact list of touched experts
 //   k_grouped_gateup  one block per (touched expert, row chunk): gate+up rows read
 //                   once, applied to every token of the expert, SwiGLU; the shared
 //                   expert gets its own blocks over all tokens
@@ -97,8 +96,10 @@ __device__ __forceinline__ void token_logits(const FwdArgs &a, int t, float (&zv
 // grouping of all T*K assignments by expert, by one block of 256 threads:
 // histogram, exclusive scans, the compact list of touched experts, and a
 // stable scatter (token order kept inside each expert)
+constexpr int kGroupThreads = 1024;
+
 __device__ void group_assignments(const FwdArgs &a) {
-    constexpr int NT = 256;
+    constexpr int NT = kGroupThreads;
     const int T = a.T, E = a.s.E, K = a.s.K;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int TK = T * K;
@@ -175,40 +176,32 @@ __device__ void group_assignments(const FwdArgs &a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_route_tokens: one block per token; wave 0 sums the partial logits and
-// routes (softmax -> top-K -> renormalise).  The block that finishes last
-// (a counter in the workspace's control block, reset by that block) groups
-// the assignments of the whole batch.
+// k_route_tokens: one wave per token sums the partial logits and routes
+// (softmax -> top-K -> renormalise).  k_group then groups the assignments of
+// the whole batch in one block.  (A last-block-done counter inside one kernel
+// would need an L2 write-back per block and same-address atomics across the
+// XCDs, both slower here than the kernel boundary.)
 // ---------------------------------------------------------------------------
 template <int EPL>
-__global__ __launch_bounds__(256) void k_route_tokens(FwdArgs a) {
+__global__ __launch_bounds__(64) void k_route_tokens(FwdArgs a) {
     const int t = blockIdx.x, K = a.s.K, E = a.s.E;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (wave == 0) {
-        float zv[EPL], gs;
-        token_logits<EPL>(a, t, zv, gs);
-        int my_sel;
-        float my_w;
-        route_wave<EPL>(zv, E, K, my_sel, my_w);
-        if (lane < K) {
-            a.ws.sel[t * K + lane] = my_sel;
-            a.ws.coef[t * (K + 1) + lane] = my_w;
-            if (a.route_idx) a.route_idx[t * K + lane] = my_sel;
-            if (a.route_w) a.route_w[t * K + lane] = my_w;
-        } else if (lane == K) {
-            a.ws.coef[t * (K + 1) + K] = sigmoidf_(gs);
-        }
-        __threadfence();  // this token's routing visible to every block
+    const int lane = threadIdx.x & 63;
+    float zv[EPL], gs;
+    token_logits<EPL>(a, t, zv, gs);
+    int my_sel;
+    float my_w;
+    route_wave<EPL>(zv, E, K, my_sel, my_w);
+    if (lane < K) {
+        a.ws.sel[t * K + lane] = my_sel;
+        a.ws.coef[t * (K + 1) + lane] = my_w;
+        if (a.route_idx) a.route_idx[t * K + lane] = my_sel;
+        if (a.route_w) a.route_w[t * K + lane] = my_w;
+    } else if (lane == K) {
+        a.ws.coef[t * (K + 1) + K] = sigmoidf_(gs);
     }
-    __syncthreads();
-    __shared__ int s_last;
-    if (threadIdx.x == 0) s_last = atomicAdd(&a.ws.ctrl[0], 1u) == (unsigned)(a.T - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();  // every other token's routing is visible from here on
-    group_assignments(a);
-    if (threadIdx.x == 0) a.ws.ctrl[0] = 0u;
 }
+
+__global__ __launch_bounds__(kGroupThreads) void k_group(FwdArgs a) { group_assignments(a); }
 
 // unit of work of the grouped kernels: a touched expert (or the shared expert
 // and a chunk of the batch's tokens) and a chunk of rows
@@ -574,9 +567,10 @@ hipError_t launch_grouped_bits(const FwdArgs &a, int stage, hipStream_t st) {
     switch (stage) {
         case 2:
             if (E > 512)
-                hipLaunchKernelGGL(k_route_tokens<16>, dim3((unsigned)T), dim3(256), 0, st, a);
+                hipLaunchKernelGGL(k_route_tokens<16>, dim3((unsigned)T), dim3(64), 0, st, a);
             else
-                hipLaunchKernelGGL(k_route_tokens<8>, dim3((unsigned)T), dim3(256), 0, st, a);
+                hipLaunchKernelGGL(k_route_tokens<8>, dim3((unsigned)T), dim3(64), 0, st, a);
+            hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), 0, st, a);
             break;
         case 3:
         case 5: {

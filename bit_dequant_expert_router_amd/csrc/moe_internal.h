@@ -15,8 +15,7 @@ MOE_HD size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 // Workspace of one forward call, carved from the caller's buffer.
 struct Workspace {
-    uint32_t *ctrl;  // control block, kCtrlBytes, zero between calls: [0] tokens routed so far
-                     // (the grouped path's last routing block resets it)
+    uint32_t *ctrl;  // control block, kCtrlBytes, zeroed by moe_workspace_init (reserved)
     float *h;        // [T][H]   normalised tokens
     float *z;        // [T][E]   router logits
     float *gs;       // [T]      shared-gate logits
