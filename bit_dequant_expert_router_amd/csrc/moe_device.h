@@ -163,32 +163,6 @@ __device__ __forceinline__ uint64_t route_key(float z, int e) {
     return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)e);
 }
 
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint32_t blo, uint32_t bhi) {
-    const uint64_t b = ((uint64_t)bhi << 32) | blo;
-    return b > a ? b : a;
-}
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
-    return max_u64(v, dpp_u<CTRL>((uint32_t)v), dpp_u<CTRL>((uint32_t)(v >> 32)));
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    v = dpp_max_u64<kDppXor1>(v);
-    v = dpp_max_u64<kDppXor2>(v);
-    v = dpp_max_u64<kDppHalfMirror>(v);
-    v = dpp_max_u64<kDppMirror>(v);
-    {
-        const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
-        const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
-        v = max_u64(((uint64_t)hi[0] << 32) | lo[0], lo[1], hi[1]);
-    }
-    {
-        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
-        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
-        v = max_u64(((uint64_t)hi[0] << 32) | lo[0], lo[1], hi[1]);
-    }
-    return v;
-}
-
 __device__ __forceinline__ float route_key_value(uint64_t key) {
     const uint32_t u = (uint32_t)(key >> 32);
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
@@ -225,9 +199,30 @@ __device__ __forceinline__ void sort_desc(uint64_t (&key)[EPL]) {
             }
 }
 
-// Softmax -> top-K -> renormalise by one wave.  Each lane sorts its EPL keys;
-// every round takes the wave maximum of the list heads and the winning lane
-// pops its head.  Lane k < K ends with the k-th selected expert and weight.
+// 32-bit maximum over the wave (DPP row steps, then the row and half swaps)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    v = mx(v, dpp_u<kDppXor1>(v));
+    v = mx(v, dpp_u<kDppXor2>(v));
+    v = mx(v, dpp_u<kDppHalfMirror>(v));
+    v = mx(v, dpp_u<kDppMirror>(v));
+    {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = mx(p[0], p[1]);
+    }
+    {
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = mx(p[0], p[1]);
+    }
+    return v;
+}
+
+// Softmax -> top-K -> renormalise by one wave.  Each lane sorts its EPL keys
+// (logit order in the high word, the complemented index in the low word).
+// Every round takes the wave maximum of the heads' high words; the lane
+// holding it (one ballot bit, or after an exact tie the largest low word,
+// i.e. the lowest index) pops its head.  Lane k < K ends with the k-th
+// selected expert and its weight.
 template <int EPL>
 __device__ __forceinline__ void route_wave(const float (&zv)[EPL], int E, int K, int &my_sel, float &my_w) {
     const int lane = threadIdx.x & 63;
@@ -241,14 +236,22 @@ __device__ __forceinline__ void route_wave(const float (&zv)[EPL], int E, int K,
     my_sel = 0;
     float my_z = 0.0f;
     for (int k = 0; k < K; ++k) {
-        const uint64_t best = wave_max_u64(key[0]);
-        const bool win = key[0] == best;  // keys are unique: the index is part of the key
+        const uint32_t hi = (uint32_t)(key[0] >> 32), lo = (uint32_t)key[0];
+        const uint32_t m = wave_max_u32(hi);
+        uint64_t cand = __ballot(hi == m);
+        if (__popcll(cand) > 1) {  // exact tie of logits: the lowest index wins
+            const uint32_t m2 = wave_max_u32(hi == m ? lo : 0u);
+            cand = __ballot(hi == m && lo == m2);
+        }
+        const int w = __ffsll((unsigned long long)cand) - 1;
+        const uint32_t lo_w = __builtin_amdgcn_readlane(lo, w);
+        const bool win = lane == w;
 #pragma unroll
         for (int i = 0; i < EPL - 1; ++i) key[i] = win ? key[i + 1] : key[i];
         key[EPL - 1] = win ? 0ull : key[EPL - 1];
         if (lane == k) {
-            my_sel = (int)(~(uint32_t)best);
-            my_z = route_key_value(best);
+            my_sel = (int)(~lo_w);
+            my_z = route_key_value(((uint64_t)m << 32) | lo_w);
         }
     }
     // softmax restricted to the selection == renormalised full softmax
