@@ -19,6 +19,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # a single-lane atomic keeps its own return (the wave-combining rewrite
+    # reads the result at once, which waits for every load in flight)
+    "-Xarch_device", "-mllvm=-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

@@ -34,13 +34,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// bf16 bits of f rounded to nearest even (NaN stays a quiet NaN)
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // ---------------------------------------------------------------------------
 // k_norm_batch: a thread owns 16 consecutive entries, four threads a group of 64
 // ---------------------------------------------------------------------------
@@ -77,28 +70,8 @@ __global__ __launch_bounds__(256) void k_norm_batch(FwdArgs a) {
         h[2 * i] = v[2 * i] * inv * bf16_lo(gw[i]);
         h[2 * i + 1] = v[2 * i + 1] * inv * bf16_hi(gw[i]);
     }
-    // three-way bf16 split, stored in the router product's fragment order: the
-    // 16 entries of reduction step u of token t go to lanes t % 32 (entries
-    // 0..7) and t % 32 + 32 (entries 8..15) of fragment (t / 32, u, part)
-    if (live) {
-        uint16_t *hb = a.ws.hb + ((size_t)(t >> 5) * (H / 16) + u) * 3 * 512 + (t & 31) * 8;
-        float r[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) r[i] = h[i];
-#pragma unroll
-        for (int p = 0; p < 3; ++p) {
-            uint32_t w[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t lo = bf16_rne_bits(r[2 * i]), hi = bf16_rne_bits(r[2 * i + 1]);
-                w[i] = lo | (hi << 16);
-                r[2 * i] -= __uint_as_float(lo << 16);
-                r[2 * i + 1] -= __uint_as_float(hi << 16);
-            }
-            *(uint4 *)(hb + p * 512) = make_uint4(w[0], w[1], w[2], w[3]);
-            *(uint4 *)(hb + p * 512 + 32 * 8) = make_uint4(w[4], w[5], w[6], w[7]);
-        }
-    }
+    // three-way bf16 split in the matrix products' fragment order
+    if (live) store_split_fragments(a.ws.hb, H, t, u, h);
     // limb form (entry k of a dword's 8 in nibble k): group max over 4 threads,
     // half-group sums over 2
     float m = 0.0f, sum = 0.0f;

@@ -32,6 +32,38 @@ namespace {
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
 
+// bf16 bits of f rounded to nearest even (NaN stays a quiet NaN)
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Entries 16u .. 16u+15 of vector t (length n) as three bf16 parts (hi, then
+// the bf16 of what hi leaves, then of what both leave: 24 significant bits),
+// stored in the operand order of v_mfma_f32_32x32x16_bf16 over 32 vectors:
+// fragment (t / 32, u, part) holds lane t % 32 (entries 0..7) and lane
+// t % 32 + 32 (entries 8..15), 8 bf16 per lane.
+__device__ __forceinline__ void store_split_fragments(uint16_t *base, int n, int t, int u, const float (&v)[16]) {
+    uint16_t *f = base + ((size_t)(t >> 5) * (n / 16) + u) * 3 * 512 + (t & 31) * 8;
+    float r[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = v[i];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t lo = bf16_rne_bits(r[2 * i]), hi = bf16_rne_bits(r[2 * i + 1]);
+            w[i] = lo | (hi << 16);
+            r[2 * i] -= __uint_as_float(lo << 16);
+            r[2 * i + 1] -= __uint_as_float(hi << 16);
+        }
+        *(uint4 *)(f + p * 512) = make_uint4(w[0], w[1], w[2], w[3]);
+        *(uint4 *)(f + p * 512 + 32 * 8) = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // cross-lane reductions on the VALU: DPP quad permutations and row mirrors
 // inside 16-lane rows, then v_permlane16_swap / v_permlane32_swap across rows.

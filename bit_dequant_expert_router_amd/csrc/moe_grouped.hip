@@ -20,6 +20,8 @@
 //   k_grouped_down  same for the down projection, writing one output vector per
 //                   (token, slot)
 //   k_combine       out = x + sum_k w_k y_k + sigmoid(g_s) y_shared, in slot order
+#include <mutex>
+
 #include "moe_device.h"
 
 namespace moe {
@@ -93,12 +95,93 @@ __device__ __forceinline__ void token_logits(const FwdArgs &a, int t, float (&zv
     }
 }
 
-// grouping of all T*K assignments by expert, by one block of 256 threads:
-// histogram, exclusive scans, the compact list of touched experts, and a
-// stable scatter (token order kept inside each expert)
+// ---------------------------------------------------------------------------
+// pass records of the two streaming launches (0: gate/up, 1: down), written by
+// the grouping block: the shared expert over token chunks of tp first (the
+// heaviest passes start first), then every touched expert over chunks of tp of
+// its assignments (token order), in expert order.  s_pv holds the assignments
+// sorted by (expert, token) as output indices t * (K+1) + slot.
+// ---------------------------------------------------------------------------
 constexpr int kGroupThreads = 1024;
 
-__device__ void group_assignments(const FwdArgs &a) {
+// ceil(c / tp) for 0 <= c <= 2^20 without an integer division: a float
+// quotient, then exact integer corrections
+__device__ __forceinline__ int passes_of(int c, int tp, float inv_tp) {
+    int q = (int)((float)c * inv_tp);
+    if (q * tp > c) --q;
+    if ((q + 1) * tp <= c) ++q;  // q = floor(c / tp)
+    return q + (q * tp < c ? 1 : 0);
+}
+
+__device__ void build_passes(const FwdArgs &a, const StreamPlan &P0, const StreamPlan &P1, const int *s_cnt,
+                             const int *s_off, const int *s_pv) {
+    constexpr int NT = kGroupThreads;
+    const int T = a.T, E = a.s.E, K = a.s.K;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ int s_pp[2][kMaxExperts];  // first pass of each touched expert, per launch
+    // waves 0 and 1: exclusive scan of the passes per expert for launch 0 and 1
+    // (E <= 1024: 16 per lane)
+    if (wave < 2) {
+        const StreamPlan &P = wave == 0 ? P0 : P1;
+        const int tp = P.tp;
+        const float inv = 1.0f / (float)tp;
+        int32_t *head = a.ws.sched + (size_t)wave * sched_launch_ints(T, K);
+        constexpr int kPer = kMaxExperts / 64;
+        int c[kPer];
+        int sum = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = lane * kPer + i;
+            c[i] = (e < E) ? passes_of(s_cnt[e], tp, inv) : 0;
+            sum += c[i];
+        }
+        int pre = wave_excl_scan(sum) + passes_of(T, tp, inv);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = lane * kPer + i;
+            if (e < E) s_pp[wave][e] = pre;
+            pre += c[i];
+        }
+        if (lane == 63) {
+            head[0] = pre;
+            head[1] = pre * P.rpp;
+        }
+    }
+    __syncthreads();
+    // records: thread x takes (launch, shared pass or expert) items
+    for (int launch = 0; launch < 2; ++launch) {
+        const int tp = launch == 0 ? P0.tp : P1.tp;
+        int32_t *rec = a.ws.sched + (size_t)launch * sched_launch_ints(T, K) + 4;
+        const int n_shared = (T + tp - 1) / tp;
+        for (int x = threadIdx.x; x < n_shared + E; x += NT) {
+            if (x < n_shared) {
+                int32_t *r = rec + (size_t)x * kPassRecord;
+                const int nv = min(tp, T - x * tp);
+                r[0] = E;
+                r[1] = nv;
+                for (int v = 0; v < nv; ++v) r[2 + v] = (x * tp + v) * (K + 1) + K;
+            } else {
+                const int e = x - n_shared;
+                const int cnt = s_cnt[e];
+                const int first = s_off[e] - cnt;
+                int32_t *r = rec + (size_t)s_pp[launch][e] * kPassRecord;
+                for (int q0 = 0; q0 < cnt; q0 += tp, r += kPassRecord) {
+                    const int nv = min(tp, cnt - q0);
+                    r[0] = e;
+                    r[1] = nv;
+                    for (int v = 0; v < nv; ++v) r[2 + v] = s_pv[first + q0 + v];
+                }
+            }
+        }
+    }
+}
+
+// grouping of all T*K assignments by expert, by one block of 1024 threads:
+// histogram, exclusive scans, the compact list of touched experts, and a
+// stable scatter (token order kept inside each expert); then the work
+// partitions of the two streaming launches
+
+__device__ void group_assignments(const FwdArgs &a, const StreamPlan &p0, const StreamPlan &p1) {
     constexpr int NT = kGroupThreads;
     const int T = a.T, E = a.s.E, K = a.s.K;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -114,6 +197,7 @@ __device__ void group_assignments(const FwdArgs &a) {
     __shared__ int s_off[kMaxExperts];
     __shared__ int s_tch[kMaxExperts];
     __shared__ uint32_t s_mask[kMaxExperts];
+    __shared__ int s_pv[kGroupMaxAssign];
 
     for (int i = threadIdx.x; i < E; i += NT) s_cnt[i] = 0;
     for (int i = threadIdx.x; i < TK; i += NT) s_sel[i] = a.ws.sel[i];
@@ -168,11 +252,14 @@ __device__ void group_assignments(const FwdArgs &a) {
             const int e = s_sel[i];
             const uint32_t below = s_mask[e] & ((1u << (i / K - c0)) - 1u);
             perm[s_off[e] + __popc(below)] = i;
+            s_pv[s_off[e] + __popc(below)] = i + i / K;  // t * (K+1) + slot
         }
         __syncthreads();
         for (int e = threadIdx.x; e < E; e += NT) s_off[e] += __popc(s_mask[e]);
         __syncthreads();
     }
+    // s_off[e] now ends expert e's assignments: its first is s_off[e] - s_cnt[e]
+    build_passes(a, p0, p1, s_cnt, s_off, s_pv);
 }
 
 // ---------------------------------------------------------------------------
@@ -201,55 +288,24 @@ __global__ __launch_bounds__(64) void k_route_tokens(FwdArgs a) {
     }
 }
 
-__global__ __launch_bounds__(kGroupThreads) void k_group(FwdArgs a) { group_assignments(a); }
-
-// unit of work of the grouped kernels: a touched expert (or the shared expert
-// and a chunk of the batch's tokens) and a chunk of rows
-struct Unit {
-    bool live;
-    bool shared;
-    int expert;
-    int first;   // first assignment in perm (routed) or first token (shared)
-    int count;   // assignments (routed) or tokens (shared)
-};
-
-// units 0 .. n_shared-1: the shared expert over token chunks (the heaviest units
-// are dispatched first); then one unit per touched routed expert
-__device__ __forceinline__ Unit decode_unit(const FwdArgs &a, const GroupView &gv, int ui, int shared_tok_chunk) {
-    Unit u;
-    u.live = false;
-    u.shared = false;
-    const int n_shared = (a.T + shared_tok_chunk - 1) / shared_tok_chunk;
-    if (ui < n_shared) {
-        u.shared = true;
-        u.expert = a.s.E;
-        u.first = ui * shared_tok_chunk;
-        u.count = (a.T - u.first) < shared_tok_chunk ? (a.T - u.first) : shared_tok_chunk;
-        u.live = u.count > 0;
-    } else {
-        // r < G always: the four loads go out together
-        const int r = ui - n_shared;
-        const int nt = *gv.n_touched;
-        u.expert = gv.expert[r];
-        u.first = gv.first[r];
-        u.count = gv.count[r];
-        u.live = r < nt;
-    }
-    return u;
+__global__ __launch_bounds__(kGroupThreads) void k_group(FwdArgs a, StreamPlan p0, StreamPlan p1) {
+    group_assignments(a, p0, p1);
 }
 
-// (token, slot) of the i-th assignment of a unit
-__device__ __forceinline__ void unit_item(const FwdArgs &a, const GroupView &gv, const Unit &u, int i, int &t,
-                                          int &slot) {
-    const int K = a.s.K;
-    if (u.shared) {
-        t = u.first + i;
-        slot = K;
-    } else {
-        const int asg = gv.perm[u.first + i];
-        t = asg / K;
-        slot = asg % K;
-    }
+// the pass records of a streaming launch, read through the constant address
+// space: scalar loads, which the weight loads' wait counter does not include
+typedef const int32_t __attribute__((address_space(4))) const_i32;
+
+struct SchedView {
+    const const_i32 *head;  // [0] passes, [1] runs
+    const const_i32 *rec;   // kPassRecord ints per pass
+};
+
+__device__ __forceinline__ SchedView sched_view(const FwdArgs &a, int launch) {
+    SchedView v;
+    v.head = (const const_i32 *)(a.ws.sched + (size_t)launch * sched_launch_ints(a.T, a.s.K));
+    v.rec = v.head + 4;
+    return v;
 }
 
 // lane slice [k0, k0 + NV) of one vector in limb form: limbs [7][n/8] dwords,
@@ -341,17 +397,22 @@ __global__ __launch_bounds__(256) void k_encode_act(FwdArgs a, int n_pairs) {
 }
 
 // ---------------------------------------------------------------------------
-// k_grouped_stream: the dequant GEMV of one expert matrix pair (gate + up, with
-// SwiGLU) or of the down matrix, for the tokens of one unit and a range of rows.
+// k_grouped_stream: the dequant GEMV of the expert matrix pair (gate + up, with
+// SwiGLU) or of the down matrix, for every pass of a launch.
 //
-// A block takes one unit (a touched expert, or the shared expert and a chunk of
-// tokens) and a range of row-steps.  It stages the limb form of up to TP
-// vectors of the unit (tokens h for gate/up, (token, slot) activations for
-// down) in LDS once, then every wave streams its row-steps: the weights of
-// step s+1 are loaded into one register set while step s is computed from the
-// other, so HBM requests stay in flight through the compute.  Each step's
-// rows are applied to every staged vector (weights read from HBM once per
-// pass; a unit with more than TP vectors takes several passes).
+// A pass applies one expert's rows to up to tp of its vectors (tokens h for
+// gate/up, (token, slot) activations for down); the shared expert's passes
+// take chunks of tp tokens.  Passes are cut into runs of block-steps, and the
+// grid is persistent: block b takes run b, then claims further runs from the
+// counter of its group, one run ahead, so that the grid drains evenly however
+// fast each block streams (fixed per-block work leaves a tail as long as one
+// block at partial occupancy).  For each run a block stages the pass's
+// vectors in LDS; every wave streams its row slots: the weights of the next
+// block-step (across run boundaries too) are loaded into one register set
+// while the current one is computed from the other, so HBM requests stay in
+// flight through the compute, and each step's rows are applied to every
+// staged vector.  No block waits on another: the claims are the only shared
+// state, and the last block to leave resets the counters.
 // ---------------------------------------------------------------------------
 // words of one staged vector of length n: limbs [7][n/8], scales [n/64], half
 // sums [n/32], rounded up to 16 bytes
@@ -364,40 +425,67 @@ struct StepWeights {
     uint32_t sb[NM][RPW][Q::NGL];
 };
 
+// block barrier for LDS only: no wait for global loads or stores in flight
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// a run: its expert matrices, pass and row-step range
+struct StreamRun {
+    const uint8_t *ex;
+    int pass, rs_lo, rs_hi, nsteps;
+};
+
 // LPR: lanes per row when the partial sums of a step are reduced together
 // (16, 32 or 64); 0: any other width, one reduction per row
 template <int BITS, int CPL, int RPW, bool DOWN, int LPR>
-__global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, int chunks, int shared_tok_chunk, int tp) {
+__global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, StreamPlan plan) {
     using Q = QSlice<BITS, CPL>;
+    using W = StepWeights<BITS, CPL, DOWN ? 1 : 2, RPW>;
     constexpr int NM = DOWN ? 1 : 2;
     constexpr int NV = NM * RPW;  // partial sums per lane per step and vector
+    constexpr int launch = DOWN ? 1 : 0;
     extern __shared__ uint4 s_dyn[];
     uint32_t *s_vec = (uint32_t *)s_dyn;
-    __shared__ int s_out[16];  // output vector index (t * (K+1) + slot) per staged vector
-    const int H = a.s.H, F = a.s.F, K = a.s.K;
+    __shared__ int s_out[kMaxPassVectors];  // output vector index (t * (K+1) + slot) per staged vector
+    __shared__ int s_next;                    // the run claimed for after the next one
+    const int H = a.s.H, F = a.s.F, K = a.s.K, E = a.s.E;
     const int n = DOWN ? F : H;  // reduction length
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const GroupView gv = group_view(a);
-    const Unit u = decode_unit(a, gv, blockIdx.x / chunks, shared_tok_chunk);
-    if (!u.live) return;
+    const SchedView sv = sched_view(a, launch);
+    const int grp = blockIdx.x % kClaimGroups;
+    uint32_t *run_ctr = a.ws.ctrl + ctrl_run_counter(launch, grp);
+    uint32_t *exit_ctr = a.ws.ctrl + ctrl_exit_counter(launch, grp);
     const QMat &M0 = a.L.m[DOWN ? 2 : 0];
     const QMat &M1 = a.L.m[1];
     const int lpr = LPR ? LPR : M0.lpr, rpi = 64 / lpr;
     const int lr = lane % lpr, rsub = lane / lpr;
     const int nrs = M0.rows / rpi;
-    const int per_block = (nrs + chunks - 1) / chunks;
-    const int rs_lo = (blockIdx.x % chunks) * per_block;
-    const int rs_hi = min(nrs, rs_lo + per_block);
-    const int nsteps = (rs_hi - rs_lo + 4 * RPW - 1) / (4 * RPW);
-    const uint8_t *ex = u.shared ? a.shared : a.experts + (size_t)u.expert * a.L.bytes;
     const int words = stage_words(n);
     const int k0 = lr * Q::NV;
     const int out_len = DOWN ? H : F;
     float *out_base = DOWN ? a.ws.ys : a.ws.act;
+    const int nb = (int)gridDim.x;
+    const int n_runs = sv.head[1];
 
-    // unconditional loads (rows past the range re-read its last row, unused)
+    auto run_of = [&](int r) {
+        StreamRun R;
+        R.pass = r / plan.rpp;
+        const int b0 = (r - R.pass * plan.rpp) * plan.run_items;
+        const int b1 = min(plan.nbs, b0 + plan.run_items);
+        const int expert = sv.rec[(size_t)R.pass * kPassRecord];
+        R.ex = expert == E ? a.shared : a.experts + (size_t)expert * a.L.bytes;
+        R.rs_lo = b0 * 4 * RPW;
+        R.rs_hi = min(nrs, b1 * 4 * RPW);
+        R.nsteps = b1 - b0;
+        return R;
+    };
+    // unconditional loads (rows past the run re-read its last row, unused)
     // so that no wait separates them
-    auto load_step = [&](int s, StepWeights<BITS, CPL, NM, RPW> &w) {
+    auto load_step = [&](const uint8_t *ex, int rs_lo, int rs_hi, int s, W &w) {
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const int r0 = rs_lo + (s * 4 + wave) * RPW + i;
@@ -406,10 +494,8 @@ __global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, int chunks, i
             if constexpr (NM == 2) load_row<BITS, CPL>(ex, M1, rs * rpi + rsub, lr, w.c[1][i], w.sb[1][i]);
         }
     };
-    auto compute_step = [&](int s, StepWeights<BITS, CPL, NM, RPW> &w, int np) {
-        const int rs0 = rs_lo + (s * 4 + wave) * RPW;
-        // row-major list of the step's rows: entry NM * i + m
-        uint4 (&c)[NV][CPL] = *reinterpret_cast<uint4 (*)[NV][CPL]>(&w.c[0][0][0]);
+    auto compute_step = [&](const StreamRun &R, int s, int np, W &w) {
+        const int rs0 = R.rs_lo + (s * 4 + wave) * RPW;
         float sc[NV][Q::NGL], of[NV][Q::NGL];
 #pragma unroll
         for (int i = 0; i < RPW; ++i)
@@ -422,6 +508,7 @@ __global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, int chunks, i
                     of[NM * i + m][g] = fmaf(Q::kCodeOffset, sc[NM * i + m][g], bf16_hi(w.sb[m][i][g]));
                 }
             }
+        // row-major list of the step's rows: entry NM * i + m
         uint4 cl[NV][CPL];
 #pragma unroll
         for (int i = 0; i < RPW; ++i)
@@ -429,7 +516,6 @@ __global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, int chunks, i
             for (int m = 0; m < NM; ++m)
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) cl[NM * i + m][j] = w.c[m][i][j];
-        (void)c;
         for (int v = 0; v < np; ++v) {
             const uint32_t *vec = s_vec + (size_t)v * words;
             float *out = out_base + (size_t)s_out[v] * out_len;
@@ -437,24 +523,24 @@ __global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, int chunks, i
             rows_dot_lds<BITS, CPL, NV>(cl, sc, of, vec, (const float *)(vec + kLimbs * (n / 8)),
                                         (const float *)(vec + kLimbs * (n / 8) + n / 64), n, k0, part);
             if constexpr (LPR != 0) {
-                // every row of the step at once; rows past the block's range
-                // are computed on stale registers and not written
+                // every row of the step at once; rows past the run are computed
+                // on stale registers and not written
                 const float r = multi_reduce<NV, LPR>(part);
                 constexpr int DL = LPR / NV;  // lanes sharing one reduced entry
                 const int j = multi_index<NV, LPR>(lane);
                 const int rs = rs0 + j / NM;
                 if constexpr (DOWN) {
-                    if ((lane & (DL - 1)) == 0 && rs < rs_hi) out[rs * rpi + rsub] = r;
+                    if ((lane & (DL - 1)) == 0 && rs < R.rs_hi) out[rs * rpi + rsub] = r;
                 } else {
                     const float up = xchg<DL>(r);  // the up sum sits across the last halving bit
                     const float act = r * up * __builtin_amdgcn_rcpf(1.0f + __expf(-r));
-                    if ((lane & (2 * DL - 1)) == 0 && rs < rs_hi) out[rs * rpi + rsub] = act;
+                    if ((lane & (2 * DL - 1)) == 0 && rs < R.rs_hi) out[rs * rpi + rsub] = act;
                 }
             } else {
 #pragma unroll
                 for (int i = 0; i < RPW; ++i) {
                     const int rs = rs0 + i;
-                    if (rs < rs_hi) {
+                    if (rs < R.rs_hi) {
                         if constexpr (DOWN) {
                             const float y = lane_group_sum(part[i], lpr);
                             if (lr == 0) out[rs * rpi + rsub] = y;
@@ -468,37 +554,112 @@ __global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, int chunks, i
             }
         }
     };
-
-    for (int p0 = 0; p0 < u.count; p0 += tp) {
-        const int np = min(tp, u.count - p0);
-        StepWeights<BITS, CPL, NM, RPW> wa, wb;
-        load_step(0, wa);  // in flight while the vectors are staged
-        if (p0 > 0) __syncthreads();  // the previous pass is done with LDS
-        // stage the np vectors: limbs as 16-byte pieces, then scales and half sums
+    // stage a run's vectors: limbs as 16-byte pieces, then scales and half
+    // sums, every load of a vector issued before its single wait (indices
+    // clamped, stores guarded); returns the vector count
+    auto stage = [&](const StreamRun &R) {
+        constexpr int kPieces = (kLimbs * kMaxDim / 32 + 255) / 256;
+        const const_i32 *rec = sv.rec + (size_t)R.pass * kPassRecord;
+        const int np = rec[1];
+        const int nl = kLimbs * n / 32, ng = n / 64, nh = n / 32;
         for (int v = 0; v < np; ++v) {
-            int t, slot;
-            unit_item(a, gv, u, p0 + v, t, slot);
-            const int pv = t * (K + 1) + slot;
+            const int pv = rec[2 + v];
+            const int t = pv / (K + 1);
             if (threadIdx.x == 0) s_out[v] = pv;
-            const uint32_t *hl = DOWN ? (const uint32_t *)a.ws.al + (size_t)pv * kLimbs * (F / 8)
-                                      : (const uint32_t *)a.ws.hl + (size_t)t * kLimbs * (H / 8);
+            const uint4 *hl = DOWN ? (const uint4 *)((const uint32_t *)a.ws.al + (size_t)pv * kLimbs * (F / 8))
+                                   : (const uint4 *)((const uint32_t *)a.ws.hl + (size_t)t * kLimbs * (H / 8));
             const float *hs = DOWN ? a.ws.as + (size_t)pv * (F / 64) : a.ws.hs + (size_t)t * (H / 64);
             const float *hx = DOWN ? a.ws.ax + (size_t)pv * (F / 32) : a.ws.hx + (size_t)t * (H / 32);
+            // every index wraps (i mod count): past the end a lane rewrites
+            // an entry that another lane writes too, with the same value, at
+            // its own address (a guarded store would let the compiler sink its
+            // load into the guard, one wait per load; a clamped one would put
+            // every such lane on one LDS word)
+            // (a native vector type: an array of uint4 here keeps dead copies in
+            // scratch memory, each store waiting for its load)
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            int li[kPieces];
+            u32x4 lp[kPieces];
+#pragma unroll
+            for (int j = 0; j < kPieces; ++j) {
+                li[j] = (int)((threadIdx.x + 256u * j) % (unsigned)nl);
+                lp[j] = ((const u32x4 *)hl)[li[j]];
+            }
+            const int gi = threadIdx.x & (ng - 1), xi = threadIdx.x & (nh - 1);  // ng, nh: powers of two
+            const float gs = hs[gi];
+            const float xs = hx[xi];
             uint32_t *dst = s_vec + (size_t)v * words;
-            for (int i = threadIdx.x; i < kLimbs * n / 32; i += 256) ((uint4 *)dst)[i] = ((const uint4 *)hl)[i];
-            for (int i = threadIdx.x; i < n / 64; i += 256) dst[kLimbs * (n / 8) + i] = __float_as_uint(hs[i]);
-            for (int i = threadIdx.x; i < n / 32; i += 256) dst[kLimbs * (n / 8) + n / 64 + i] = __float_as_uint(hx[i]);
+#pragma unroll
+            for (int j = 0; j < kPieces; ++j) ((u32x4 *)dst)[li[j]] = lp[j];
+            dst[kLimbs * (n / 8) + gi] = __float_as_uint(gs);
+            dst[kLimbs * (n / 8) + ng + xi] = __float_as_uint(xs);
         }
-        __syncthreads();
-        // the prefetches are unconditional (past the last step they re-read
-        // it, from cache): a load issued on one path only would make the
-        // waits after the join count for the path without it, i.e. wait for
-        // the prefetch itself
-        for (int s = 0; s < nsteps; s += 2) {
-            load_step(s + 1 < nsteps ? s + 1 : nsteps - 1, wb);
-            compute_step(s, wa, np);
-            load_step(s + 2 < nsteps ? s + 2 : nsteps - 1, wa);
-            if (s + 1 < nsteps) compute_step(s + 1, wb, np);
+        return np;
+    };
+
+    uint32_t claim = 0;  // thread 0: the counter value of the last claim
+    // thread 0, once the claim made earlier has returned: publish its run (or
+    // -1 past the last) and claim the run after it
+    auto take_claim = [&]() {
+        const int r = nb + kClaimGroups * (int)claim + grp;
+        s_next = r < n_runs ? r : -1;
+        if (r < n_runs) claim = atomicAdd(run_ctr, 1u);
+    };
+    int cur_r = blockIdx.x;
+    if (cur_r < n_runs) {
+        if (threadIdx.x == 0) claim = atomicAdd(run_ctr, 1u);
+        StreamRun cur = run_of(cur_r);
+        W w0, w1;
+        load_step(cur.ex, cur.rs_lo, cur.rs_hi, 0, w0);  // in flight while the vectors are staged
+        int np = stage(cur);
+        if (threadIdx.x == 0) take_claim();  // after the staging loads' wait
+        lds_barrier();
+        int nxt_r = s_next;
+        StreamRun nxt = run_of(nxt_r >= 0 ? nxt_r : cur_r);
+        int s = 0;  // step of `cur` computed next
+        // one block-step: load the one after it (the next step, else the next
+        // run's first, else this one again, unused: the loads are
+        // unconditional, since a load issued on one path only would make the
+        // waits after the join count for the path without it), compute this
+        // one, and cross into the next run at the end of this one.  At the
+        // crossing the claim made one run earlier is read (its wait also
+        // covers the next step's weights, which the staging waits for anyway)
+        // and the next claim goes out just before the staging loads.
+        auto advance = [&](W &wc, W &wl) {
+            const bool in_cur = s + 1 < cur.nsteps;
+            const bool to_nxt = !in_cur && nxt_r >= 0;
+            const uint8_t *lex = to_nxt ? nxt.ex : cur.ex;
+            const int llo = to_nxt ? nxt.rs_lo : cur.rs_lo, lhi = to_nxt ? nxt.rs_hi : cur.rs_hi;
+            const int ls = in_cur ? s + 1 : (to_nxt ? 0 : s);
+            load_step(lex, llo, lhi, ls, wl);
+            compute_step(cur, s, np, wc);
+            if (in_cur) {
+                ++s;
+                return true;
+            }
+            if (nxt_r < 0) return false;
+            lds_barrier();  // the run is done with LDS
+            cur_r = nxt_r;
+            cur = nxt;
+            if (threadIdx.x == 0) take_claim();  // the new claim returns with the staging loads
+            np = stage(cur);
+            lds_barrier();  // staged vectors and s_next visible
+            nxt_r = s_next;
+            nxt = run_of(nxt_r >= 0 ? nxt_r : cur_r);
+            s = 0;
+            return true;
+        };
+        while (advance(w0, w1) && advance(w1, w0)) {
+        }
+    }
+    // the last block of the group to leave resets the group's counters for
+    // the next launch (its own last claim has returned: the exit count
+    // depends on it)
+    if (threadIdx.x == 0) {
+        const uint32_t prior = atomicAdd(exit_ctr, claim != 0xffffffffu ? 1u : 2u);
+        if (prior == (uint32_t)(nb / kClaimGroups) - 1u) {
+            atomicExch(run_ctr, 0u);
+            atomicExch(exit_ctr, 0u);
         }
     }
 }
@@ -521,8 +682,10 @@ __global__ __launch_bounds__(256) void k_combine(FwdArgs a) {
 // row-slots per wave and step of k_grouped_stream: two register sets of
 // weights stay within ~80 VGPRs
 constexpr int stream_rpw(int cpl) { return cpl == 1 ? 4 : 2; }
-constexpr int kStreamStepsPerWave = 8;  // row-steps a wave streams per block
-constexpr int kStreamMaxVectors = 16;
+// block-steps per run: the gate/up runs take about as long as down runs of
+// half as many steps (two matrices per step)
+constexpr int kGateUpRunItems = 8;
+constexpr int kDownRunItems = 4;
 
 // vectors staged per pass: as many as fit the block's LDS budget (48 KiB for
 // gate/up: three blocks per CU; 40 KiB for down, whose registers allow four),
@@ -530,61 +693,119 @@ constexpr int kStreamMaxVectors = 16;
 inline int stream_vectors(int n, bool down) {
     const int budget = (down ? 40 : 48) * 1024;
     const int v = budget / (stage_words(n) * 4);
-    return v < kStreamMaxVectors ? v : kStreamMaxVectors;
+    return v < kMaxPassVectors ? v : kMaxPassVectors;
 }
 
-template <int BITS, int CPL, bool DOWN, int LPR>
-void launch_stream(const FwdArgs &a, hipStream_t st) {
-    const QMat &M = a.L.m[DOWN ? 2 : 0];
-    const int rpi = 64 / M.lpr;
-    const int nrs = M.rows / rpi;
-    constexpr int rpw = stream_rpw(CPL);
-    const int chunks = (nrs + 4 * rpw * kStreamStepsPerWave - 1) / (4 * rpw * kStreamStepsPerWave);
-    const int n = DOWN ? a.s.F : a.s.H;
-    const int tp = stream_vectors(n, DOWN);
-    // shared-expert units of tp tokens: one pass each
-    const int units = touched_bound(a.s, a.T) + (a.T + tp - 1) / tp;
-    const size_t lds = (size_t)tp * stage_words(n) * 4;
-    hipLaunchKernelGGL((k_grouped_stream<BITS, CPL, rpw, DOWN, LPR>), dim3((unsigned)(units * chunks)), dim3(256), lds, st,
-                       a, chunks, tp, tp);
+// block slots of the GPU for a kernel (cached per kernel, LDS size and device)
+hipError_t stream_block_slots(const void *fn, size_t lds, int &slots) {
+    struct Entry {
+        const void *fn;
+        size_t lds;
+        int dev, slots;
+    };
+    static std::mutex mu;
+    static Entry cache[64];
+    static int n_cache = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n_cache; ++i)
+        if (cache[i].fn == fn && cache[i].lds == lds && cache[i].dev == dev) {
+            slots = cache[i].slots;
+            return hipSuccess;
+        }
+    int per_cu = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, lds);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
+    slots = per_cu * cus;
+    if (n_cache < 64) cache[n_cache++] = Entry{fn, lds, dev, slots};
+    return hipSuccess;
 }
+
+// the plan of one streaming launch (and, with launch set, the launch itself)
+struct StreamOp {
+    const FwdArgs *a;
+    hipStream_t st;
+    bool launch;
+    StreamPlan plan;
+    template <int BITS, int CPL, bool DOWN, int LPR>
+    hipError_t run() {
+        constexpr int rpw = stream_rpw(CPL);
+        auto fn = k_grouped_stream<BITS, CPL, rpw, DOWN, LPR>;
+        const QMat &M = a->L.m[DOWN ? 2 : 0];
+        const int rpi = 64 / M.lpr;
+        const int nrs = M.rows / rpi;
+        const int n = DOWN ? a->s.F : a->s.H;
+        StreamPlan p;
+        p.tp = stream_vectors(n, DOWN);
+        p.nbs = (nrs + 4 * rpw - 1) / (4 * rpw);
+        p.run_items = DOWN ? kDownRunItems : kGateUpRunItems;
+        p.rpp = (p.nbs + p.run_items - 1) / p.run_items;
+        const size_t lds = (size_t)p.tp * stage_words(n) * 4;
+        const hipError_t e = stream_block_slots((const void *)fn, lds, p.nb);
+        if (e != hipSuccess) return e;
+        p.nb = (p.nb + kClaimGroups - 1) / kClaimGroups * kClaimGroups;
+        plan = p;
+        if (launch) hipLaunchKernelGGL(fn, dim3((unsigned)p.nb), dim3(256), lds, st, *a, p);
+        return hipSuccess;
+    }
+};
 
 // the butterfly reduction needs lanes per row >= partial sums per lane
 template <int BITS, int CPL, bool DOWN>
-void launch_grouped_mats(const FwdArgs &a, hipStream_t st) {
+hipError_t dispatch_lpr(StreamOp &op) {
     constexpr int nv = (DOWN ? 1 : 2) * stream_rpw(CPL);
-    switch (a.L.m[DOWN ? 2 : 0].lpr) {
-        case 64: launch_stream<BITS, CPL, DOWN, 64>(a, st); break;
-        case 32: launch_stream<BITS, CPL, DOWN, (nv <= 32 ? 32 : 0)>(a, st); break;
-        case 16: launch_stream<BITS, CPL, DOWN, (nv <= 16 ? 16 : 0)>(a, st); break;
-        default: launch_stream<BITS, CPL, DOWN, 0>(a, st); break;
+    switch (op.a->L.m[DOWN ? 2 : 0].lpr) {
+        case 64: return op.template run<BITS, CPL, DOWN, 64>();
+        case 32: return op.template run<BITS, CPL, DOWN, (nv <= 32 ? 32 : 0)>();
+        case 16: return op.template run<BITS, CPL, DOWN, (nv <= 16 ? 16 : 0)>();
+        default: return op.template run<BITS, CPL, DOWN, 0>();
     }
+}
+
+template <int BITS, bool DOWN>
+hipError_t dispatch_stream(StreamOp &op) {
+    const int cpl = op.a->L.m[DOWN ? 2 : 0].cpl;
+    if (cpl == 1) return dispatch_lpr<BITS, 1, DOWN>(op);
+    if constexpr (BITS == 4) {
+        if (cpl == 2) return dispatch_lpr<4, 2, DOWN>(op);  // 2-bit rows of 4096 or fewer codes take one chunk per lane
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int BITS>
+hipError_t stream_op(const FwdArgs &a, bool down, bool launch, hipStream_t st, StreamPlan &plan) {
+    StreamOp op{&a, st, launch, StreamPlan{}};
+    const hipError_t e = down ? dispatch_stream<BITS, true>(op) : dispatch_stream<BITS, false>(op);
+    plan = op.plan;
+    return e;
 }
 
 template <int BITS>
 hipError_t launch_grouped_bits(const FwdArgs &a, int stage, hipStream_t st) {
     const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K, T = a.T;
     switch (stage) {
-        case 2:
+        case 2: {
+            StreamPlan p0, p1;
+            hipError_t e = stream_op<BITS>(a, false, false, st, p0);
+            if (e == hipSuccess) e = stream_op<BITS>(a, true, false, st, p1);
+            if (e != hipSuccess) return e;
             if (E > 512)
                 hipLaunchKernelGGL(k_route_tokens<16>, dim3((unsigned)T), dim3(64), 0, st, a);
             else
                 hipLaunchKernelGGL(k_route_tokens<8>, dim3((unsigned)T), dim3(64), 0, st, a);
-            hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), 0, st, a);
+            hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), 0, st, a, p0, p1);
             break;
+        }
         case 3:
         case 5: {
-            const bool down = stage == 5;
-            const int cpl = a.L.m[down ? 2 : 0].cpl;
-            if (cpl == 1) {
-                if (down) launch_grouped_mats<BITS, 1, true>(a, st);
-                else launch_grouped_mats<BITS, 1, false>(a, st);
-            } else if (BITS == 4 && cpl == 2) {  // 2-bit rows of 4096 or fewer codes take one chunk per lane
-                if (down) launch_grouped_mats<4, 2, true>(a, st);
-                else launch_grouped_mats<4, 2, false>(a, st);
-            } else {
-                return hipErrorInvalidValue;
-            }
+            StreamPlan p;
+            const hipError_t e = stream_op<BITS>(a, stage == 5, true, st, p);
+            if (e != hipSuccess) return e;
             break;
         }
         case 4: {

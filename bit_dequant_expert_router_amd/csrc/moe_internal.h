@@ -9,13 +9,14 @@
 namespace moe {
 
 constexpr size_t kAlign = 256;
-constexpr size_t kCtrlBytes = 256;
+constexpr size_t kCtrlBytes = 8192;  // 2 launches x 2 counters x kClaimGroups x 256 bytes
 
 MOE_HD size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 // Workspace of one forward call, carved from the caller's buffer.
 struct Workspace {
-    uint32_t *ctrl;  // control block, kCtrlBytes, zeroed by moe_workspace_init (reserved)
+    uint32_t *ctrl;  // control block, kCtrlBytes, zeroed by moe_workspace_init: the streaming
+                     // launches' run and exit counters (each launch leaves them at zero)
     float *h;        // [T][H]   normalised tokens
     float *z;        // [T][E]   router logits
     float *gs;       // [T]      shared-gate logits
@@ -35,6 +36,8 @@ struct Workspace {
     uint16_t *hb;    // h = hi + mid + lo in bf16, the router GEMM's operand, in fragment order:
                      // [ceil(T/32)][H/16][3][64 lanes][8] (see k_norm_batch)
     float *zp;       // [KS][T][E+1] partial router logits (column E: shared gate), KS = router_ksplit(H)
+    int32_t *sched;  // passes of the two streaming launches (gate/up, down), each
+                     // sched_launch_ints(T, K) ints: head, then kPassRecord ints per pass
 };
 
 // k-splits of the batched router GEMM: 512 reduction entries per block when H >= 512
@@ -46,6 +49,36 @@ struct Shape {
     int H, F, E, K, bits;
     float eps;
 };
+
+// Work of the grouped path's streaming kernels.  A "pass" applies one expert's
+// rows to up to tp (<= kMaxPassVectors) of its vectors; every pass is cut into
+// nbs block-steps (4 waves x RPW row slots) and those into runs of up to
+// `run_items` block-steps.  A persistent grid of nb blocks (a multiple of
+// kClaimGroups) takes the runs: block b runs b first, then claims runs
+// nb + G c + b % G, c = 0, 1, ... from the counter of its group in the control
+// block (claimed one run ahead, so the claim's latency is hidden).  The
+// grouping kernel writes, per launch, a head ([0]
+// passes, [1] runs) and one record per pass: expert (E: the shared one),
+// vector count, then the vectors' output indices t * (K+1) + slot.
+constexpr int kMaxPassVectors = 16;
+constexpr int kPassRecord = 2 + kMaxPassVectors;
+MOE_HD int sched_max_passes(int T, int K) { return T * (K + 1); }
+MOE_HD int sched_launch_ints(int T, int K) { return 4 + kPassRecord * sched_max_passes(T, K); }
+struct StreamPlan {
+    int tp;         // vectors staged per pass
+    int nbs;        // block-steps per pass
+    int run_items;  // block-steps per run
+    int rpp;        // runs per pass, ceil(nbs / run_items)
+    int nb;         // blocks of the persistent grid
+};
+// Run claims go through kClaimGroups counters (block b uses counter b % G and
+// claims the runs r = b mod G), so that no single address takes every claim;
+// each counter sits in its own 256-byte line of the control block, after the
+// claim counters of launch 0 and 1 come the exit counters.
+constexpr int kClaimGroups = 8;
+constexpr int kCtrlStride = 64;  // words between counters
+MOE_HD int ctrl_run_counter(int launch, int g) { return ((launch * 2 + 0) * kClaimGroups + g) * kCtrlStride; }
+MOE_HD int ctrl_exit_counter(int launch, int g) { return ((launch * 2 + 1) * kClaimGroups + g) * kCtrlStride; }
 
 // touched-expert bound of a batch and the integers of the grouping table
 inline int touched_bound(const Shape &s, int T) { return (T * s.K < s.E) ? T * s.K : s.E; }
@@ -71,6 +104,7 @@ inline size_t workspace_bytes(const Shape &s, int T) {
     b += align_up((size_t)T * (s.K + 1) * (s.F / 32) * 4);
     b += align_up((size_t)token_tiles(T) * 32 * 3 * s.H * 2);
     b += align_up((size_t)router_ksplit(s.H) * T * (s.E + 1) * 4);
+    b += align_up((size_t)2 * sched_launch_ints(T, s.K) * 4);
     return b;
 }
 
@@ -110,6 +144,8 @@ inline Workspace carve_workspace(void *base, const Shape &s, int T) {
     w.hb = (uint16_t *)p;
     p += align_up((size_t)token_tiles(T) * 32 * 3 * s.H * 2);
     w.zp = (float *)p;
+    p += align_up((size_t)router_ksplit(s.H) * T * (s.E + 1) * 4);
+    w.sched = (int32_t *)p;
     return w;
 }
 

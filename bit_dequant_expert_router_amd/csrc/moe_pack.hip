@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void k_generate(GenArgs a, size_t expert_bytes
 }
 
 __global__ void k_clear_ctrl(uint32_t *ctrl) {
-    if (threadIdx.x < kCtrlBytes / 4) ctrl[threadIdx.x] = 0u;
+    for (int i = threadIdx.x; i < (int)(kCtrlBytes / 4); i += blockDim.x) ctrl[i] = 0u;
 }
 
 }  // namespace

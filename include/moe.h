@@ -117,9 +117,11 @@ size_t moe_expert_bytes(const moe_dims_t *dims);
 size_t moe_workspace_bytes(const moe_dims_t *dims, int32_t n_tokens);
 
 /*
- * Zero the workspace's control block (device memory, >= 256 B, 256-B aligned).
- * Needed once, before the first forward call on a new workspace; every forward
- * call leaves the control block zero again.  Enqueued on `stream`.
+ * Zero the workspace's control block: its first 8 KiB (device memory, 256-B
+ * aligned, workspace_bytes >= 8192), which hold the counters through which
+ * the batched path's blocks claim their work.  Needed once, before the first
+ * forward call on a new workspace; every forward call that completes leaves
+ * the control block zero again.  Enqueued on `stream`.
  */
 int moe_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 

@@ -219,9 +219,10 @@ def test_pack_generate_init_reject():
     assert g(ctypes.byref(dims), 0, 0, None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert g(ctypes.byref(dims), 0, 0, A + 0x80, None, None) == moe.MOE_ERR_ALIGNMENT
     i = moe._lib.moe_workspace_init
-    assert i(None, 4096, None) == moe.MOE_ERR_INVALID_ARG
+    assert i(None, 16384, None) == moe.MOE_ERR_INVALID_ARG
     assert i(A, 16, None) == moe.MOE_ERR_WORKSPACE
-    assert i(A + 8, 4096, None) == moe.MOE_ERR_ALIGNMENT
+    assert i(A, 4096, None) == moe.MOE_ERR_WORKSPACE  # the control block is 8 KiB
+    assert i(A + 8, 16384, None) == moe.MOE_ERR_ALIGNMENT
 
 
 def test_status_strings():
