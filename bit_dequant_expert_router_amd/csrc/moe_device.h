@@ -7,17 +7,17 @@
 //
 // Gate/up (activation h, the normalised token): the code products sum_i q_i h_i
 // are taken exactly in integers.  Each group of h is written as V_i * S with S a
-// power of two (max|h| < 2^26 S) and V_i an integer split into seven signed
+// power of two (max|h| < 2^22 S) and V_i an integer split into six signed
 // base-16 digits (limbs) V = sum_x L_x 16^x, L_x in [-8, 7].  Eight limbs of
 // consecutive entries are packed per dword, the operand form of v_dot8_i32_i4;
 // the codes q, made signed as q - 8 by one XOR per 8 codes (4-bit), are the other
 // operand, so one instruction accumulates 8 exact code x limb products.  Per group
 // and limb the sums stay below 2^12; one fp32 combination restores
 // s*S*sum_x D_x 16^x, and the -8 folds into the bias term, (b + 8 s) * sum h.
-// Values within a factor 4 of their group's maximum are represented exactly
-// (a float has 24 significant bits), smaller ones with an absolute error below
-// 2^-27 of it, so the result matches an fp32 dot product; the VALU does 1.0
-// instruction per weight against ~2.3 for convert-and-FMA.
+// Every entry is rounded to a multiple of S, an error of at most 2^-23 of the
+// group's power-of-two bound (fp32 rounds an entry at 2^-24 of itself); the
+// products and their sums are exact.  The VALU does about one instruction
+// per weight against ~2.3 for convert-and-FMA.
 //
 // Down (activation a = SwiGLU output, widely spread magnitudes): fp32, codes
 // converted with v_cvt_f32_ubyte (byte code order) and folded per group.
@@ -147,10 +147,10 @@ __device__ __forceinline__ uint32_t ld_stream4(const uint32_t *p) { return __bui
 // ---------------------------------------------------------------------------
 // fixed-point limbs
 // ---------------------------------------------------------------------------
-constexpr int kLimbs = 7;                  // signed base-16 digits
-constexpr int kFixBits = 4 * kLimbs - 2;   // |V| <= 2^26
+constexpr int kLimbs = 6;                  // signed base-16 digits
+constexpr int kFixBits = 4 * kLimbs - 2;   // |V| <= 2^22
 
-// Exponent e with max|v| < 2^e, clamped so that 2^(e-26) and 2^(26-e) are
+// Exponent e with max|v| < 2^e, clamped so that 2^(e-22) and 2^(22-e) are
 // normal floats.  NaN / inf maxima are flagged by limb_scale.
 __device__ __forceinline__ int limb_exponent(float m) {
     const uint32_t E = (__float_as_uint(m) >> 23) & 0xFFu;
@@ -158,16 +158,16 @@ __device__ __forceinline__ int limb_exponent(float m) {
     return e < -90 ? -90 : e;
 }
 __device__ __forceinline__ float pow2f(int p) { return __uint_as_float((uint32_t)(p + 127) << 23); }
-// scale S of a group: 2^(e-26), or NaN when the group holds a NaN or an inf
+// scale S of a group: 2^(e-22), or NaN when the group holds a NaN or an inf
 __device__ __forceinline__ float limb_scale(float m) {
     return (m <= 3.4028234663852886e38f) ? pow2f(limb_exponent(m) - kFixBits) : __uint_as_float(0x7FC00000u);
 }
-// integer V = rint(v / S) for finite groups (|V| <= 2^26), 0 otherwise
+// integer V = rint(v / S) for finite groups (|V| <= 2^22), 0 otherwise
 __device__ __forceinline__ int limb_value(float v, float m) {
     if (!(m <= 3.4028234663852886e38f)) return 0;
     return (int)rintf(v * pow2f(kFixBits - limb_exponent(m)));
 }
-// balanced base-16 digits: V = sum_x l[x] 16^x, l[0..5] in [-8, 7], l[6] in [-4, 4]
+// balanced base-16 digits: V = sum_x l[x] 16^x, l[0..4] in [-8, 7], l[5] in [-4, 4]
 __device__ __forceinline__ void limb_split(int V, int (&l)[kLimbs]) {
 #pragma unroll
     for (int x = 0; x < kLimbs - 1; ++x) {
@@ -365,8 +365,8 @@ __device__ __forceinline__ float qdot(const uint4 (&c)[CPL], const uint32_t (&sb
 
 // Variant for weights reused across several activation vectors: the codes are
 // prepared once per row (4-bit: made signed by the XOR), the group scale s and
-// offset o = b + off * s are unpacked once, and the seven limb sums are
-// combined in integers by Horner steps (limbs 4-6 and 0-3: |sum| < 2^25),
+// offset o = b + off * s are unpacked once, and the six limb sums are
+// combined in integers by Horner steps (limbs 4-5 and 0-3: |sum| < 2^25),
 // then in fp32: f = hi * 2^16 + lo.
 template <int BITS, int CPL>
 struct RowPrep {
@@ -438,7 +438,7 @@ __device__ __forceinline__ float qdot_prep(const RowPrep<BITS, CPL> &r, const Li
 
 // NR prepared rows against one vector's lane slice held in LDS.  The limb
 // words are read one limb at a time, limb-major, so that only 8 of them are
-// live; each row keeps two integer Horner accumulators (limbs 6-4, 3-0).
+// live; each row keeps two integer Horner accumulators (limbs 5-4, 3-0).
 // Codes must be prepared (prep_codes) and s, o unpacked (prep_scales).
 template <int BITS, int CPL>
 __device__ __forceinline__ void prep_codes(uint4 (&c)[CPL]) {
@@ -449,7 +449,7 @@ __device__ __forceinline__ void prep_codes(uint4 (&c)[CPL]) {
     }
 }
 
-// limbs: [7][n/8] words; S: [n/64] group scales; Xh: [n/32] half-group sums
+// limbs: [kLimbs][n/8] words; S: [n/64] group scales; Xh: [n/32] half-group sums
 template <int BITS, int CPL, int NR>
 __device__ __forceinline__ void rows_dot_lds(const uint4 (&c)[NR][CPL], const float (&s)[NR][QSlice<BITS, CPL>::NGL],
                                              const float (&o)[NR][QSlice<BITS, CPL>::NGL], const uint32_t *limbs,

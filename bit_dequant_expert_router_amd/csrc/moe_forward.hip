@@ -260,17 +260,17 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
 
     // stage the limb form of h in LDS, once per block
     {
-        const int4 *src = (const int4 *)((const uint32_t *)a.ws.hl + (size_t)t * kLimbs * (H / 8));
+        // kStage 16-byte pieces per thread (a native vector type: an array of
+        // int4 can keep dead copies in scratch memory)
+        typedef int i32x4 __attribute__((ext_vector_type(4)));
+        const i32x4 *src = (const i32x4 *)((const uint32_t *)a.ws.hl + (size_t)t * kLimbs * (H / 8));
         const int n16 = kLimbs * H / 32;
         constexpr int kStage = (kLimbs * kMaxDim / 32 + 255) / 256;
-        int4 st0, st1, st2, st3;  // kStage == 4 staged 16-byte pieces per thread
-        static_assert(kStage == 4, "staging assumes 4 pieces per thread");
-        {
-            const int i0 = threadIdx.x, i1 = threadIdx.x + 256, i2 = threadIdx.x + 512, i3 = threadIdx.x + 768;
-            st0 = src[i0 < n16 ? i0 : 0];
-            st1 = src[i1 < n16 ? i1 : 0];
-            st2 = src[i2 < n16 ? i2 : 0];
-            st3 = src[i3 < n16 ? i3 : 0];
+        i32x4 st[kStage];
+#pragma unroll
+        for (int j = 0; j < kStage; ++j) {
+            const int i = threadIdx.x + 256 * j;
+            st[j] = src[i < n16 ? i : 0];
         }
         float hs = 0.0f, hx = 0.0f;
         if (threadIdx.x < H / 64) hs = a.ws.hs[(size_t)t * (H / 64) + threadIdx.x];
@@ -295,12 +295,12 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
             }
         }
         {
-            int4 *dst = (int4 *)s_hl;
-            const int i0 = threadIdx.x, i1 = threadIdx.x + 256, i2 = threadIdx.x + 512, i3 = threadIdx.x + 768;
-            if (i0 < n16) dst[i0] = st0;
-            if (i1 < n16) dst[i1] = st1;
-            if (i2 < n16) dst[i2] = st2;
-            if (i3 < n16) dst[i3] = st3;
+            i32x4 *dst = (i32x4 *)s_hl;
+#pragma unroll
+            for (int j = 0; j < kStage; ++j) {
+                const int i = threadIdx.x + 256 * j;
+                if (i < n16) dst[i] = st[j];
+            }
         }
         if (threadIdx.x < H / 64) s_hs[threadIdx.x] = hs;
         if (threadIdx.x < H / 32) s_hx[threadIdx.x] = hx;

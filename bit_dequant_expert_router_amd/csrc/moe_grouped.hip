@@ -308,7 +308,7 @@ __device__ __forceinline__ SchedView sched_view(const FwdArgs &a, int launch) {
     return v;
 }
 
-// lane slice [k0, k0 + NV) of one vector in limb form: limbs [7][n/8] dwords,
+// lane slice [k0, k0 + NV) of one vector in limb form: limbs [kLimbs][n/8] dwords,
 // group scales [n/64], half-group sums [n/32]
 template <int BITS, int CPL>
 __device__ __forceinline__ void load_limb_slice(const uint32_t *hl, const float *hs, const float *hx, int n, int k0,
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(256) void k_encode_act(FwdArgs a, int n_pairs) {
 // staged vector.  No block waits on another: the claims are the only shared
 // state, and the last block to leave resets the counters.
 // ---------------------------------------------------------------------------
-// words of one staged vector of length n: limbs [7][n/8], scales [n/64], half
+// words of one staged vector of length n: limbs [kLimbs][n/8], scales [n/64], half
 // sums [n/32], rounded up to 16 bytes
 MOE_HD int stage_words(int n) { return (kLimbs * (n / 8) + n / 64 + n / 32 + 3) & ~3; }
 
@@ -665,18 +665,39 @@ __global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, StreamPlan pl
 }
 
 // ---------------------------------------------------------------------------
-// k_combine: out = x + sum_k w_k y_k + sigmoid(g_s) y_shared (slot order)
+// k_combine: out = x + sum_k w_k y_k + sigmoid(g_s) y_shared, in slot order
+// (k = 0 .. K, the shared slot last).  A thread takes four outputs; the loads
+// of every slot are issued at once (slot index clamped, the extra terms
+// dropped by a select, not a branch: a load used only under a branch would
+// be sunk into it and wait there, one slot at a time).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_combine(FwdArgs a) {
+__global__ __launch_bounds__(64) void k_combine(FwdArgs a) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
     const int H = a.s.H, K = a.s.K;
     const int t = blockIdx.y;
-    const int o = blockIdx.x * 256 + threadIdx.x;
+    const int o = (blockIdx.x * 64 + threadIdx.x) * 4;
     if (o >= H) return;
     const float *c = a.ws.coef + (size_t)t * (K + 1);
     const float *ys = a.ws.ys + (size_t)t * (K + 1) * H + o;
-    float acc = a.x[(size_t)t * H + o];
-    for (int k = 0; k <= K; ++k) acc = fmaf(c[k], ys[(size_t)k * H], acc);
-    a.y[(size_t)t * H + o] = acc;
+    f32x4 acc = *(const f32x4 *)(a.x + (size_t)t * H + o);
+    f32x4 v[kMaxTopK + 1];
+    float w[kMaxTopK + 1];
+#pragma unroll
+    for (int k = 0; k <= kMaxTopK; ++k) {
+        const int kk = k <= K ? k : K;
+        v[k] = *(const f32x4 *)(ys + (size_t)kk * H);
+        w[k] = c[kk];
+    }
+#pragma unroll
+    for (int k = 0; k <= kMaxTopK; ++k) {
+        f32x4 r;
+        r.x = fmaf(w[k], v[k].x, acc.x);
+        r.y = fmaf(w[k], v[k].y, acc.y);
+        r.z = fmaf(w[k], v[k].z, acc.z);
+        r.w = fmaf(w[k], v[k].w, acc.w);
+        acc = k <= K ? r : acc;
+    }
+    *(f32x4 *)(a.y + (size_t)t * H + o) = acc;
 }
 
 // row-slots per wave and step of k_grouped_stream: two register sets of
@@ -816,7 +837,7 @@ hipError_t launch_grouped_bits(const FwdArgs &a, int stage, hipStream_t st) {
             break;
         }
         case 6:
-            hipLaunchKernelGGL(k_combine, dim3((unsigned)((H + 255) / 256), (unsigned)T), dim3(256), 0, st, a);
+            hipLaunchKernelGGL(k_combine, dim3((unsigned)((H / 4 + 63) / 64), (unsigned)T), dim3(64), 0, st, a);
             break;
         default: return hipErrorInvalidValue;
     }

@@ -23,14 +23,14 @@ struct Workspace {
     int32_t *sel;    // [T][K]   selected experts
     float *coef;     // [T][K+1] combine coefficients (renormalised weights, sigmoid(gs))
     float *act;      // [T][K+1][F] SwiGLU activations of the selected experts and the shared one
-    int8_t *hl;      // [T][7][H/8] dwords: base-16 limbs of the fixed-point normalised tokens
+    int8_t *hl;      // [T][kLimbs][H/8] dwords: base-16 limbs of the fixed-point normalised tokens
     float *hs;       // [T][H/64]  group scales (powers of two) of the limbs
     float *hx;       // [T][H/32]  sums of h over each half group
     // batched (grouped-by-expert) path
     int32_t *grp;    // [4 + 3 * (G + 1) + T*K]: n_touched, then expert, first slot and count of
                      // each touched expert, then the assignments t*K+k sorted by (expert, token)
     float *ys;       // [T][K+1][H] per-slot expert outputs
-    int8_t *al;      // [T][K+1][7][F/8] dwords: limbs of the activations, in the down codes' order
+    int8_t *al;      // [T][K+1][kLimbs][F/8] dwords: limbs of the activations, in the down codes' order
     float *as;       // [T][K+1][F/64] group scales of those limbs
     float *ax;       // [T][K+1][F/32] sums of the activations over each half group
     uint16_t *hb;    // h = hi + mid + lo in bf16, the router GEMM's operand, in fragment order:
@@ -94,12 +94,12 @@ inline size_t workspace_bytes(const Shape &s, int T) {
     b += align_up((size_t)T * s.K * 4);
     b += align_up((size_t)T * (s.K + 1) * 4);
     b += align_up((size_t)T * (s.K + 1) * s.F * 4);
-    b += align_up((size_t)T * 4 * s.H);  // 7 limbs x H/2 bytes fit in 4 H
+    b += align_up((size_t)T * 4 * s.H);  // kLimbs (<= 8) limbs x H/2 bytes fit in 4 H
     b += align_up((size_t)T * (s.H / 64) * 4);
     b += align_up((size_t)T * (s.H / 32) * 4);
     b += align_up(grouped_ints(s, T) * 4);
     b += align_up((size_t)T * (s.K + 1) * s.H * 4);
-    b += align_up((size_t)T * (s.K + 1) * 4 * s.F);  // 7 limbs x F/2 bytes fit in 4 F
+    b += align_up((size_t)T * (s.K + 1) * 4 * s.F);  // kLimbs (<= 8) limbs x F/2 bytes fit in 4 F
     b += align_up((size_t)T * (s.K + 1) * (s.F / 64) * 4);
     b += align_up((size_t)T * (s.K + 1) * (s.F / 32) * 4);
     b += align_up((size_t)token_tiles(T) * 32 * 3 * s.H * 2);

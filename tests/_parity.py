@@ -73,6 +73,7 @@ def check_token(out, idx, w, ref: Dict, K: int, what: str = "", unit_scale: bool
     e2 = rel_l2(out, ref["out"])
     ea = float(np.max(np.abs(np.asarray(out, np.float64) - ref["out"])))
     scale = max(1.0, float(np.sqrt(np.mean(np.square(ref["out"]))))) if unit_scale else 1.0
+    log(f"{what}: rel-L2 {e2:.2e}, max-abs {ea:.2e}")
     assert e2 <= REL_L2 and ea <= MAX_ABS * scale, f"{what}: rel-L2 {e2:.3e}, max-abs {ea:.3e} (scale {scale:.3g})"
     return True
 
