@@ -60,6 +60,41 @@ __device__ __forceinline__ int wave_excl_scan(int v) {
     return incl - v;
 }
 
+// exclusive prefix sums of NV values per thread over a block of NT threads
+// (thread order); tot receives the block totals.  s_tmp: NT / 64 * NV ints.
+template <int NV, int NT>
+__device__ __forceinline__ void block_excl_scan(int (&v)[NV], int (&tot)[NV], int *s_tmp) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) incl[j] = v[j];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int u = __shfl_up(incl[j], o, 64);
+            if (lane >= o) incl[j] += u;
+        }
+    }
+    if (lane == 63) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) s_tmp[wave * NV + j] = incl[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        int pre = 0, t = 0;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) {
+            const int x = s_tmp[w * NV + j];
+            pre += w < wave ? x : 0;
+            t += x;
+        }
+        v[j] = pre + incl[j] - v[j];
+        tot[j] = t;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // routing of every token and grouping of assignments by expert
 // ---------------------------------------------------------------------------
@@ -113,41 +148,11 @@ __device__ __forceinline__ int passes_of(int c, int tp, float inv_tp) {
     return q + (q * tp < c ? 1 : 0);
 }
 
+// s_pp[launch][e]: first pass of expert e (the scan in group_assignments)
 __device__ void build_passes(const FwdArgs &a, const StreamPlan &P0, const StreamPlan &P1, const int *s_cnt,
-                             const int *s_off, const int *s_pv) {
+                             const int *s_off, const int *s_pv, const int (*s_pp)[kMaxExperts]) {
     constexpr int NT = kGroupThreads;
     const int T = a.T, E = a.s.E, K = a.s.K;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    __shared__ int s_pp[2][kMaxExperts];  // first pass of each touched expert, per launch
-    // waves 0 and 1: exclusive scan of the passes per expert for launch 0 and 1
-    // (E <= 1024: 16 per lane)
-    if (wave < 2) {
-        const StreamPlan &P = wave == 0 ? P0 : P1;
-        const int tp = P.tp;
-        const float inv = 1.0f / (float)tp;
-        int32_t *head = a.ws.sched + (size_t)wave * sched_launch_ints(T, K);
-        constexpr int kPer = kMaxExperts / 64;
-        int c[kPer];
-        int sum = 0;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int e = lane * kPer + i;
-            c[i] = (e < E) ? passes_of(s_cnt[e], tp, inv) : 0;
-            sum += c[i];
-        }
-        int pre = wave_excl_scan(sum) + passes_of(T, tp, inv);
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int e = lane * kPer + i;
-            if (e < E) s_pp[wave][e] = pre;
-            pre += c[i];
-        }
-        if (lane == 63) {
-            head[0] = pre;
-            head[1] = pre * P.rpp;
-        }
-    }
-    __syncthreads();
     // records: thread x takes (launch, shared pass or expert) items
     for (int launch = 0; launch < 2; ++launch) {
         const int tp = launch == 0 ? P0.tp : P1.tp;
@@ -178,8 +183,8 @@ __device__ void build_passes(const FwdArgs &a, const StreamPlan &P0, const Strea
 
 // grouping of all T*K assignments by expert, by one block of 1024 threads:
 // histogram, exclusive scans, the compact list of touched experts, and a
-// stable scatter (token order kept inside each expert); then the work
-// partitions of the two streaming launches
+// stable scatter (token order kept inside each expert); then the pass
+// records of the two streaming launches
 
 __device__ void group_assignments(const FwdArgs &a, const StreamPlan &p0, const StreamPlan &p1) {
     constexpr int NT = kGroupThreads;
@@ -198,36 +203,39 @@ __device__ void group_assignments(const FwdArgs &a, const StreamPlan &p0, const 
     __shared__ int s_tch[kMaxExperts];
     __shared__ uint32_t s_mask[kMaxExperts];
     __shared__ int s_pv[kGroupMaxAssign];
+    __shared__ int s_pp[2][kMaxExperts];  // first pass of each expert, per streaming launch
+    __shared__ int s_scan[NT / 64 * 4];
 
     for (int i = threadIdx.x; i < E; i += NT) s_cnt[i] = 0;
     for (int i = threadIdx.x; i < TK; i += NT) s_sel[i] = a.ws.sel[i];
     __syncthreads();
     for (int i = threadIdx.x; i < TK; i += NT) atomicAdd(&s_cnt[s_sel[i]], 1);
     __syncthreads();
-    // exclusive scans of the counts and of the touched flags (E <= 1024: 16 per lane)
-    if (wave == 0) {
-        constexpr int kPer = kMaxExperts / 64;
-        int c[kPer];
-        int sc = 0, sf = 0;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int e = lane * kPer + i;
-            c[i] = (e < E) ? s_cnt[e] : 0;
-            sc += c[i];
-            sf += c[i] > 0 ? 1 : 0;
+    // one block-wide exclusive scan over the experts (thread e holds expert e,
+    // E <= 1024): assignment counts, touched flags and the passes of the two
+    // streaming launches
+    {
+        static_assert(kMaxExperts <= NT, "one expert per thread");
+        const int n_sh0 = (T + p0.tp - 1) / p0.tp, n_sh1 = (T + p1.tp - 1) / p1.tp;
+        const int e = threadIdx.x;
+        const int c = e < E ? s_cnt[e] : 0;
+        int v[4] = {c, c > 0 ? 1 : 0, passes_of(c, p0.tp, 1.0f / (float)p0.tp), passes_of(c, p1.tp, 1.0f / (float)p1.tp)};
+        int tot[4];
+        block_excl_scan<4, NT>(v, tot, s_scan);
+        if (e < E) {
+            s_off[e] = v[0];
+            s_tch[e] = v[1];
+            s_pp[0][e] = n_sh0 + v[2];
+            s_pp[1][e] = n_sh1 + v[3];
         }
-        int pc = wave_excl_scan(sc), pf = wave_excl_scan(sf);
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int e = lane * kPer + i;
-            if (e < E) {
-                s_off[e] = pc;
-                s_tch[e] = pf;
-            }
-            pc += c[i];
-            pf += c[i] > 0 ? 1 : 0;
+        if (threadIdx.x == 0) {
+            a.ws.grp[0] = tot[1];  // number of touched experts
+            int32_t *h0 = a.ws.sched, *h1 = a.ws.sched + sched_launch_ints(T, K);
+            h0[0] = n_sh0 + tot[2];
+            h0[1] = (n_sh0 + tot[2]) * p0.rpp;
+            h1[0] = n_sh1 + tot[3];
+            h1[1] = (n_sh1 + tot[3]) * p1.rpp;
         }
-        if (lane == 63) a.ws.grp[0] = pf;  // number of touched experts
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += NT) {
@@ -259,7 +267,7 @@ __device__ void group_assignments(const FwdArgs &a, const StreamPlan &p0, const 
         __syncthreads();
     }
     // s_off[e] now ends expert e's assignments: its first is s_off[e] - s_cnt[e]
-    build_passes(a, p0, p1, s_cnt, s_off, s_pv);
+    build_passes(a, p0, p1, s_cnt, s_off, s_pv, s_pp);
 }
 
 // ---------------------------------------------------------------------------
