@@ -64,6 +64,8 @@ def parse_args():
     p.add_argument("--workload", default="layer4", choices=["layer4", "layer2", "batch32", "tiny"])
     p.add_argument("--layers", type=int, default=32, help="resident layers the steps rotate over")
     p.add_argument("--pool", type=int, default=1024, help="distinct tokens the steps rotate over")
+    p.add_argument("--tokens", type=int, default=0,
+                   help="tokens per step (0: the workload's own; other values are for batch-size sweeps)")
     p.add_argument("--mode", default="graph", choices=["graph", "api"],
                    help="graph: the timed steps are one captured HIP graph; api: one ABI call per step")
     p.add_argument("--cpu-sample", type=int, default=24, help="tokens for the oracle CPU baseline (0: skip)")
@@ -97,7 +99,7 @@ def main():
 
     wl = syn.WORKLOADS[args.workload]
     dims = wl.dims
-    T = wl.n_tokens
+    T = args.tokens if args.tokens > 0 else wl.n_tokens
     K = dims.top_k
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
@@ -222,7 +224,7 @@ def main():
     dom = max(kbytes, key=lambda k: stage_mean[k])
     achieved = kbytes[dom] / stage_mean[dom]
     traffic = None
-    tr = KERNEL_TRAFFIC.get((wl.name, names[dom]))
+    tr = KERNEL_TRAFFIC.get((wl.name, names[dom])) if T == wl.n_tokens else None
     if tr is not None and tr["source_sha256_prefix"] == kernel_source_hash(grouped)[:16]:
         traffic = round((tr["fetch_kib"] * tr["fetch_scale"] + tr["write_kib"] * tr["write_scale"]) * 1024)
 
@@ -240,7 +242,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{wl.name}: {wl.description}",
+            "workload": f"{wl.name}: {wl.description}" if T == wl.n_tokens else
+                        f"{wl.name} shape at {T} tokens per step: {wl.description}",
             "hidden": dims.hidden, "ffn": dims.ffn, "n_experts": dims.n_experts, "top_k": K,
             "bits": dims.bits, "group_size": dims.group_size, "tokens_per_step": T,
             "resident_layers": R, "token_pool": P, "mode": args.mode,
