@@ -133,8 +133,9 @@ __device__ __forceinline__ void token_logits(const FwdArgs &a, int t, float (&zv
 // ---------------------------------------------------------------------------
 // pass records of the two streaming launches (0: gate/up, 1: down), written by
 // the grouping block: the shared expert over token chunks of tp first (the
-// heaviest passes start first), then every touched expert over chunks of tp of
-// its assignments (token order), in expert order.  s_pv holds the assignments
+// heaviest passes start first; none when the launch runs the shared expert on
+// the matrix cores), then every touched expert over chunks of tp of its
+// assignments (token order), in expert order.  s_pv holds the assignments
 // sorted by (expert, token) as output indices t * (K+1) + slot.
 // ---------------------------------------------------------------------------
 constexpr int kGroupThreads = 1024;
@@ -155,9 +156,10 @@ __device__ void build_passes(const FwdArgs &a, const StreamPlan &P0, const Strea
     const int T = a.T, E = a.s.E, K = a.s.K;
     // records: thread x takes (launch, shared pass or expert) items
     for (int launch = 0; launch < 2; ++launch) {
-        const int tp = launch == 0 ? P0.tp : P1.tp;
+        const StreamPlan &P = launch == 0 ? P0 : P1;
+        const int tp = P.tp;
         int32_t *rec = a.ws.sched + (size_t)launch * sched_launch_ints(T, K) + 4;
-        const int n_shared = (T + tp - 1) / tp;
+        const int n_shared = P.n_mfma > 0 ? 0 : (T + tp - 1) / tp;
         for (int x = threadIdx.x; x < n_shared + E; x += NT) {
             if (x < n_shared) {
                 int32_t *r = rec + (size_t)x * kPassRecord;
@@ -216,7 +218,8 @@ __device__ void group_assignments(const FwdArgs &a, const StreamPlan &p0, const 
     // streaming launches
     {
         static_assert(kMaxExperts <= NT, "one expert per thread");
-        const int n_sh0 = (T + p0.tp - 1) / p0.tp, n_sh1 = (T + p1.tp - 1) / p1.tp;
+        const int n_sh0 = p0.n_mfma > 0 ? 0 : (T + p0.tp - 1) / p0.tp;
+        const int n_sh1 = p1.n_mfma > 0 ? 0 : (T + p1.tp - 1) / p1.tp;
         const int e = threadIdx.x;
         const int c = e < E ? s_cnt[e] : 0;
         int v[4] = {c, c > 0 ? 1 : 0, passes_of(c, p0.tp, 1.0f / (float)p0.tp), passes_of(c, p1.tp, 1.0f / (float)p1.tp)};
@@ -232,9 +235,9 @@ __device__ void group_assignments(const FwdArgs &a, const StreamPlan &p0, const 
             a.ws.grp[0] = tot[1];  // number of touched experts
             int32_t *h0 = a.ws.sched, *h1 = a.ws.sched + sched_launch_ints(T, K);
             h0[0] = n_sh0 + tot[2];
-            h0[1] = (n_sh0 + tot[2]) * p0.rpp;
+            h0[1] = p0.n_mfma + (n_sh0 + tot[2]) * p0.rpp;
             h1[0] = n_sh1 + tot[3];
-            h1[1] = (n_sh1 + tot[3]) * p1.rpp;
+            h1[1] = p1.n_mfma + (n_sh1 + tot[3]) * p1.rpp;
         }
     }
     __syncthreads();
@@ -353,19 +356,77 @@ __device__ __forceinline__ void load_limb_slice(const uint32_t *hl, const float 
 //          each nibble) are dotted with limb dwords 2w and 2w+1, which put
 //          k = 16w + (n >> 1) + 4 p + 8 (n & 1) in nibble n (p = 0, 1).
 // ---------------------------------------------------------------------------
+// sks > 0: the shared expert's gate and up sums arrive as sks partial sums
+// of matrix-core units over reduction chunks, and its down product runs on
+// the matrix cores too: blocks past pair_blocks add the partials in chunk
+// order, apply SwiGLU and write that slot's bf16 fragments and half-group
+// sums (a thread per 4 values, every partial's load issued at once); the
+// pair blocks skip the slot.
+__device__ __forceinline__ void shared_act(const FwdArgs &a, int sks, int b) {
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    const int F = a.s.F, K = a.s.K, T = a.T;
+    const int gt = b * 256 + threadIdx.x;
+    const int t = gt / (F / 4), k0 = (gt % (F / 4)) * 4;
+    if (t >= T) return;  // whole groups of 8 lanes (F / 4 is a multiple of 8)
+    f32x4v q[kMaxMfmaKsplit][2];
+#pragma unroll
+    for (int kc = 0; kc < kMaxMfmaKsplit; ++kc)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            q[kc][m] = *(const f32x4v *)(a.ws.sp + ((size_t)((kc < sks ? kc : 0) * 2 + m) * T + t) * F + k0);
+    f32x4v g = q[0][0], u = q[0][1];
+#pragma unroll
+    for (int kc = 1; kc < kMaxMfmaKsplit; ++kc) {
+        g = kc < sks ? g + q[kc][0] : g;
+        u = kc < sks ? u + q[kc][1] : u;
+    }
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = g[i] * u[i] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[i]));
+    // fragments: values k0 .. k0+3 of token t, three bf16 parts
+    uint16_t *f = a.ws.ab + ((size_t)(t >> 5) * (F / 16) + k0 / 16) * 3 * 512 + ((t & 31) + 32 * ((k0 % 16) / 8)) * 8 +
+                  (k0 % 8);
+    float r[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+        uint32_t w[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t lo = bf16_rne_bits(r[2 * i]), hi = bf16_rne_bits(r[2 * i + 1]);
+            w[i] = lo | (hi << 16);
+            r[2 * i] -= __uint_as_float(lo << 16);
+            r[2 * i + 1] -= __uint_as_float(hi << 16);
+        }
+        *(uint2 *)(f + p * 512) = make_uint2(w[0], w[1]);
+    }
+    // half-group sums: 8 threads of 4 values
+    float sum = (v[0] + v[1]) + (v[2] + v[3]);
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    sum += __shfl_xor(sum, 4, 64);
+    if ((k0 & 31) == 0) a.ws.ax[((size_t)t * (K + 1) + K) * (F / 32) + k0 / 32] = sum;
+}
+
 template <int BITS>
-__global__ __launch_bounds__(256) void k_encode_act(FwdArgs a, int n_pairs) {
-    const int F = a.s.F;
+__global__ __launch_bounds__(256) void k_encode_act(FwdArgs a, int n_pairs, int sks, int pair_blocks) {
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    if (BITS == 4 && (int)blockIdx.x >= pair_blocks) {
+        shared_act(a, sks, blockIdx.x - pair_blocks);
+        return;
+    }
+    const int F = a.s.F, K = a.s.K;
     const int tpp = F / 16;  // threads per pair (a multiple of 8)
     const int p = blockIdx.x * (256 / tpp) + threadIdx.x / tpp;
     const int u = threadIdx.x % tpp;
-    const bool live = p < n_pairs;
+    const bool live = p < n_pairs && !(sks > 0 && p % (K + 1) == K);
     float v[16];
-    const float *src = a.ws.act + (size_t)(live ? p : 0) * F + 16 * u;
+    {
+        const f32x4v *src = (const f32x4v *)(a.ws.act + (size_t)(p < n_pairs ? p : 0) * F + 16 * u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float4 q = *(const float4 *)(src + 4 * i);
-        v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+        for (int i = 0; i < 4; ++i) {
+            const f32x4v q = src[i];
+            v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+        }
     }
     float m = 0.0f, sum = 0.0f;
 #pragma unroll
@@ -401,6 +462,8 @@ __global__ __launch_bounds__(256) void k_encode_act(FwdArgs a, int n_pairs) {
         for (int x = 0; x < kLimbs; ++x) *(uint2 *)(al + (size_t)x * (F / 8)) = make_uint2(pk[x][0], pk[x][1]);
         if ((u & 1) == 0) a.ws.ax[(size_t)p * (F / 32) + u / 2] = sum;
         if ((u & 3) == 0) a.ws.as[(size_t)p * (F / 64) + u / 4] = limb_scale(m);
+        // the shared slot also as bf16 fragments, the operand of its matrix-core down product
+        if (BITS == 4 && p % (K + 1) == K) store_split_fragments(a.ws.ab, F, p / (K + 1), u, v);  // sks == 0
     }
 }
 
@@ -446,6 +509,188 @@ struct StreamRun {
     int pass, rs_lo, rs_hi, nsteps;
 };
 
+// ---------------------------------------------------------------------------
+// The shared expert on the matrix cores (4-bit codes).  Every token of the
+// batch uses it, so it is a dense product [rows x n] x [n x T].  A unit is 128
+// rows (32 per wave) by one tile of 32 tokens over the whole reduction, on
+// v_mfma_f32_32x32x16_bf16: the codes enter as 16 + q, exact in bf16; the
+// activations as their three bf16 parts (hi, mid, lo; written in fragment
+// order by k_norm_batch and k_encode_act); the fp32 product C of each group
+// of 64 is folded as s * C + (b - 16 s) * sum(v).  The block stages every
+// group's fragments, per-row scale s and offset b - 16 s, and per-token sums
+// in a ring of three LDS buffers, two groups ahead.
+// Lane layouts of the 32x32x16 product: A lane l holds row l % 32 and the
+// step's reduction entries 8 (l / 32) .. +7; B lane l holds those entries of
+// token l % 32; result v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4,
+// token l % 32.  A lane loads the 16-byte chunk (32 codes) of its row that
+// covers half l / 32 of the group; one v_permlane32_swap per two dwords gives
+// each lane the 8-code dword of every step.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaFrag = 12 * 64;     // 16-byte fragments of a group: 4 steps x 3 parts x 64 lanes
+constexpr int kMfmaMinTokens = 32;     // smaller batches keep the shared expert in passes (a half-empty tile measured slower)
+MOE_HD int mfma_buf_words(bool down) { return kMfmaFrag * 4 + (down ? 1 : 2) * 256 + 32; }
+MOE_HD int mfma_lds_bytes(bool down) { return 3 * mfma_buf_words(down) * 4; }
+
+// the 8 codes of a dword as bf16 values 16 + q in reduction order (4 dwords,
+// value 2j in the low half of dword j): one byte-select and one shift-or per
+// two codes.  Nibble order: code j in nibble j; byte order: code j in byte
+// j % 4 at bit 4 (j / 4).
+template <bool BYTE_CODES>
+__device__ __forceinline__ u32x4v codes_bf16(uint32_t d) {
+    const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;
+    u32x4v r;
+    if constexpr (BYTE_CODES) {
+        r.x = __builtin_amdgcn_perm(hi, lo, 0x0C010C00u);
+        r.y = __builtin_amdgcn_perm(hi, lo, 0x0C030C02u);
+        r.z = __builtin_amdgcn_perm(hi, lo, 0x0C050C04u);
+        r.w = __builtin_amdgcn_perm(hi, lo, 0x0C070C06u);
+    } else {
+        r.x = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u);
+        r.y = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u);
+        r.z = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u);
+        r.w = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u);
+    }
+    return (r << 3u) | 0x41804180u;  // bf16(16 + q) = 0x4180 | q << 3
+}
+
+// unit = (token tile, row block, reduction chunk), the chunk fastest; with
+// ks > 1 chunks the unit writes fp32 partial sums (gate/up only), which
+// k_encode_act adds in chunk order
+template <bool DOWN>
+__device__ void shared_mfma_unit(const FwdArgs &a, int unit, int ks, uint32_t *lds) {
+    constexpr int NM = DOWN ? 1 : 2;
+    constexpr int NSB = NM * 128;  // scale/bias words of a group: NM matrices x 128 rows
+    const int H = a.s.H, F = a.s.F, K = a.s.K, T = a.T;
+    const int n = DOWN ? F : H, rows = DOWN ? H : F;
+    const int nrb = rows / 128, gpu = (n / 64) / ks;  // groups per unit (>= 2)
+    const int kc = unit % ks, rt = unit / ks;
+    const int tt = rt / nrb, rb = rt - tt * nrb;
+    const int g0 = kc * gpu, ng = g0 + gpu;  // the unit's groups: g0 .. ng-1
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+    const int row = rb * 128 + wave * 32 + (lane & 31);
+    const QMat &M0 = a.L.m[DOWN ? 2 : 0];
+    const QMat &M1 = a.L.m[1];
+    const u32x4v *frag = (const u32x4v *)(DOWN ? a.ws.ab : a.ws.hb) + (size_t)tt * (n / 16) * 3 * 64;
+    const int bw = mfma_buf_words(DOWN);
+    // staging of group g, loads: fragments i, i+256, i+512 of thread i; the
+    // scale/bias word of row i % NSB (a thread past NSB re-reads row i % NSB);
+    // the group sum of token i % 32 (clamped to the batch)
+    auto stage_load = [&](int g, u32x4v (&fp)[3], uint32_t &sbw, float &xs) {
+        const u32x4v *src = frag + (size_t)g * kMfmaFrag;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) fp[j] = src[threadIdx.x + 256 * j];
+        const int i = threadIdx.x & (NSB - 1);
+        const QMat &M = (i >> 7) ? M1 : M0;
+        sbw = ld_stream4((const uint32_t *)(a.shared + M.sb_off) + (size_t)(rb * 128 + (i & 127)) * M.ngroups + g);
+        const int tok = tt * 32 + (threadIdx.x & 31);
+        const int tc = tok < T ? tok : T - 1;
+        const float *hx = DOWN ? a.ws.ax + (size_t)(tc * (K + 1) + K) * (F / 32) : a.ws.hx + (size_t)tc * (H / 32);
+        xs = hx[2 * g] + hx[2 * g + 1];
+    };
+    // stores (every index in range: duplicate writers store equal values)
+    auto stage_store = [&](int g, const u32x4v (&fp)[3], uint32_t sbw, float xs) {
+        uint32_t *buf = lds + (g % 3) * bw;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) ((u32x4v *)buf)[threadIdx.x + 256 * j] = fp[j];
+        const float sc = bf16_lo(sbw);
+        float *so = (float *)(buf + kMfmaFrag * 4) + 2 * (threadIdx.x & (NSB - 1));
+        so[0] = sc;
+        so[1] = fmaf(-16.0f, sc, bf16_hi(sbw));
+        ((float *)buf)[kMfmaFrag * 4 + 2 * NSB + (threadIdx.x & 31)] = xs;
+    };
+    // the lane's code chunk of group g: logical chunk 2 g + half of its row
+    auto load_codes = [&](int g, uint4 (&ac)[NM]) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const QMat &M = m ? M1 : M0;
+            const int L = 2 * g + half;
+            ac[m] = ld_stream16(a.shared + M.codes_off + (size_t)row * M.row_bytes + 16 * (L / M.cpl + M.lpr * (L % M.cpl)));
+        }
+    };
+
+    f32x16_t acc[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[m] = f32x16_t{};
+    {
+        u32x4v fp[3];
+        uint32_t sbw;
+        float xs;
+        stage_load(g0, fp, sbw, xs);
+        stage_store(g0, fp, sbw, xs);
+        stage_load(g0 + 1, fp, sbw, xs);  // at least two groups per unit
+        stage_store(g0 + 1, fp, sbw, xs);
+    }
+    uint4 ac[NM];
+    load_codes(g0, ac);
+    for (int g = g0; g < ng; ++g) {
+        lds_barrier();  // group g's buffer is complete; group g - 1's is free
+        // group g + 2 into the freed buffer (past the end: the last group again,
+        // into a buffer no later group reads), the next group's codes
+        const int g2 = g + 2 < ng ? g + 2 : ng - 1;
+        u32x4v fp[3];
+        uint32_t sbw;
+        float xs;
+        stage_load(g2, fp, sbw, xs);
+        uint4 an[NM];
+        load_codes(g + 1 < ng ? g + 1 : g, an);
+        const uint32_t *buf = lds + (g % 3) * bw;
+        const u32x4v *bf = (const u32x4v *)buf;
+        const float X = ((const float *)buf)[kMfmaFrag * 4 + 2 * NSB + (lane & 31)];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const auto p01 = __builtin_amdgcn_permlane32_swap(ac[m].x, ac[m].y, false, false);
+            const auto p23 = __builtin_amdgcn_permlane32_swap(ac[m].z, ac[m].w, false, false);
+            const uint32_t dw[4] = {p01[0], p23[0], p01[1], p23[1]};  // the dword of steps 0 .. 3
+            f32x16_t c = f32x16_t{};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const bf16x8_t av = __builtin_bit_cast(bf16x8_t, codes_bf16<DOWN>(dw[st]));
+#pragma unroll
+                for (int p = 2; p >= 0; --p)
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, bf[(st * 3 + p) * 64 + lane]),
+                                                                c, 0, 0, 0);
+            }
+            // fold: rows 8 j + 4 half + i of the wave's 32, (s, b - 16 s) pairs
+            const float *so = (const float *)(buf + kMfmaFrag * 4) + 2 * (m * 128 + wave * 32 + 4 * half);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x4v q0 = *(const u32x4v *)(so + 16 * j);
+                const u32x4v q1 = *(const u32x4v *)(so + 16 * j + 4);
+                const float sv[4] = {__uint_as_float(q0.x), __uint_as_float(q0.z), __uint_as_float(q1.x),
+                                     __uint_as_float(q1.z)};
+                const float ov[4] = {__uint_as_float(q0.y), __uint_as_float(q0.w), __uint_as_float(q1.y),
+                                     __uint_as_float(q1.w)};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[m][4 * j + i] = fmaf(sv[i], c[4 * j + i], fmaf(ov[i], X, acc[m][4 * j + i]));
+            }
+        }
+        stage_store(g2, fp, sbw, xs);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) ac[m] = an[m];
+    }
+    const int tok = tt * 32 + (lane & 31);
+    if (tok < T) {
+        const size_t pv = (size_t)tok * (K + 1) + K;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int r = rb * 128 + wave * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+            if constexpr (DOWN) {
+                a.ws.ys[pv * H + r] = acc[0][v];
+            } else if (ks > 1) {
+                a.ws.sp[((size_t)(kc * 2 + 0) * T + tok) * F + r] = acc[0][v];
+                a.ws.sp[((size_t)(kc * 2 + 1) * T + tok) * F + r] = acc[1][v];
+            } else {
+                const float g = acc[0][v];
+                a.ws.act[pv * F + r] = g * acc[1][v] * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+            }
+        }
+    }
+}
+
 // LPR: lanes per row when the partial sums of a step are reduced together
 // (16, 32 or 64); 0: any other width, one reduction per row
 template <int BITS, int CPL, int RPW, bool DOWN, int LPR>
@@ -459,6 +704,7 @@ __global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, StreamPlan pl
     uint32_t *s_vec = (uint32_t *)s_dyn;
     __shared__ int s_out[kMaxPassVectors];  // output vector index (t * (K+1) + slot) per staged vector
     __shared__ int s_next;                    // the run claimed for after the next one
+    __shared__ int s_first;                   // after a matrix-core unit: the first streaming run
     const int H = a.s.H, F = a.s.F, K = a.s.K, E = a.s.E;
     const int n = DOWN ? F : H;  // reduction length
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -479,8 +725,11 @@ __global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, StreamPlan pl
     const int nb = (int)gridDim.x;
     const int n_runs = sv.head[1];
 
+    // runs 0 .. n_mfma-1 are matrix-core units of the shared expert; run r
+    // after them is run r - n_mfma of the passes
     auto run_of = [&](int r) {
         StreamRun R;
+        r -= plan.n_mfma;
         R.pass = r / plan.rpp;
         const int b0 = (r - R.pass * plan.rpp) * plan.run_items;
         const int b1 = min(plan.nbs, b0 + plan.run_items);
@@ -614,7 +863,21 @@ __global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, StreamPlan pl
         if (r < n_runs) claim = atomicAdd(run_ctr, 1u);
     };
     int cur_r = blockIdx.x;
-    if (cur_r < n_runs) {
+    if constexpr (BITS == 4) {
+        // matrix-core units first: a block's claims come in increasing order,
+        // so every unit precedes every streaming run
+        while (cur_r >= 0 && cur_r < plan.n_mfma) {
+            shared_mfma_unit<DOWN>(a, cur_r, plan.mfma_ks, s_vec);
+            if (threadIdx.x == 0) {
+                claim = atomicAdd(run_ctr, 1u);
+                const int r = nb + kClaimGroups * (int)claim + grp;
+                s_first = r < n_runs ? r : -1;
+            }
+            lds_barrier();  // the unit is done with LDS; s_first visible
+            cur_r = s_first;
+        }
+    }
+    if (cur_r >= 0 && cur_r < n_runs) {
         if (threadIdx.x == 0) claim = atomicAdd(run_ctr, 1u);
         StreamRun cur = run_of(cur_r);
         W w0, w1;
@@ -774,7 +1037,26 @@ struct StreamOp {
         p.nbs = (nrs + 4 * rpw - 1) / (4 * rpw);
         p.run_items = DOWN ? kDownRunItems : kGateUpRunItems;
         p.rpp = (p.nbs + p.run_items - 1) / p.run_items;
-        const size_t lds = (size_t)p.tp * stage_words(n) * 4;
+        size_t lds = (size_t)p.tp * stage_words(n) * 4;
+        p.n_mfma = 0;
+        p.mfma_ks = 1;
+        if (BITS == 4 && a->T >= kMfmaMinTokens) {
+            // the shared expert on the matrix cores: one unit per 128 rows and
+            // 32-token tile, each a block's first run
+            const size_t lds_m = lds > (size_t)mfma_lds_bytes(DOWN) ? lds : (size_t)mfma_lds_bytes(DOWN);
+            // gate/up: chunks of 8 groups (a unit's groups run one after the
+            // other, each waiting on HBM: 64 in a row made the units the
+            // critical path); down: the whole reduction (16 groups at F = 1024).
+            // The split depends on the shape only, so that a token's result
+            // does not depend on its batch.
+            const int ng = n / 64;
+            const int ks = DOWN ? 1 : (ng > 8 ? ng / 8 : 1);
+            if (ks <= kMaxMfmaKsplit) {
+                p.n_mfma = token_tiles(a->T) * (M.rows / 128) * ks;
+                p.mfma_ks = ks;
+                lds = lds_m;
+            }
+        }
         const hipError_t e = stream_block_slots((const void *)fn, lds, p.nb);
         if (e != hipSuccess) return e;
         p.nb = (p.nb + kClaimGroups - 1) / kClaimGroups * kClaimGroups;
@@ -838,10 +1120,16 @@ hipError_t launch_grouped_bits(const FwdArgs &a, int stage, hipStream_t st) {
             break;
         }
         case 4: {
+            StreamPlan p0;
+            const hipError_t e = stream_op<BITS>(a, false, false, st, p0);
+            if (e != hipSuccess) return e;
+            const int sks = (p0.n_mfma > 0 && p0.mfma_ks > 1) ? p0.mfma_ks : 0;
             const int n_pairs = T * (K + 1);
             const int ppb = 256 / (F / 16);
-            hipLaunchKernelGGL(k_encode_act<BITS>, dim3((unsigned)((n_pairs + ppb - 1) / ppb)), dim3(256), 0, st, a,
-                               n_pairs);
+            const int pair_blocks = (n_pairs + ppb - 1) / ppb;
+            const int shared_blocks = sks > 0 ? (T * (F / 4) + 255) / 256 : 0;
+            hipLaunchKernelGGL(k_encode_act<BITS>, dim3((unsigned)(pair_blocks + shared_blocks)), dim3(256), 0, st, a,
+                               n_pairs, sks, pair_blocks);
             break;
         }
         case 6:

@@ -36,6 +36,10 @@ struct Workspace {
     uint16_t *hb;    // h = hi + mid + lo in bf16, the router GEMM's operand, in fragment order:
                      // [ceil(T/32)][H/16][3][64 lanes][8] (see k_norm_batch)
     float *zp;       // [KS][T][E+1] partial router logits (column E: shared gate), KS = router_ksplit(H)
+    float *sp;       // [kMaxMfmaKsplit][2][T][F] partial gate and up sums of the shared expert's
+                     // matrix-core units (one per reduction chunk)
+    uint16_t *ab;    // the shared expert's activations a = hi + mid + lo in bf16, fragment order
+                     // [ceil(T/32)][F/16][3][64 lanes][8] (the shared down product's operand)
     int32_t *sched;  // passes of the two streaming launches (gate/up, down), each
                      // sched_launch_ints(T, K) ints: head, then kPassRecord ints per pass
 };
@@ -70,7 +74,10 @@ struct StreamPlan {
     int run_items;  // block-steps per run
     int rpp;        // runs per pass, ceil(nbs / run_items)
     int nb;         // blocks of the persistent grid
+    int n_mfma;     // matrix-core units of the shared expert (runs 0 .. n_mfma-1; then it has no passes)
+    int mfma_ks;    // reduction chunks per unit row block and token tile (> 1: partial sums in sp)
 };
+constexpr int kMaxMfmaKsplit = 8;
 // Run claims go through kClaimGroups counters (block b uses counter b % G and
 // claims the runs r = b mod G), so that no single address takes every claim;
 // each counter sits in its own 256-byte line of the control block, after the
@@ -104,6 +111,8 @@ inline size_t workspace_bytes(const Shape &s, int T) {
     b += align_up((size_t)T * (s.K + 1) * (s.F / 32) * 4);
     b += align_up((size_t)token_tiles(T) * 32 * 3 * s.H * 2);
     b += align_up((size_t)router_ksplit(s.H) * T * (s.E + 1) * 4);
+    b += align_up((size_t)kMaxMfmaKsplit * 2 * T * s.F * 4);
+    b += align_up((size_t)token_tiles(T) * 32 * 3 * s.F * 2);
     b += align_up((size_t)2 * sched_launch_ints(T, s.K) * 4);
     return b;
 }
@@ -145,6 +154,10 @@ inline Workspace carve_workspace(void *base, const Shape &s, int T) {
     p += align_up((size_t)token_tiles(T) * 32 * 3 * s.H * 2);
     w.zp = (float *)p;
     p += align_up((size_t)router_ksplit(s.H) * T * (s.E + 1) * 4);
+    w.sp = (float *)p;
+    p += align_up((size_t)kMaxMfmaKsplit * 2 * T * s.F * 4);
+    w.ab = (uint16_t *)p;
+    p += align_up((size_t)token_tiles(T) * 32 * 3 * s.F * 2);
     w.sched = (int32_t *)p;
     return w;
 }
