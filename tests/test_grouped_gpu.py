@@ -95,12 +95,14 @@ def test_stages_rerun(moe):
 
 
 def test_batch_independence_up_to_largest_batch(moe):
-    """400 tokens with top-10 (4000 assignments, near the grouped path's limit
+    """384 tokens with top-10 (3840 assignments, near the grouped path's limit
     of 4096): each token's output equals the one it gets in 32-token batches,
-    bit for bit; sampled tokens match the oracle."""
+    bit for bit; sampled tokens match the oracle.  (Batches of 32 tokens or
+    more run the shared expert on the matrix cores, smaller ones in limb
+    passes: equal within rounding, not bit for bit.)"""
     w = syn.WORKLOADS["batch32"]
     dims = w.dims
-    T = 400
+    T = 384
     log(f"batch of {T}: {dims}")
     lw = _layer(dims, w.seed, 0)
     x = syn.tokens(14, T, dims.hidden)
@@ -111,7 +113,7 @@ def test_batch_independence_up_to_largest_batch(moe):
     for t0 in range(0, T, 32):
         part, _, _ = run_layer(dims, lw, x[t0:t0 + 32])
         assert np.array_equal(big[t0:t0 + 32], part), f"tokens {t0}..{t0 + len(part) - 1}"
-    for t in (0, 31, 32, 200, 399):
+    for t in (0, 31, 32, 200, 383):
         ref = oracle_layer_generated(dims, w.seed, 0, x[t])
         check_token(big[t], idx[t], wt[t], ref, dims.top_k, f"batch {T} token {t}")
 
