@@ -293,6 +293,78 @@ __device__ __forceinline__ void route_wave(const float (&zv)[EPL], int E, int K,
     my_w = p / denom;
 }
 
+// The K largest of the wave's keys (N per lane, 0 = no key): lane k < K ends
+// with the k-th (0 when the wave holds fewer).  Same rounds as route_wave.
+template <int N>
+__device__ __forceinline__ uint64_t wave_top_keys(uint64_t (&key)[N], int K) {
+    const int lane = threadIdx.x & 63;
+    sort_desc<N>(key);
+    uint64_t mine = 0;
+    for (int k = 0; k < K; ++k) {
+        const uint32_t hi = (uint32_t)(key[0] >> 32), lo = (uint32_t)key[0];
+        const uint32_t m = wave_max_u32(hi);
+        uint64_t cand = __ballot(hi == m);
+        if (__popcll(cand) > 1) {  // exact tie of the high words: the largest low word (lowest index)
+            const uint32_t m2 = wave_max_u32(hi == m ? lo : 0u);
+            cand = __ballot(hi == m && lo == m2);
+        }
+        const int w = __ffsll((unsigned long long)cand) - 1;
+        const uint32_t lo_w = __builtin_amdgcn_readlane(lo, w);
+        const bool win = lane == w;
+#pragma unroll
+        for (int i = 0; i < N - 1; ++i) key[i] = win ? key[i + 1] : key[i];
+        key[N - 1] = win ? 0ull : key[N - 1];
+        if (lane == k) mine = ((uint64_t)m << 32) | lo_w;
+    }
+    return mine;
+}
+
+// Softmax -> top-K -> renormalise by the 4 waves of a block (every thread
+// calls it): each wave selects the K largest keys of its quarter of the
+// logits, z[q] of lane l in wave w being expert e = 256 q + 64 w + l; wave 0
+// selects the K largest of those 4 K candidates.  Lane k < K of wave 0 ends
+// with the k-th selected expert and its weight, as route_wave would.
+// s_cand: 4 * kMaxTopK keys of LDS.
+template <int EPW>
+__device__ __forceinline__ void route_block(const float (&zq)[EPW], int E, int K, uint64_t *s_cand, int &my_sel,
+                                            float &my_w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t key[EPW];
+#pragma unroll
+    for (int q = 0; q < EPW; ++q) {
+        const int e = 256 * q + 64 * wave + lane;
+        key[q] = (e < E) ? route_key(zq[q], e) : 0ull;
+    }
+    const uint64_t best = wave_top_keys<EPW>(key, K);
+    if (lane < K) s_cand[wave * kMaxTopK + lane] = best;
+    __syncthreads();
+    my_sel = 0;
+    my_w = 0.0f;
+    if (wave == 0) {
+        uint64_t c[1] = {lane < 4 * K ? s_cand[(lane / K) * kMaxTopK + lane % K] : 0ull};
+        const uint64_t top = wave_top_keys<1>(c, K);
+        const float my_z = (lane < K) ? route_key_value(top) : 0.0f;
+        my_sel = (int)(~(uint32_t)top);
+        // softmax restricted to the selection == renormalised full softmax
+        const float z0 = lane_bcast(my_z, 0);
+        const float p = (lane < K) ? expf(my_z - z0) : 0.0f;
+        const float denom = lane_sum<64>(p);
+        my_w = p / denom;
+    }
+}
+
+// the logits of one token a block's wave routes: e = 256 q + 64 w + lane
+// (clamped index: all loads in flight at once)
+template <int EPW>
+__device__ __forceinline__ void load_logits_quarter(const float *__restrict__ z, int E, float (&zq)[EPW]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < EPW; ++q) {
+        const int e = 256 * q + 64 * wave + lane;
+        zq[q] = z[e < E ? e : E - 1];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // dequantised dot product of one row slice with a lane's limb slice
 // ---------------------------------------------------------------------------

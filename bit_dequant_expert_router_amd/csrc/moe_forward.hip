@@ -2,7 +2,7 @@
 //
 //   k_router : two-pass RMSNorm + router GEMV (E rows) + shared-gate logit;
 //              a few blocks also store h in the fixed-point limb form below
-//   k_gateup : per wave, softmax/top-K/renormalise from the logits, then the
+//   k_gateup : per block, softmax/top-K/renormalise from the logits, then the
 //              fused gate+up dequant GEMV of the selected experts and the
 //              shared expert with SwiGLU in registers
 //   k_down   : down-projection dequant GEMV of all K+1 experts for a set of
@@ -254,9 +254,12 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
     __shared__ float s_hs[kMaxDim / 64];
     __shared__ float s_hx[kMaxDim / 32];
 
-    // wave 0 routes for the whole block: its logit loads go first (loads complete in order)
-    float zv[EPL];
-    if (block_routed && wave == 0) load_logits<EPL>(a.ws.z + (size_t)t * E, E, zv);
+    // the block's four waves route together, a quarter of the logits each:
+    // their loads go first (loads complete in order)
+    constexpr int EPW = EPL / 4;
+    __shared__ uint64_t s_cand[4 * kMaxTopK];
+    float zq[EPW];
+    if (block_routed) load_logits_quarter<EPW>(a.ws.z + (size_t)t * E, E, zq);
 
     // stage the limb form of h in LDS, once per block
     {
@@ -275,22 +278,24 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
         float hs = 0.0f, hx = 0.0f;
         if (threadIdx.x < H / 64) hs = a.ws.hs[(size_t)t * (H / 64) + threadIdx.x];
         if (threadIdx.x < H / 32) hx = a.ws.hx[(size_t)t * (H / 32) + threadIdx.x];
-        if (block_routed && wave == 0) {
+        if (block_routed) {
             int my_sel;
             float my_w;
-            route_wave<EPL>(zv, E, K, my_sel, my_w);
-            if (lane < K) {
-                s_sel[lane] = my_sel;
-                s_w[lane] = my_w;
-            }
-            if (blockIdx.x == 0) {
+            route_block<EPW>(zq, E, K, s_cand, my_sel, my_w);
+            if (wave == 0) {
                 if (lane < K) {
-                    a.ws.sel[t * K + lane] = my_sel;
-                    a.ws.coef[t * (K + 1) + lane] = my_w;
-                    if (a.route_idx) a.route_idx[t * K + lane] = my_sel;
-                    if (a.route_w) a.route_w[t * K + lane] = my_w;
-                } else if (lane == K) {
-                    a.ws.coef[t * (K + 1) + K] = sigmoidf_(a.ws.gs[t]);
+                    s_sel[lane] = my_sel;
+                    s_w[lane] = my_w;
+                }
+                if (blockIdx.x == 0) {
+                    if (lane < K) {
+                        a.ws.sel[t * K + lane] = my_sel;
+                        a.ws.coef[t * (K + 1) + lane] = my_w;
+                        if (a.route_idx) a.route_idx[t * K + lane] = my_sel;
+                        if (a.route_w) a.route_w[t * K + lane] = my_w;
+                    } else if (lane == K) {
+                        a.ws.coef[t * (K + 1) + K] = sigmoidf_(a.ws.gs[t]);
+                    }
                 }
             }
         }

@@ -10,7 +10,7 @@
 //
 //   k_norm_batch, k_router_mfma (moe_batch_router.hip) RMSNorm, limb and bf16
 //                   forms of h, router logits on the matrix cores
-//   k_route_tokens  one wave per token: softmax/top-K/renormalise
+//   k_route_tokens  one block per token: softmax/top-K/renormalise
 //   k_group         one block: histogram of assignments per expert, exclusive
 //                   scan, stable scatter (token order kept inside each expert)
 //                   and the compact list of touched experts
@@ -98,12 +98,13 @@ __device__ __forceinline__ void block_excl_scan(int (&v)[NV], int (&tot)[NV], in
 // ---------------------------------------------------------------------------
 // routing of every token and grouping of assignments by expert
 // ---------------------------------------------------------------------------
-// logits of token t: the KS partial sums of the router GEMM, every load issued
-// at once, added in a fixed order
+// logits of token t that a wave of its block routes (experts 256 i + 64 w +
+// lane, route_block's layout) and the shared-gate logit: the KS partial sums of
+// the router GEMM, every load issued at once, added in a fixed order
 template <int EPL>
 __device__ __forceinline__ void token_logits(const FwdArgs &a, int t, float (&zv)[EPL], float &gs) {
     const int E = a.s.E, T = a.T, ksn = router_ksplit(a.s.H);
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float *zt = a.ws.zp + (size_t)t * (E + 1);
     const size_t kstride = (size_t)T * (E + 1);
     float z[kMaxKsplit][EPL], g[kMaxKsplit];
@@ -112,7 +113,7 @@ __device__ __forceinline__ void token_logits(const FwdArgs &a, int t, float (&zv
         const float *zk = zt + (size_t)(ks < ksn ? ks : 0) * kstride;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
-            const int e = lane + 64 * i;
+            const int e = 256 * i + 64 * wave + lane;
             z[ks][i] = zk[e < E ? e : E - 1];
         }
         g[ks] = zk[E];
@@ -274,28 +275,32 @@ __device__ void group_assignments(const FwdArgs &a, const StreamPlan &p0, const 
 }
 
 // ---------------------------------------------------------------------------
-// k_route_tokens: one wave per token sums the partial logits and routes
-// (softmax -> top-K -> renormalise).  k_group then groups the assignments of
+// k_route_tokens: one block of four waves per token sums the partial logits of
+// the router GEMM (a quarter of the experts per wave) and routes (softmax ->
+// top-K -> renormalise, route_block).  k_group then groups the assignments of
 // the whole batch in one block.  (A last-block-done counter inside one kernel
 // would need an L2 write-back per block and same-address atomics across the
 // XCDs, both slower here than the kernel boundary.)
 // ---------------------------------------------------------------------------
-template <int EPL>
-__global__ __launch_bounds__(64) void k_route_tokens(FwdArgs a) {
+template <int EPW>
+__global__ __launch_bounds__(256) void k_route_tokens(FwdArgs a) {
     const int t = blockIdx.x, K = a.s.K, E = a.s.E;
-    const int lane = threadIdx.x & 63;
-    float zv[EPL], gs;
-    token_logits<EPL>(a, t, zv, gs);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ uint64_t s_cand[4 * kMaxTopK];
+    float zq[EPW], gs;
+    token_logits<EPW>(a, t, zq, gs);
     int my_sel;
     float my_w;
-    route_wave<EPL>(zv, E, K, my_sel, my_w);
-    if (lane < K) {
-        a.ws.sel[t * K + lane] = my_sel;
-        a.ws.coef[t * (K + 1) + lane] = my_w;
-        if (a.route_idx) a.route_idx[t * K + lane] = my_sel;
-        if (a.route_w) a.route_w[t * K + lane] = my_w;
-    } else if (lane == K) {
-        a.ws.coef[t * (K + 1) + K] = sigmoidf_(gs);
+    route_block<EPW>(zq, E, K, s_cand, my_sel, my_w);
+    if (wave == 0) {
+        if (lane < K) {
+            a.ws.sel[t * K + lane] = my_sel;
+            a.ws.coef[t * (K + 1) + lane] = my_w;
+            if (a.route_idx) a.route_idx[t * K + lane] = my_sel;
+            if (a.route_w) a.route_w[t * K + lane] = my_w;
+        } else if (lane == K) {
+            a.ws.coef[t * (K + 1) + K] = sigmoidf_(gs);
+        }
     }
 }
 
@@ -1106,9 +1111,9 @@ hipError_t launch_grouped_bits(const FwdArgs &a, int stage, hipStream_t st) {
             if (e == hipSuccess) e = stream_op<BITS>(a, true, false, st, p1);
             if (e != hipSuccess) return e;
             if (E > 512)
-                hipLaunchKernelGGL(k_route_tokens<16>, dim3((unsigned)T), dim3(64), 0, st, a);
+                hipLaunchKernelGGL(k_route_tokens<4>, dim3((unsigned)T), dim3(256), 0, st, a);
             else
-                hipLaunchKernelGGL(k_route_tokens<8>, dim3((unsigned)T), dim3(64), 0, st, a);
+                hipLaunchKernelGGL(k_route_tokens<2>, dim3((unsigned)T), dim3(256), 0, st, a);
             hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), 0, st, a, p0, p1);
             break;
         }
