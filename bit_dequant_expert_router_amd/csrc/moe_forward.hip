@@ -397,6 +397,9 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // k_down processes the K+1 slots in batches of at most kDownBatch; a batch's
 // activations and their half-group sums are staged in LDS once per block.
+// Each lane reads the NV consecutive activations of its slice; a pad of 4
+// floats after every slice puts consecutive lanes on consecutive 16-byte bank
+// groups (unpadded, slices 128 or 256 bytes apart share their banks).
 constexpr int kDownBatch = 5;
 constexpr int kDownStageValues = 5120;  // activations staged per batch (batch * F <= this)
 
@@ -426,9 +429,11 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
         xres[i] = a.x[(size_t)t * H + rs * rpi + rsub];
     }
 
+    constexpr int NVP = Q::NV + 4;  // padded slice
+    const int FP = F / Q::NV * NVP;  // padded activations of one slot
     extern __shared__ __align__(16) unsigned char smem[];
-    float *s_act = (float *)smem;              // [batch][F]
-    float *s_half = s_act + (size_t)batch * F;  // [batch][F/32]
+    float *s_act = (float *)smem;               // [batch][F / NV][NVP]
+    float *s_half = s_act + (size_t)batch * FP;  // [batch][F/32]
 
     // lane s (s <= K) holds slot s: expert index (s < K) and combine
     // coefficient; only those lanes are ever read (unconditional loads, lanes
@@ -480,7 +485,8 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
             const int v0 = threadIdx.x * 4 + 1024 * r;
             if (1024 * r < batch * F) {  // uniform: whole 8-thread groups are live or not
                 const bool live = v0 < nb * F;
-                if (live) *(float4 *)(s_act + v0) = stv[r];
+                const int si = v0 / F, j = v0 - si * F;
+                if (live) *(float4 *)(s_act + si * FP + j / Q::NV * NVP + j % Q::NV) = stv[r];
                 const float4 v = stv[r];
                 const float half = lane_sum<8>((v.x + v.y) + (v.z + v.w));  // 8 threads = 32 values
                 if (live && (threadIdx.x & 7) == 0) s_half[v0 / 32] = half;
@@ -496,7 +502,7 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
                     float av[Q::NV];
 #pragma unroll
                     for (int i = 0; i < Q::NV / 4; ++i) {
-                        const float4 v = *(const float4 *)(s_act + (size_t)si * F + k0 + 4 * i);
+                        const float4 v = *(const float4 *)(s_act + si * FP + lr * NVP + 4 * i);
                         av[4 * i] = v.x; av[4 * i + 1] = v.y; av[4 * i + 2] = v.z; av[4 * i + 3] = v.w;
                     }
                     float X[Q::NGL];
@@ -589,7 +595,8 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
         const int nrs = H / rpi;
         const int blocks = (nrs + 4 * kRpwDown - 1) / (4 * kRpwDown);
         dim3 grid(blocks, T);
-        const size_t per_slot = (size_t)F * 4 + (size_t)(F / 32) * 4;
+        // padded activations (4 floats per lane slice) and half-group sums
+        const size_t per_slot = (size_t)(F + 4 * Dm.lpr) * 4 + (size_t)(F / 32) * 4;
         int batch = kDownStageValues / F;
         if (batch > kDownBatch) batch = kDownBatch;
         if (batch > K + 1) batch = K + 1;
