@@ -684,7 +684,11 @@ __device__ __forceinline__ float qdot_f32(const uint4 (&c)[CPL], const uint32_t 
         for (int w4 = 0; w4 < 4; ++w4) {
 #pragma unroll
             for (int n = 0; n < NS; ++n) {
-                const uint32_t m = d[w4] & (Q::kByteMask << (BITS * n));
+                uint32_t m = d[w4] & (Q::kByteMask << (BITS * n));
+                // opaque from here: byte b of m then converts with
+                // v_cvt_f32_ubyte{b} (seen through, each code would be
+                // narrowed to a bit-field extract plus a conversion)
+                asm("" : "+v"(m));
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const int i = j * Q::C + w4 * Q::D + 4 * n + b;

@@ -408,7 +408,7 @@ constexpr int kDownStageValues = 5120;  // activations staged per batch (batch *
 // ONE: all K+1 slots in a single batch (straight-line code: no loop-header
 // wait holds back the first loads)
 template <int BITS, int CPL, int RPW, int LPR, bool ONE>
-__global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
+__global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_recip) {
     using Q = QSlice<BITS, CPL>;
     const int t = blockIdx.y;
     const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K;
@@ -420,6 +420,7 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
     const int rs0 = (blockIdx.x * 4 + wave) * RPW;
     const bool active = rs0 < nrs;
     const int k0 = lr * Q::NV;
+    const uint32_t F4 = F / 4;
 
     // the residual of the rows this lane may write, fetched now
     float xres[RPW];
@@ -454,14 +455,20 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
         // every load below is unconditional (indices past the end are
         // clamped to valid ones and their results unused), so that all of
         // them are in flight before the first wait
+        // float4 piece p = tid + 256 r: slot p / (F/4) by a multiply-high
+        // with f4_recip = ceil(2^32 / (F/4)) (exact: p (F/4) < 2^32)
         float4 stv[kStageMax];
+        uint32_t sti[kStageMax], stj[kStageMax];
+        const float *act_t = a.ws.act + (size_t)t * (K + 1) * F;
 #pragma unroll
         for (int r = 0; r < kStageMax; ++r) {
-            const int v0 = threadIdx.x * 4 + 1024 * r;
-            const int vc = v0 < nb * F ? v0 : 0;
-            const int si = vc / F, j = vc % F;
-            const int s = (b0 + si == 0) ? K : b0 + si - 1;
-            stv[r] = *(const float4 *)(a.ws.act + ((size_t)t * (K + 1) + s) * F + j);
+            const uint32_t p = threadIdx.x + 256 * r;
+            const uint32_t pc = p < (uint32_t)(nb * F4) ? p : 0u;
+            const uint32_t si = __umulhi(pc, f4_recip), j = (pc - __umul24(si, F4)) * 4;
+            const uint32_t s = (b0 + si == 0) ? K : b0 + si - 1;
+            sti[r] = si;
+            stj[r] = j;
+            stv[r] = *(const float4 *)(act_t + (__umul24(s, (uint32_t)F) + j));
         }
         // weights of up to kDownBatch slots of this batch, all in flight together
         uint4 wc[kDownBatch][RPW][CPL];
@@ -485,7 +492,7 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
             const int v0 = threadIdx.x * 4 + 1024 * r;
             if (1024 * r < batch * F) {  // uniform: whole 8-thread groups are live or not
                 const bool live = v0 < nb * F;
-                const int si = v0 / F, j = v0 - si * F;
+                const uint32_t si = sti[r], j = stj[r];
                 if (live) *(float4 *)(s_act + si * FP + j / Q::NV * NVP + j % Q::NV) = stv[r];
                 const float4 v = stv[r];
                 const float half = lane_sum<8>((v.x + v.y) + (v.z + v.w));  // 8 threads = 32 values
@@ -545,11 +552,13 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch) {
 }
 
 constexpr int kRpwGateUp = 2;
-constexpr int kRpwDown = 2;
+constexpr int kRpwDown4 = 2;  // 4-bit codes
+constexpr int kRpwDown2 = 1;  // 2-bit codes
 
 template <int BITS>
 hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
     const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K, T = a.T;
+    constexpr int RD = BITS == 4 ? kRpwDown4 : kRpwDown2;  // down row-steps per wave
     if (stage == 0 && (H == 2048 || H == 4096)) {  // RMSNorm + router + limbs of h, H split over 4 waves
         const int rows = (E + 1 + kRouterSplitRows - 1) / kRouterSplitRows;
         const int blocks = rows > H / 256 ? rows : H / 256;
@@ -593,7 +602,7 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
         const QMat &Dm = a.L.m[2];
         const int rpi = 64 / Dm.lpr;
         const int nrs = H / rpi;
-        const int blocks = (nrs + 4 * kRpwDown - 1) / (4 * kRpwDown);
+        const int blocks = (nrs + 4 * RD - 1) / (4 * RD);
         dim3 grid(blocks, T);
         // padded activations (4 floats per lane slice) and half-group sums
         const size_t per_slot = (size_t)(F + 4 * Dm.lpr) * 4 + (size_t)(F / 32) * 4;
@@ -603,20 +612,21 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
         if (batch < 1) batch = 1;
         const size_t lds = per_slot * batch;
         const bool one = K + 1 <= batch;
+        const uint32_t f4r = (uint32_t)((0x100000000ull + F / 4 - 1) / (F / 4));
         if (Dm.cpl == 2) {
-            if (one) hipLaunchKernelGGL((k_down<BITS, 2, kRpwDown, 64, true>), grid, dim3(256), lds, st, a, batch);
-            else hipLaunchKernelGGL((k_down<BITS, 2, kRpwDown, 64, false>), grid, dim3(256), lds, st, a, batch);
+            if (one) hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, true>), grid, dim3(256), lds, st, a, batch, f4r);
+            else hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, false>), grid, dim3(256), lds, st, a, batch, f4r);
         } else if (Dm.cpl == 1) {
             const int key = (Dm.lpr == 64 ? 0 : Dm.lpr == 32 ? 1 : Dm.lpr == 16 ? 2 : 3) * 2 + (one ? 1 : 0);
             switch (key) {
-                case 0: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 64, false>), grid, dim3(256), lds, st, a, batch); break;
-                case 1: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 64, true>), grid, dim3(256), lds, st, a, batch); break;
-                case 2: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 32, false>), grid, dim3(256), lds, st, a, batch); break;
-                case 3: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 32, true>), grid, dim3(256), lds, st, a, batch); break;
-                case 4: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 16, false>), grid, dim3(256), lds, st, a, batch); break;
-                case 5: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 16, true>), grid, dim3(256), lds, st, a, batch); break;
-                case 6: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 0, false>), grid, dim3(256), lds, st, a, batch); break;
-                default: hipLaunchKernelGGL((k_down<BITS, 1, kRpwDown, 0, true>), grid, dim3(256), lds, st, a, batch); break;
+                case 0: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, false>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                case 1: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, true>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                case 2: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, false>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                case 3: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, true>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                case 4: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, false>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                case 5: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, true>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                case 6: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, false>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                default: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, true>), grid, dim3(256), lds, st, a, batch, f4r); break;
             }
         } else {
             return hipErrorInvalidValue;
