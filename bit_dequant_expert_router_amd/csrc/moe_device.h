@@ -249,52 +249,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
-// Softmax -> top-K -> renormalise by one wave.  Each lane sorts its EPL keys
-// (logit order in the high word, the complemented index in the low word).
-// Every round takes the wave maximum of the heads' high words; the lane
-// holding it (one ballot bit, or after an exact tie the largest low word,
-// i.e. the lowest index) pops its head.  Lane k < K ends with the k-th
-// selected expert and its weight.
-template <int EPL>
-__device__ __forceinline__ void route_wave(const float (&zv)[EPL], int E, int K, int &my_sel, float &my_w) {
-    const int lane = threadIdx.x & 63;
-    uint64_t key[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane + 64 * i;
-        key[i] = (e < E) ? route_key(zv[i], e) : 0ull;
-    }
-    sort_desc<EPL>(key);
-    my_sel = 0;
-    float my_z = 0.0f;
-    for (int k = 0; k < K; ++k) {
-        const uint32_t hi = (uint32_t)(key[0] >> 32), lo = (uint32_t)key[0];
-        const uint32_t m = wave_max_u32(hi);
-        uint64_t cand = __ballot(hi == m);
-        if (__popcll(cand) > 1) {  // exact tie of logits: the lowest index wins
-            const uint32_t m2 = wave_max_u32(hi == m ? lo : 0u);
-            cand = __ballot(hi == m && lo == m2);
-        }
-        const int w = __ffsll((unsigned long long)cand) - 1;
-        const uint32_t lo_w = __builtin_amdgcn_readlane(lo, w);
-        const bool win = lane == w;
-#pragma unroll
-        for (int i = 0; i < EPL - 1; ++i) key[i] = win ? key[i + 1] : key[i];
-        key[EPL - 1] = win ? 0ull : key[EPL - 1];
-        if (lane == k) {
-            my_sel = (int)(~lo_w);
-            my_z = route_key_value(((uint64_t)m << 32) | lo_w);
-        }
-    }
-    // softmax restricted to the selection == renormalised full softmax
-    const float z0 = lane_bcast(my_z, 0);
-    const float p = (lane < K) ? expf(my_z - z0) : 0.0f;
-    const float denom = lane_sum<64>(p);
-    my_w = p / denom;
-}
-
-// The K largest of the wave's keys (N per lane, 0 = no key): lane k < K ends
-// with the k-th (0 when the wave holds fewer).  Same rounds as route_wave.
+// The K largest of the wave's keys (logit order in the high word, the
+// complemented index in the low word; N per lane, 0 = no key).  Each lane
+// sorts its keys; every round takes the wave maximum of the heads' high
+// words, and the lane holding it (one ballot bit, or after an exact tie the
+// largest low word, i.e. the lowest index) pops its head.  Lane k < K ends
+// with the k-th (0 when the wave holds fewer).
 template <int N>
 __device__ __forceinline__ uint64_t wave_top_keys(uint64_t (&key)[N], int K) {
     const int lane = threadIdx.x & 63;
@@ -319,15 +279,15 @@ __device__ __forceinline__ uint64_t wave_top_keys(uint64_t (&key)[N], int K) {
     return mine;
 }
 
-// Softmax -> top-K -> renormalise by the 4 waves of a block (every thread
-// calls it): each wave selects the K largest keys of its quarter of the
-// logits, z[q] of lane l in wave w being expert e = 256 q + 64 w + l; wave 0
-// selects the K largest of those 4 K candidates.  Lane k < K of wave 0 ends
-// with the k-th selected expert and its weight, as route_wave would.
-// s_cand: 4 * kMaxTopK keys of LDS.
+// Softmax -> top-K -> renormalise by the 4 waves of a block, in two steps
+// around a block barrier that the caller places.
+//
+// route_candidates: each wave selects the K largest keys of its quarter of
+// the logits (z[q] of lane l in wave w is expert e = 256 q + 64 w + l) and
+// stores them at s_cand[w K + k] (s_cand: 4 * kMaxTopK keys of LDS, 16-byte
+// aligned).
 template <int EPW>
-__device__ __forceinline__ void route_block(const float (&zq)[EPW], int E, int K, uint64_t *s_cand, int &my_sel,
-                                            float &my_w) {
+__device__ __forceinline__ void route_candidates(const float (&zq)[EPW], int E, int K, uint64_t *s_cand) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint64_t key[EPW];
 #pragma unroll
@@ -336,21 +296,56 @@ __device__ __forceinline__ void route_block(const float (&zq)[EPW], int E, int K
         key[q] = (e < E) ? route_key(zq[q], e) : 0ull;
     }
     const uint64_t best = wave_top_keys<EPW>(key, K);
-    if (lane < K) s_cand[wave * kMaxTopK + lane] = best;
-    __syncthreads();
-    my_sel = 0;
-    my_w = 0.0f;
-    if (wave == 0) {
-        uint64_t c[1] = {lane < 4 * K ? s_cand[(lane / K) * kMaxTopK + lane % K] : 0ull};
-        const uint64_t top = wave_top_keys<1>(c, K);
-        const float my_z = (lane < K) ? route_key_value(top) : 0.0f;
-        my_sel = (int)(~(uint32_t)top);
-        // softmax restricted to the selection == renormalised full softmax
-        const float z0 = lane_bcast(my_z, 0);
-        const float p = (lane < K) ? expf(my_z - z0) : 0.0f;
-        const float denom = lane_sum<64>(p);
-        my_w = p / denom;
+    if (lane < K) s_cand[wave * K + lane] = best;
+}
+
+// route_select, after the barrier, in any wave: lane i < 4K takes candidate i
+// and counts the candidates above it.  The keys of experts are distinct and
+// nonzero (absent ones are 0), so the candidates of rank k < K are the K
+// largest logits in selection order, without further rounds.  The weights
+// are the softmax restricted to the selection, which equals the full softmax
+// renormalised over it.  rank == K marks a lane outside the selection.
+struct RouteSel {
+    int rank;
+    int sel;
+    float w;
+};
+
+__device__ __forceinline__ RouteSel route_select(int K, const uint64_t *s_cand) {
+    const int lane = threadIdx.x & 63, n = 4 * K;
+    const uint64_t mine = s_cand[lane < n ? lane : 0];
+    int above = 0;
+    // 8 keys per step, read together (s_cand holds 64; n is a multiple of 4,
+    // so only the upper half of a step can lie past n: read and ignored)
+    for (int j0 = 0; j0 < n; j0 += 8) {
+        uint64_t c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = s_cand[j0 + u];
+        int lo = 0, hi = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            lo += c[u] > mine ? 1 : 0;
+            hi += c[u + 4] > mine ? 1 : 0;
+        }
+        above += lo + (j0 + 4 < n ? hi : 0);
     }
+    const bool in = lane < n && above < K;
+    const float z = in ? route_key_value(mine) : 0.0f;
+    // the candidate of rank 0 holds the largest logit
+    const uint64_t top = __ballot(in && above == 0);
+    const float zmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), __ffsll((unsigned long long)top) - 1));
+    const float p = in ? expf(z - zmax) : 0.0f;
+    RouteSel r;
+    r.rank = in ? above : K;
+    r.sel = (int)(~(uint32_t)mine);
+    r.w = p / lane_sum<64>(p);
+    return r;
+}
+
+// the expert selected for slot s (wave-uniform, s < K)
+__device__ __forceinline__ int routed_expert(const RouteSel &r, int s) {
+    const uint64_t b = __ballot(r.rank == s);
+    return __builtin_amdgcn_readlane(r.sel, __ffsll((unsigned long long)b) - 1);
 }
 
 // the logits of one token a block's wave routes: e = 256 q + 64 w + lane

@@ -248,18 +248,18 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
     const bool block_routed = (blockIdx.x * 4 * RPW * rpi) / F < K;
     const bool wave_shared_only = (rs0 * rpi) / F >= K;
 
-    __shared__ int s_sel[kMaxTopK];
-    __shared__ float s_w[kMaxTopK];
     __shared__ __align__(16) uint32_t s_hl[kLimbs * kMaxDim / 8];  // limbs of h, [kLimbs][H/8]
     __shared__ float s_hs[kMaxDim / 64];
     __shared__ float s_hx[kMaxDim / 32];
 
-    // the block's four waves route together, a quarter of the logits each:
-    // their loads go first (loads complete in order)
+    // the block's four waves route together, a quarter of the logits each
+    // (route_candidates, then route_select after the block's barrier): the
+    // logit loads go first (loads complete in order)
     constexpr int EPW = EPL / 4;
-    __shared__ uint64_t s_cand[4 * kMaxTopK];
+    __shared__ __align__(16) uint64_t s_cand[4 * kMaxTopK];
     float zq[EPW];
     if (block_routed) load_logits_quarter<EPW>(a.ws.z + (size_t)t * E, E, zq);
+    const float gs = a.ws.gs[t];  // shared-gate logit (block 0 writes its coefficient)
 
     // stage the limb form of h in LDS, once per block
     {
@@ -278,27 +278,7 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
         float hs = 0.0f, hx = 0.0f;
         if (threadIdx.x < H / 64) hs = a.ws.hs[(size_t)t * (H / 64) + threadIdx.x];
         if (threadIdx.x < H / 32) hx = a.ws.hx[(size_t)t * (H / 32) + threadIdx.x];
-        if (block_routed) {
-            int my_sel;
-            float my_w;
-            route_block<EPW>(zq, E, K, s_cand, my_sel, my_w);
-            if (wave == 0) {
-                if (lane < K) {
-                    s_sel[lane] = my_sel;
-                    s_w[lane] = my_w;
-                }
-                if (blockIdx.x == 0) {
-                    if (lane < K) {
-                        a.ws.sel[t * K + lane] = my_sel;
-                        a.ws.coef[t * (K + 1) + lane] = my_w;
-                        if (a.route_idx) a.route_idx[t * K + lane] = my_sel;
-                        if (a.route_w) a.route_w[t * K + lane] = my_w;
-                    } else if (lane == K) {
-                        a.ws.coef[t * (K + 1) + K] = sigmoidf_(a.ws.gs[t]);
-                    }
-                }
-            }
-        }
+        if (block_routed) route_candidates<EPW>(zq, E, K, s_cand);
         {
             i32x4 *dst = (i32x4 *)s_hl;
 #pragma unroll
@@ -317,7 +297,8 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
     // every row's loads unconditional (rows past the end re-read the last
     // row), so that they are all in flight before the first wait
     // (addresses first, then every load back to back)
-    auto issue_loads = [&]() {
+    // er[i]: the expert of row-step i when its slot is routed
+    auto issue_loads = [&](const int (&er)[RPW]) {
         const uint8_t *exr[RPW];
         int jr[RPW];
 #pragma unroll
@@ -326,7 +307,7 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
             const int p = rs * rpi + rsub;
             const int s = p / F;
             jr[i] = p - s * F;
-            exr[i] = (s < K) ? a.experts + (size_t)s_sel[s < K ? s : 0] * a.L.bytes : a.shared;
+            exr[i] = (s < K) ? a.experts + (size_t)er[i] * a.L.bytes : a.shared;
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -336,10 +317,33 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    if (active && wave_shared_only) issue_loads();
+    if (active && wave_shared_only) {
+        const int none[RPW] = {};
+        issue_loads(none);
+    }
     __syncthreads();
     if (!active) return;
-    if (!wave_shared_only) issue_loads();
+    if (!wave_shared_only) {
+        // every routed wave ranks the block's candidates itself
+        const RouteSel rt = route_select(K, s_cand);
+        if (blockIdx.x == 0 && wave == 0) {
+            if (rt.rank < K) {
+                a.ws.sel[t * K + rt.rank] = rt.sel;
+                a.ws.coef[t * (K + 1) + rt.rank] = rt.w;
+                if (a.route_idx) a.route_idx[t * K + rt.rank] = rt.sel;
+                if (a.route_w) a.route_w[t * K + rt.rank] = rt.w;
+            }
+            if (lane == 0) a.ws.coef[t * (K + 1) + K] = sigmoidf_(gs);
+        }
+        int er[RPW];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int rs = rs0 + i < nrs ? rs0 + i : nrs - 1;
+            const int s = (rs * rpi) / F;  // uniform: a row-step's rows share their slot
+            er[i] = routed_expert(rt, s < K ? s : K - 1);
+        }
+        issue_loads(er);
+    }
 
     // codes prepared once, then every row against the lane's limb slice of h
     // in LDS, limb-major

@@ -99,7 +99,7 @@ __device__ __forceinline__ void block_excl_scan(int (&v)[NV], int (&tot)[NV], in
 // routing of every token and grouping of assignments by expert
 // ---------------------------------------------------------------------------
 // logits of token t that a wave of its block routes (experts 256 i + 64 w +
-// lane, route_block's layout) and the shared-gate logit: the KS partial sums of
+// lane, route_candidates' layout) and the shared-gate logit: the KS partial sums of
 // the router GEMM, every load issued at once, added in a fixed order
 template <int EPL>
 __device__ __forceinline__ void token_logits(const FwdArgs &a, int t, float (&zv)[EPL], float &gs) {
@@ -277,7 +277,7 @@ __device__ void group_assignments(const FwdArgs &a, const StreamPlan &p0, const 
 // ---------------------------------------------------------------------------
 // k_route_tokens: one block of four waves per token sums the partial logits of
 // the router GEMM (a quarter of the experts per wave) and routes (softmax ->
-// top-K -> renormalise, route_block).  k_group then groups the assignments of
+// top-K -> renormalise, route_candidates and route_select).  k_group then groups the assignments of
 // the whole batch in one block.  (A last-block-done counter inside one kernel
 // would need an L2 write-back per block and same-address atomics across the
 // XCDs, both slower here than the kernel boundary.)
@@ -286,21 +286,20 @@ template <int EPW>
 __global__ __launch_bounds__(256) void k_route_tokens(FwdArgs a) {
     const int t = blockIdx.x, K = a.s.K, E = a.s.E;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    __shared__ uint64_t s_cand[4 * kMaxTopK];
+    __shared__ __align__(16) uint64_t s_cand[4 * kMaxTopK];
     float zq[EPW], gs;
     token_logits<EPW>(a, t, zq, gs);
-    int my_sel;
-    float my_w;
-    route_block<EPW>(zq, E, K, s_cand, my_sel, my_w);
+    route_candidates<EPW>(zq, E, K, s_cand);
+    __syncthreads();
     if (wave == 0) {
-        if (lane < K) {
-            a.ws.sel[t * K + lane] = my_sel;
-            a.ws.coef[t * (K + 1) + lane] = my_w;
-            if (a.route_idx) a.route_idx[t * K + lane] = my_sel;
-            if (a.route_w) a.route_w[t * K + lane] = my_w;
-        } else if (lane == K) {
-            a.ws.coef[t * (K + 1) + K] = sigmoidf_(gs);
+        const RouteSel rt = route_select(K, s_cand);
+        if (rt.rank < K) {
+            a.ws.sel[t * K + rt.rank] = rt.sel;
+            a.ws.coef[t * (K + 1) + rt.rank] = rt.w;
+            if (a.route_idx) a.route_idx[t * K + rt.rank] = rt.sel;
+            if (a.route_w) a.route_w[t * K + rt.rank] = rt.w;
         }
+        if (lane == 0) a.ws.coef[t * (K + 1) + K] = sigmoidf_(gs);
     }
 }
 
