@@ -119,7 +119,8 @@ def test_batch_independence_up_to_largest_batch(moe):
 
 
 def test_many_experts_grouped(moe):
-    """1024 experts (the routing wave's 16-per-lane path) on the grouped path."""
+    """1024 experts (four logits per lane in each routing wave) on the grouped
+    path, and tokens 0-1 on the per-token path."""
     from bit_dequant_expert_router_amd.weights import layer_from_canonical
     import oracle
     dims = syn.Dims(256, 128, 1024, 8, 4)
@@ -128,6 +129,25 @@ def test_many_experts_grouped(moe):
     lw = layer_from_canonical(dims, dense, experts)
     x = syn.tokens(15, 12, dims.hidden)
     out, idx, wt = run_layer(dims, lw, x)
+    refs = [oracle.layer_all(dims, x[t], dense, experts) for t in range(x.shape[0])]
     for t in range(x.shape[0]):
-        check_token(out[t], idx[t], wt[t], oracle.layer_all(dims, x[t], dense, experts), dims.top_k,
-                    f"1024 experts token {t}")
+        check_token(out[t], idx[t], wt[t], refs[t], dims.top_k, f"1024 experts token {t}")
+    out, idx, wt = run_layer(dims, lw, x[:2])
+    for t in range(2):
+        check_token(out[t], idx[t], wt[t], refs[t], dims.top_k, f"1024 experts per-token path, token {t}")
+
+
+def test_ragged_token_tile_full_size(moe):
+    """45 tokens at the batched shape: the shared expert's second 32-token
+    matrix-core tile holds 13 tokens; sampled tokens of both tiles against the
+    oracle."""
+    w = syn.WORKLOADS["batch32"]
+    dims = w.dims
+    T = 45
+    log(f"batch of {T}: {dims}")
+    lw = _layer(dims, w.seed, 3)
+    x = syn.tokens(16, T, dims.hidden)
+    out, idx, wt = run_layer(dims, lw, x)
+    for t in (0, 31, 32, 40, 44):
+        ref = oracle_layer_generated(dims, w.seed, 3, x[t])
+        check_token(out[t], idx[t], wt[t], ref, dims.top_k, f"batch {T} token {t}")

@@ -69,15 +69,21 @@ SMALL_SHAPES = [
 
 @pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_small_shapes(moe, shape):
+    """Five tokens through the grouped kernels, then tokens 0-2 and 3 through
+    the per-token kernels (batches of 1 to 3 tokens)."""
     H, F, E, K, bits = shape
     dims = syn.Dims(H, F, E, K, bits)
     log(f"small shape {shape}")
     dense, experts, lw = _canonical_layer(dims, seed=3, layer=1)
     x = syn.tokens(3, 5, H)
+    refs = [oracle.layer_all(dims, x[t], dense, experts) for t in range(x.shape[0])]
     out, idx, wt = run_layer(dims, lw, x)
     for t in range(x.shape[0]):
-        ref = oracle.layer_all(dims, x[t], dense, experts)
-        check_token(out[t], idx[t], wt[t], ref, K, f"{shape} token {t}")
+        check_token(out[t], idx[t], wt[t], refs[t], K, f"{shape} token {t}")
+    for t0, t1 in ((0, 3), (3, 4)):
+        out, idx, wt = run_layer(dims, lw, x[t0:t1])
+        for t in range(t0, t1):
+            check_token(out[t - t0], idx[t - t0], wt[t - t0], refs[t], K, f"{shape} per-token path, token {t}")
 
 
 @pytest.mark.parametrize("n_tokens", [1, 3, 6, 40])  # ungrouped (1, 3) and grouped (6, 40)
