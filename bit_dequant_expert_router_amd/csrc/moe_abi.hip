@@ -63,7 +63,7 @@ size_t workspace_bytes_checked(const moe_dims_t *dims, int32_t n_tokens) {
     return workspace_bytes(shape_of(dims), n_tokens);
 }
 
-// batches of kGroupMinTokens or more tokens are grouped by expert
+// batches of kGroupMinAssign to kGroupMaxAssign assignments are grouped by expert
 hipError_t launch_layer(const FwdArgs &a, hipStream_t stream) {
     if (uses_grouped(a.s, a.T)) return launch_grouped(a, stream);
     return launch_forward(a, stream);

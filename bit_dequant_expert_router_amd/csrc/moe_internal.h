@@ -180,12 +180,20 @@ struct FwdArgs {
 };
 
 constexpr int kForwardStages = 3;
-// batches of at least this many tokens (and at most kGroupMaxAssign assignments)
-// take the grouped-by-expert path
-constexpr int kGroupMinTokens = 4;
+// Batches of at least kGroupMinAssign assignments (tokens x top-K) and at most
+// kGroupMaxAssign take the grouped-by-expert path; smaller batches run the
+// per-token kernels, one row of blocks per token.  On the 4096/1024/512-expert
+// shape the per-token kernels are ahead up to 64 assignments with top-4 and 70
+// with top-10 (the grouped path's seven launches and its grouping cost more than
+// re-reading the few experts two tokens share), the grouped path from 96 and
+// 120; at 80 the two are within 3%.
+constexpr int kGroupMinAssign = 80;
 constexpr int kGroupMaxAssign = 4096;
 constexpr int kGroupedStages = 7;
-inline bool uses_grouped(const Shape &s, int T) { return T >= kGroupMinTokens && T * s.K <= kGroupMaxAssign; }
+inline bool uses_grouped(const Shape &s, int T) {
+    const long a = (long)T * s.K;
+    return a >= kGroupMinAssign && a <= kGroupMaxAssign;
+}
 hipError_t launch_grouped(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_grouped_stage(const FwdArgs &a, int stage, hipStream_t stream);
 // batched RMSNorm (stage 0) and router GEMM (stage 1) of the grouped path

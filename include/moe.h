@@ -151,10 +151,11 @@ int moe_generate_layer(const moe_dims_t *dims, uint64_t seed, uint32_t layer, vo
                        void *shared_expert, void *stream);
 
 /*
- * One MoE layer for n_tokens tokens.  A single token (or up to 3) runs three
- * kernels per layer; batches of 4 or more tokens (with n_tokens * top_k <= 4096)
- * are grouped by expert so that every selected expert's weights are read once
- * for all of its tokens.  Both give the same results up to fp32 rounding order.
+ * One MoE layer for n_tokens tokens.  Batches of fewer than 80 assignments
+ * (n_tokens * top_k < 80) run three kernels per layer, one row of blocks per
+ * token; batches of 80 to 4096 assignments are grouped by expert so that every
+ * selected expert's weights are read once for all of its tokens (larger ones run
+ * the per-token kernels).  Both give the same results up to fp32 rounding order.
  *   x          fp32 [n_tokens][H] device, 16-B aligned (may equal y: in place)
  *   y          fp32 [n_tokens][H] device, 16-B aligned: x + routed combine + gated shared
  *   route_idx  int32 [n_tokens][K] device or NULL: selected experts, ordered by
@@ -175,7 +176,7 @@ int moe_layer_forward(const moe_dims_t *dims, const moe_layer_t *layer, const fl
  * n_tokens (moe_forward_stage_count gives their number); enqueued in order
  * 0, 1, ... with identical arguments (same workspace, stream order) they
  * produce exactly what moe_layer_forward produces.
- * Per-token path (fewer than 4 tokens, 3 stages): 0 RMSNorm, router GEMV and
+ * Per-token path (3 stages): 0 RMSNorm, router GEMV and
  * shared-gate logit; 1 softmax/top-K/renormalise and the fused gate+up dequant
  * GEMV with SwiGLU for the selected and the shared experts; 2 down projection
  * with the weighted combine, sigmoid-gated shared expert and residual.

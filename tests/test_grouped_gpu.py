@@ -119,15 +119,17 @@ def test_batch_independence_up_to_largest_batch(moe):
 
 
 def test_many_experts_grouped(moe):
-    """1024 experts (four logits per lane in each routing wave) on the grouped
-    path, and tokens 0-1 on the per-token path."""
+    """1024 experts (four logits per lane in each routing wave): 24 tokens
+    (96 assignments) on the grouped path, and tokens 0-1 on the per-token
+    path."""
     from bit_dequant_expert_router_amd.weights import layer_from_canonical
     import oracle
     dims = syn.Dims(256, 128, 1024, 8, 4)
     dense = syn.layer_dense(5, 0, dims)
     experts = [syn.expert_canonical(5, 0, e, dims) for e in range(dims.n_experts + 1)]
     lw = layer_from_canonical(dims, dense, experts)
-    x = syn.tokens(15, 12, dims.hidden)
+    x = syn.tokens(15, 24, dims.hidden)
+    assert moe.moe_forward_stage_count(dims, 24) == 7
     out, idx, wt = run_layer(dims, lw, x)
     refs = [oracle.layer_all(dims, x[t], dense, experts) for t in range(x.shape[0])]
     for t in range(x.shape[0]):

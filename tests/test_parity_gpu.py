@@ -41,7 +41,7 @@ def test_tiny_layer(moe):
     dims = w.dims
     log(f"tiny: {dims}")
     dense, experts, lw = _canonical_layer(dims)
-    x = syn.tokens(0, 19, dims.hidden)  # a ragged batch, plus single-token calls
+    x = syn.tokens(0, 45, dims.hidden)  # a ragged grouped batch (90 assignments), plus single-token calls
     out, idx, wt = run_layer(dims, lw, x)
     for t in range(x.shape[0]):
         ref = oracle.layer_all(dims, x[t], dense, experts)
@@ -52,6 +52,8 @@ def test_tiny_layer(moe):
         assert np.array_equal(i1[0], idx[t])
         np.testing.assert_allclose(o1[0], out[t], rtol=1e-5, atol=1e-4)
 
+
+GROUPED_MIN_ASSIGN = 80  # tokens x top-K from which a batch is grouped by expert (include/moe.h)
 
 SMALL_SHAPES = [
     # hidden, ffn, experts, top_k, bits
@@ -69,24 +71,30 @@ SMALL_SHAPES = [
 
 @pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_small_shapes(moe, shape):
-    """Five tokens through the grouped kernels, then tokens 0-2 and 3 through
-    the per-token kernels (batches of 1 to 3 tokens)."""
+    """A batch of at least 80 assignments through the grouped kernels (tokens
+    0-4 and the last checked), then tokens 0-4 and 3 through the per-token
+    kernels."""
     H, F, E, K, bits = shape
     dims = syn.Dims(H, F, E, K, bits)
     log(f"small shape {shape}")
     dense, experts, lw = _canonical_layer(dims, seed=3, layer=1)
-    x = syn.tokens(3, 5, H)
-    refs = [oracle.layer_all(dims, x[t], dense, experts) for t in range(x.shape[0])]
+    T = max(5, -(-GROUPED_MIN_ASSIGN // K))
+    x = syn.tokens(3, T, H)
+    checked = list(range(5)) + [T - 1]
+    refs = {t: oracle.layer_all(dims, x[t], dense, experts) for t in checked}
+    assert moe.moe_forward_stage_count(dims, T) == 7
     out, idx, wt = run_layer(dims, lw, x)
-    for t in range(x.shape[0]):
+    for t in checked:
         check_token(out[t], idx[t], wt[t], refs[t], K, f"{shape} token {t}")
-    for t0, t1 in ((0, 3), (3, 4)):
+    for t0, t1 in ((0, 5), (3, 4)):
+        if t1 - t0 > 1 and (t1 - t0) * K >= GROUPED_MIN_ASSIGN:
+            continue
         out, idx, wt = run_layer(dims, lw, x[t0:t1])
         for t in range(t0, t1):
             check_token(out[t - t0], idx[t - t0], wt[t - t0], refs[t], K, f"{shape} per-token path, token {t}")
 
 
-@pytest.mark.parametrize("n_tokens", [1, 3, 6, 40])  # ungrouped (1, 3) and grouped (6, 40)
+@pytest.mark.parametrize("n_tokens", [1, 3, 6, 40])  # per-token (1, 3, 6) and grouped (40: 80 assignments)
 def test_inplace_determinism_and_optional_outputs(moe, n_tokens):
     dims = syn.WORKLOADS["tiny"].dims
     log(f"tiny: in place / determinism, {n_tokens} tokens")
@@ -102,10 +110,10 @@ def test_inplace_determinism_and_optional_outputs(moe, n_tokens):
         check_token(a[t], ia[t], wa[t], oracle.layer_all(dims, x[t], dense, experts), dims.top_k, f"token {t}")
 
 
-@pytest.mark.parametrize("name,T", [("tiny", 3), ("tiny", 6), ("layer4", 1)])
+@pytest.mark.parametrize("name,T", [("tiny", 3), ("tiny", 40), ("layer4", 1)])
 def test_stages_equal_full_forward(moe, name, T):
     """The stages enqueued one by one give exactly the one-call result, on the
-    per-token path (3 tokens, 3 stages), the grouped path (6 tokens, 7 stages)
+    per-token path (3 tokens, 3 stages), the grouped path (40 tokens, 7 stages)
     and the full-size single-token layer."""
     dims = syn.WORKLOADS[name].dims
     if name != "tiny":
@@ -132,7 +140,7 @@ def _check_stages(moe, dims, lw, x, full, fidx, fw):
     ws = torch.empty(moe.moe_workspace_bytes(dims, T), dtype=torch.uint8, device="cuda")
     moe.moe_workspace_init(ws)
     n_stages = moe.moe_forward_stage_count(dims, T)
-    assert n_stages == (3 if T < 4 else 7)
+    assert n_stages == (3 if T * dims.top_k < GROUPED_MIN_ASSIGN else 7)
     for stage in range(n_stages):
         moe.moe_layer_forward_stage(dims, lw.descriptor(), xt, yt, T, ridx, rw, ws, None, stage)
     torch.cuda.synchronize()
@@ -140,7 +148,7 @@ def _check_stages(moe, dims, lw, x, full, fidx, fw):
     assert np.array_equal(rw.cpu().numpy(), fw)
 
 
-@pytest.mark.parametrize("T", [3, 6])
+@pytest.mark.parametrize("T", [3, 40])
 def test_nan_propagates(moe, T):
     """A NaN in x reaches every output of its token and no other token."""
     dims = syn.WORKLOADS["tiny"].dims
@@ -192,12 +200,14 @@ def test_full_layer(moe, name):
     dims = w.dims
     log(f"full layer {name}: {dims}")
     lw = layer_generated(dims, dense_layer(w.seed, 0, dims), w.seed, 0)
-    x = syn.tokens(w.seed, 6, dims.hidden)
-    out_b, idx_b, w_b = run_layer(dims, lw, x)  # one call with 6 tokens
-    for t in range(x.shape[0]):
+    x = syn.tokens(w.seed, 20, dims.hidden)
+    out_b, idx_b, w_b = run_layer(dims, lw, x)  # one grouped call with 20 tokens (80 assignments)
+    out_p, idx_p, w_p = run_layer(dims, lw, x[:6])  # one per-token call with 6 tokens
+    for t in range(6):
         out1, idx1, w1 = run_layer(dims, lw, x[t:t + 1])  # the bench's single-token call
         ref = oracle_layer_generated(dims, w.seed, 0, x[t])
         check_token(out1[0], idx1[0], w1[0], ref, dims.top_k, f"{name} token {t}")
+        check_token(out_p[t], idx_p[t], w_p[t], ref, dims.top_k, f"{name} 6-token call, token {t}")
         check_token(out_b[t], idx_b[t], w_b[t], ref, dims.top_k, f"{name} batched token {t}")
 
 
