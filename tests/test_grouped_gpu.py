@@ -153,3 +153,28 @@ def test_ragged_token_tile_full_size(moe):
     for t in (0, 31, 32, 40, 44):
         ref = oracle_layer_generated(dims, w.seed, 3, x[t])
         check_token(out[t], idx[t], wt[t], ref, dims.top_k, f"batch {T} token {t}")
+
+
+def test_batch_past_grouping_limit(moe):
+    """2049 tiny tokens with top-2 (4098 assignments, past the grouped path's
+    4096) run the per-token kernels, one row of blocks per token; sampled
+    tokens against the oracle, and the first 2048 tokens as one grouped call
+    give the same routing."""
+    import oracle
+    w = syn.WORKLOADS["tiny"]
+    dims = w.dims
+    T = 2049
+    assert moe.moe_forward_stage_count(dims, T) == 3
+    assert moe.moe_forward_stage_count(dims, T - 1) == 7
+    from bit_dequant_expert_router_amd.weights import layer_from_canonical
+    dense = syn.layer_dense(w.seed, 0, dims)
+    experts = [syn.expert_canonical(w.seed, 0, e, dims) for e in range(dims.n_experts + 1)]
+    lw = layer_from_canonical(dims, dense, experts)
+    x = syn.tokens(17, T, dims.hidden)
+    out, idx, wt = run_layer(dims, lw, x)
+    for t in (0, 1, 1000, 2047, 2048):
+        check_token(out[t], idx[t], wt[t], oracle.layer_all(dims, x[t], dense, experts), dims.top_k,
+                    f"token {t} of {T}")
+    og, ig, wg = run_layer(dims, lw, x[:T - 1])
+    assert np.array_equal(ig, idx[:T - 1])
+    np.testing.assert_allclose(og, out[:T - 1], rtol=1e-5, atol=1e-4)
