@@ -183,11 +183,11 @@ constexpr int kForwardStages = 3;
 // Batches of at least kGroupMinAssign assignments (tokens x top-K) and at most
 // kGroupMaxAssign take the grouped-by-expert path; smaller batches run the
 // per-token kernels, one row of blocks per token.  On the 4096/1024/512-expert
-// shape the per-token kernels are ahead up to 64 assignments with top-4 and 70
+// shape the per-token kernels are ahead up to 96 assignments with top-4 and 80
 // with top-10 (the grouped path's seven launches and its grouping cost more than
-// re-reading the few experts two tokens share), the grouped path from 96 and
-// 120; at 80 the two are within 3%.
-constexpr int kGroupMinAssign = 80;
+// re-reading the few experts two tokens share), the grouped path from 112 and
+// 100.
+constexpr int kGroupMinAssign = 100;
 constexpr int kGroupMaxAssign = 4096;
 constexpr int kGroupedStages = 7;
 inline bool uses_grouped(const Shape &s, int T) {

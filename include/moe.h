@@ -151,9 +151,9 @@ int moe_generate_layer(const moe_dims_t *dims, uint64_t seed, uint32_t layer, vo
                        void *shared_expert, void *stream);
 
 /*
- * One MoE layer for n_tokens tokens.  Batches of fewer than 80 assignments
- * (n_tokens * top_k < 80) run three kernels per layer, one row of blocks per
- * token; batches of 80 to 4096 assignments are grouped by expert so that every
+ * One MoE layer for n_tokens tokens.  Batches of fewer than 100 assignments
+ * (n_tokens * top_k < 100) run three kernels per layer, one row of blocks per
+ * token; batches of 100 to 4096 assignments are grouped by expert so that every
  * selected expert's weights are read once for all of its tokens (larger ones run
  * the per-token kernels).  Both give the same results up to fp32 rounding order.
  *   x          fp32 [n_tokens][H] device, 16-B aligned (may equal y: in place)

@@ -172,8 +172,8 @@ def test_stage_count():
     dims = d()
     K = dims.top_k
     assert moe.moe_forward_stage_count(dims, 1) == 3
-    assert moe.moe_forward_stage_count(dims, 19) == 3  # 76 assignments: per-token kernels
-    assert moe.moe_forward_stage_count(dims, 20) == 7  # 80: grouped by expert
+    assert moe.moe_forward_stage_count(dims, 24) == 3  # 96 assignments: per-token kernels
+    assert moe.moe_forward_stage_count(dims, 25) == 7  # 100: grouped by expert
     assert moe.moe_forward_stage_count(dims, 4096 // K) == 7
     assert moe.moe_forward_stage_count(dims, 4096 // K + 1) == 3
     f = moe._lib.moe_forward_stage_count
@@ -186,7 +186,7 @@ def test_stage_count():
 
 def test_grouped_stage_rejects():
     dims = d()
-    T = 20
+    T = 25
     wsb = moe.moe_workspace_bytes(dims, T)
     f = moe._lib.moe_layer_forward_stage
     lay = _layer()
