@@ -40,14 +40,14 @@ HBM_PEAK_BPS = 8.0e12  # MI355X HBM3E peak
 # was measured on.  FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0, the ratios
 # of bytes moved to counts reported for a 256 MiB copy.
 KERNEL_TRAFFIC = {
-    ("layer4", "k_gateup"): {"source_sha256_prefix": "fc06bccae2fdc253", "fetch_kib": 11640.0, "write_kib": 20.1,
+    ("layer4", "k_gateup"): {"source_sha256_prefix": "9c0d0a86ed91ca2e", "fetch_kib": 11640.0, "write_kib": 20.1,
                              "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer4", "k_down"): {"source_sha256_prefix": "fc06bccae2fdc253", "fetch_kib": 5929.5, "write_kib": 16.0,
+    ("layer4", "k_down"): {"source_sha256_prefix": "9c0d0a86ed91ca2e", "fetch_kib": 5929.5, "write_kib": 16.0,
                            "fetch_scale": 2.0, "write_scale": 1.0},
-    ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "1be19c54d68a4e8b", "fetch_kib": 577997.6,
-                                      "write_kib": 3513.3, "fetch_scale": 2.0, "write_scale": 1.0},
-    ("batch32", "k_grouped_down"): {"source_sha256_prefix": "1be19c54d68a4e8b", "fetch_kib": 290098.9,
-                                    "write_kib": 5907.0, "fetch_scale": 2.0, "write_scale": 1.0},
+    ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "9e0210c89c7e9558", "fetch_kib": 578712.2,
+                                      "write_kib": 3511.7, "fetch_scale": 2.0, "write_scale": 1.0},
+    ("batch32", "k_grouped_down"): {"source_sha256_prefix": "9e0210c89c7e9558", "fetch_kib": 289498.5,
+                                    "write_kib": 5907.2, "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
 
@@ -290,7 +290,7 @@ def cpu_baseline(args, wl, dims):
 
     import oracle
     import synthetic as syn
-    n = args.cpu_sample
+    n = max(1, args.cpu_sample // wl.n_tokens)  # steps holding about cpu_sample tokens
     R = max(1, args.layers)
     xs = syn.tokens(wl.seed, n * wl.n_tokens, dims.hidden).reshape(n, wl.n_tokens, dims.hidden)
     cache = {}
