@@ -28,7 +28,6 @@ namespace moe {
 
 namespace {
 
-
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
 
@@ -200,17 +199,6 @@ __device__ __forceinline__ float route_key_value(uint64_t key) {
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
-// the router logits of one token, EPL per lane (clamped index: all loads in flight at once)
-template <int EPL>
-__device__ __forceinline__ void load_logits(const float *__restrict__ z, int E, float (&zv)[EPL]) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane + 64 * i;
-        zv[i] = z[e < E ? e : E - 1];
-    }
-}
-
 // bitonic sort of n = EPL keys, descending
 template <int EPL>
 __device__ __forceinline__ void sort_desc(uint64_t (&key)[EPL]) {
@@ -375,138 +363,8 @@ struct QSlice {
     static constexpr float kCodeOffset = BITS == 4 ? 8.0f : 0.0f;  // signed code = q - offset
 };
 
-template <int BITS, int CPL>
-struct LimbSlice {
-    using Q = QSlice<BITS, CPL>;
-    int L[kLimbs][Q::NL];
-    float S[Q::NGL];  // group scale (power of two)
-    float X[Q::NGL];  // sum of the activations of the slice within the group
-};
-
-// nibble-order codes (gate, up) against the lane's limb slice
-template <int BITS, int CPL>
-__device__ __forceinline__ float qdot(const uint4 (&c)[CPL], const uint32_t (&sb)[QSlice<BITS, CPL>::NGL],
-                                      const LimbSlice<BITS, CPL> &v) {
-    using Q = QSlice<BITS, CPL>;
-    int acc[Q::NGL][kLimbs];
-#pragma unroll
-    for (int g = 0; g < Q::NGL; ++g)
-#pragma unroll
-        for (int x = 0; x < kLimbs; ++x) acc[g][x] = 0;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const uint32_t d[4] = {c[j].x, c[j].y, c[j].z, c[j].w};
-#pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) {
-            if constexpr (BITS == 4) {
-                const int q = (int)(d[w4] ^ 0x88888888u);  // eight signed codes q - 8
-                const int li = j * 4 + w4;
-                const int g = (8 * li) / Q::GL;
-#pragma unroll
-                for (int x = 0; x < kLimbs; ++x) acc[g][x] = __builtin_amdgcn_sdot8(q, v.L[x][li], acc[g][x], false);
-            } else {
-                const int qa = (int)(d[w4] & 0x33333333u);         // codes 0..7 of the dword
-                const int qb = (int)((d[w4] >> 2) & 0x33333333u);  // codes 8..15
-                const int li = j * 8 + 2 * w4;
-                const int g = (8 * li) / Q::GL;
-#pragma unroll
-                for (int x = 0; x < kLimbs; ++x) {
-                    acc[g][x] = __builtin_amdgcn_sdot8(qa, v.L[x][li], acc[g][x], false);
-                    acc[g][x] = __builtin_amdgcn_sdot8(qb, v.L[x][li + 1], acc[g][x], false);
-                }
-            }
-        }
-    }
-    float total = 0.0f;
-#pragma unroll
-    for (int g = 0; g < Q::NGL; ++g) {
-        float f = (float)acc[g][kLimbs - 1];
-#pragma unroll
-        for (int x = kLimbs - 2; x >= 0; --x) f = fmaf(f, 16.0f, (float)acc[g][x]);
-        const float s = bf16_lo(sb[g]);
-        total = fmaf(s * v.S[g], f, total);
-        total = fmaf(fmaf(Q::kCodeOffset, s, bf16_hi(sb[g])), v.X[g], total);
-    }
-    return total;
-}
-
-// Variant for weights reused across several activation vectors: the codes are
-// prepared once per row (4-bit: made signed by the XOR), the group scale s and
-// offset o = b + off * s are unpacked once, and the six limb sums are
-// combined in integers by Horner steps (limbs 4-5 and 0-3: |sum| < 2^25),
-// then in fp32: f = hi * 2^16 + lo.
-template <int BITS, int CPL>
-struct RowPrep {
-    using Q = QSlice<BITS, CPL>;
-    uint4 q[CPL];
-    float s[Q::NGL], o[Q::NGL];
-};
-
-template <int BITS, int CPL>
-__device__ __forceinline__ void prep_row(const uint4 (&c)[CPL], const uint32_t (&sb)[QSlice<BITS, CPL>::NGL],
-                                         RowPrep<BITS, CPL> &r) {
-    using Q = QSlice<BITS, CPL>;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        if constexpr (BITS == 4)
-            r.q[j] = make_uint4(c[j].x ^ 0x88888888u, c[j].y ^ 0x88888888u, c[j].z ^ 0x88888888u, c[j].w ^ 0x88888888u);
-        else
-            r.q[j] = c[j];
-    }
-#pragma unroll
-    for (int g = 0; g < Q::NGL; ++g) {
-        r.s[g] = bf16_lo(sb[g]);
-        r.o[g] = fmaf(Q::kCodeOffset, r.s[g], bf16_hi(sb[g]));
-    }
-}
-
-template <int BITS, int CPL>
-__device__ __forceinline__ float qdot_prep(const RowPrep<BITS, CPL> &r, const LimbSlice<BITS, CPL> &v) {
-    using Q = QSlice<BITS, CPL>;
-    // dword list of the slice: (operand, limb dword index, group)
-    constexpr int ND = BITS == 4 ? CPL * 4 : CPL * 8;
-    int op[ND];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const uint32_t d[4] = {r.q[j].x, r.q[j].y, r.q[j].z, r.q[j].w};
-#pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) {
-            if constexpr (BITS == 4) {
-                op[j * 4 + w4] = (int)d[w4];
-            } else {
-                op[j * 8 + 2 * w4] = (int)(d[w4] & 0x33333333u);
-                op[j * 8 + 2 * w4 + 1] = (int)((d[w4] >> 2) & 0x33333333u);
-            }
-        }
-    }
-    constexpr int DPG = ND / Q::NGL;  // limb dwords per group
-    float total = 0.0f;
-#pragma unroll
-    for (int g = 0; g < Q::NGL; ++g) {
-        int hi = 0, lo = 0;
-#pragma unroll
-        for (int x = kLimbs - 1; x >= 4; --x) {
-            if (x != kLimbs - 1) hi <<= 4;
-#pragma unroll
-            for (int i = 0; i < DPG; ++i) hi = __builtin_amdgcn_sdot8(op[g * DPG + i], v.L[x][g * DPG + i], hi, false);
-        }
-#pragma unroll
-        for (int x = 3; x >= 0; --x) {
-            if (x != 3) lo <<= 4;
-#pragma unroll
-            for (int i = 0; i < DPG; ++i) lo = __builtin_amdgcn_sdot8(op[g * DPG + i], v.L[x][g * DPG + i], lo, false);
-        }
-        const float f = fmaf((float)hi, 65536.0f, (float)lo);
-        total = fmaf(r.s[g] * v.S[g], f, total);
-        total = fmaf(r.o[g], v.X[g], total);
-    }
-    return total;
-}
-
-// NR prepared rows against one vector's lane slice held in LDS.  The limb
-// words are read one limb at a time, limb-major, so that only 8 of them are
-// live; each row keeps two integer Horner accumulators (limbs 5-4, 3-0).
-// Codes must be prepared (prep_codes) and s, o unpacked (prep_scales).
+// 4-bit codes made signed (q - 8, as v_dot8_i32_i4 reads them) by one XOR per
+// dword, once per row; 2-bit codes are used as stored
 template <int BITS, int CPL>
 __device__ __forceinline__ void prep_codes(uint4 (&c)[CPL]) {
     if constexpr (BITS == 4) {
@@ -516,7 +374,13 @@ __device__ __forceinline__ void prep_codes(uint4 (&c)[CPL]) {
     }
 }
 
-// limbs: [kLimbs][n/8] words; S: [n/64] group scales; Xh: [n/32] half-group sums
+// NR prepared rows (prep_codes) against one vector's lane slice held in LDS.
+// The limb words are read one limb at a time, limb-major, so that only 8 of
+// them are live; each row keeps two integer Horner accumulators (limbs 5-4 and
+// 3-0, each below 2^25), combined in fp32 as hi * 2^16 + lo.  s: the rows'
+// group scales; o: b + 8 s (4-bit) or b (2-bit), unpacked by the caller once
+// per row.  limbs: [kLimbs][n/8] words; S: [n/64] group scales; Xh: [n/32]
+// half-group sums.
 template <int BITS, int CPL, int NR>
 __device__ __forceinline__ void rows_dot_lds(const uint4 (&c)[NR][CPL], const float (&s)[NR][QSlice<BITS, CPL>::NGL],
                                              const float (&o)[NR][QSlice<BITS, CPL>::NGL], const uint32_t *limbs,

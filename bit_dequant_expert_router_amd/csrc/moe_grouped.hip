@@ -48,18 +48,6 @@ __device__ __forceinline__ GroupView group_view(const FwdArgs &a) {
     return g;
 }
 
-// exclusive prefix sum over the 64 lanes of a wave (small, one-time use)
-__device__ __forceinline__ int wave_excl_scan(int v) {
-    const int lane = threadIdx.x & 63;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += u;
-    }
-    return incl - v;
-}
-
 // exclusive prefix sums of NV values per thread over a block of NT threads
 // (thread order); tot receives the block totals.  s_tmp: NT / 64 * NV ints.
 template <int NV, int NT>
@@ -321,31 +309,6 @@ __device__ __forceinline__ SchedView sched_view(const FwdArgs &a, int launch) {
     v.head = (const const_i32 *)(a.ws.sched + (size_t)launch * sched_launch_ints(a.T, a.s.K));
     v.rec = v.head + 4;
     return v;
-}
-
-// lane slice [k0, k0 + NV) of one vector in limb form: limbs [kLimbs][n/8] dwords,
-// group scales [n/64], half-group sums [n/32]
-template <int BITS, int CPL>
-__device__ __forceinline__ void load_limb_slice(const uint32_t *hl, const float *hs, const float *hx, int n, int k0,
-                                                LimbSlice<BITS, CPL> &hv) {
-    using Q = QSlice<BITS, CPL>;
-    hl += k0 / 8;
-#pragma unroll
-    for (int x = 0; x < kLimbs; ++x)
-#pragma unroll
-        for (int i = 0; i < Q::NL / 4; ++i) {
-            const int4 v = *(const int4 *)(hl + (size_t)x * (n / 8) + 4 * i);
-            hv.L[x][4 * i + 0] = v.x; hv.L[x][4 * i + 1] = v.y;
-            hv.L[x][4 * i + 2] = v.z; hv.L[x][4 * i + 3] = v.w;
-        }
-#pragma unroll
-    for (int g = 0; g < Q::NGL; ++g) {
-        hv.S[g] = hs[k0 / 64 + g];
-        float xs = 0.0f;
-#pragma unroll
-        for (int hh = 0; hh < Q::GL / 32; ++hh) xs += hx[(k0 + g * 64) / 32 + hh];
-        hv.X[g] = xs;
-    }
 }
 
 // ---------------------------------------------------------------------------

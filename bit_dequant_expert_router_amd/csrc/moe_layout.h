@@ -99,8 +99,10 @@ MOE_HD ExpertLayout make_layout(int H, int F, int bits) {
     return L;
 }
 
-// physical chunk position of logical chunk L in a row
-MOE_HD int phys_chunk(const QMat &q, int L) { return (L / q.cpl) + q.lpr * (L % q.cpl); }
+// logical chunk (16 bytes of codes in reduction order) stored at physical
+// chunk p of a row: lane l of a row's lpr lanes loads physical chunks l,
+// l + lpr, ..., which hold its cpl consecutive logical chunks l cpl ..
+MOE_HD int logical_chunk(const QMat &q, int p) { return (p % q.lpr) * q.cpl + p / q.lpr; }
 
 // position of code i (0 <= i < C) inside a 16-byte chunk: dword index and
 // bit shift within that dword

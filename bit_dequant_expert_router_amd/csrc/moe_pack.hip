@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs a) {
             const size_t local = i - w.chunk_begin[m];
             const int r = (int)(local / q.nchunks);
             const int p = (int)(local % q.nchunks);
-            const int Lc = (p % q.lpr) * q.cpl + p / q.lpr;  // logical chunk stored at p
+            const int Lc = logical_chunk(q, p);
             const int C = 128 / q.bits;
             const uint8_t *src = a.codes[m] + (size_t)r * q.cols + (size_t)Lc * C;
             const uint4 v = make_chunk(q.bits, q.order, [&](int c) { return src[c]; });
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void k_generate(GenArgs a, size_t expert_bytes
             const size_t local = i - w.chunk_begin[m];
             const int r = (int)(local / q.nchunks);
             const int p = (int)(local % q.nchunks);
-            const int Lc = (p % q.lpr) * q.cpl + p / q.lpr;
+            const int Lc = logical_chunk(q, p);
             const int C = 128 / q.bits;
             const int per_word = 64 / q.bits;
             const size_t first_code = (size_t)r * q.cols + (size_t)Lc * C;  // multiple of per_word
