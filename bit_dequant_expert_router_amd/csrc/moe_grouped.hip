@@ -943,8 +943,8 @@ __global__ __launch_bounds__(64) void k_combine(FwdArgs a) {
 constexpr int stream_rpw(int cpl) { return cpl == 1 ? 4 : 2; }
 // block-steps per run: the gate/up runs take about as long as down runs of
 // half as many steps (two matrices per step)
-constexpr int kGateUpRunItems = 8;
-constexpr int kDownRunItems = 4;
+constexpr int kGateUpRunItems = 4;
+constexpr int kDownRunItems = 2;
 
 // vectors staged per pass: as many as fit the block's LDS budget (48 KiB for
 // gate/up: three blocks per CU; 40 KiB for down, whose registers allow four),
