@@ -941,14 +941,18 @@ __global__ __launch_bounds__(64) void k_combine(FwdArgs a) {
 // row-slots per wave and step of k_grouped_stream: two register sets of
 // weights stay within ~80 VGPRs
 constexpr int stream_rpw(int cpl) { return cpl == 1 ? 4 : 2; }
-// block-steps per run: the gate/up runs take about as long as down runs of
-// half as many steps (two matrices per step)
+// block-steps per run (8 rows per gate/up step, 32 per down step): short runs
+// keep the end of the grid tight, since a block holds its current run and the
+// one it has claimed ahead (runs of 8 and 4 steps left the last blocks ~40 us
+// behind the median in a 200 us gate/up launch; 4 and 2 halve that)
 constexpr int kGateUpRunItems = 4;
 constexpr int kDownRunItems = 2;
 
 // vectors staged per pass: as many as fit the block's LDS budget (48 KiB for
-// gate/up: three blocks per CU; 40 KiB for down, whose registers allow four),
-// at most 16
+// gate/up, 40 KiB for down), at most 16.  The grid is as many blocks as the
+// occupancy query allows at that LDS size: registers make it two per CU for
+// gate/up (three, with the registers capped to fit, measured no faster) and
+// four for down.
 inline int stream_vectors(int n, bool down) {
     const int budget = (down ? 40 : 48) * 1024;
     const int v = budget / (stage_words(n) * 4);
