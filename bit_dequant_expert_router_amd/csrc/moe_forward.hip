@@ -2,9 +2,14 @@
 //
 //   k_router : two-pass RMSNorm + router GEMV (E rows) + shared-gate logit;
 //              a few blocks also store h in the fixed-point limb form below
+//              (k_router_split for H = 2048 / 4096, one token per block;
+//              k_router_tokens from 4 tokens, four per block; k_router else)
 //   k_gateup : per block, softmax/top-K/renormalise from the logits, then the
 //              fused gate+up dequant GEMV of the selected experts and the
 //              shared expert with SwiGLU in registers
+//
+// A batch runs one row of blocks per token (grid.y); batches from 100
+// assignments (tokens x top-K) take the grouped kernels instead.
 //   k_down   : down-projection dequant GEMV of all K+1 experts for a set of
 //              output rows, weighted combine, sigmoid-gated shared expert and
 //              residual, written once per row (no atomics, deterministic)
