@@ -110,11 +110,12 @@ def test_inplace_determinism_and_optional_outputs(moe, n_tokens):
         check_token(a[t], ia[t], wa[t], oracle.layer_all(dims, x[t], dense, experts), dims.top_k, f"token {t}")
 
 
-@pytest.mark.parametrize("name,T", [("tiny", 3), ("tiny", 50), ("layer4", 1)])
+@pytest.mark.parametrize("name,T", [("tiny", 3), ("tiny", 50), ("layer4", 1), ("layer4", 6)])
 def test_stages_equal_full_forward(moe, name, T):
     """The stages enqueued one by one give exactly the one-call result, on the
     per-token path (3 tokens, 3 stages), the grouped path (50 tokens, 7 stages)
-    and the full-size single-token layer."""
+    and the full-size layer (one token; six tokens, whose router reads each
+    row once per four tokens)."""
     dims = syn.WORKLOADS[name].dims
     if name != "tiny":
         from bit_dequant_expert_router_amd.weights import layer_generated
