@@ -47,6 +47,11 @@ class moe_layer_t(ctypes.Structure):
                 ("shared_expert", ctypes.c_void_p)]
 
 
+class moe_tier_stats_t(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_uint64), ("lookups", ctypes.c_uint64), ("hits", ctypes.c_uint64),
+                ("misses", ctypes.c_uint64), ("bytes_copied", ctypes.c_uint64)]
+
+
 _vp = ctypes.c_void_p
 _dimsp = ctypes.POINTER(moe_dims_t)
 _layerp = ctypes.POINTER(moe_layer_t)
@@ -65,6 +70,12 @@ _SIGS = {
     "moe_layer_forward_stage": (ctypes.c_int, [_dimsp, _layerp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _i32, _vp]),
     "moe_forward_stage_count": (ctypes.c_int, [_dimsp, _i32]),
     "moe_stack_forward": (ctypes.c_int, [_dimsp, _layerp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "moe_tier_state_bytes": (_sz, [_dimsp, _i32, _i32, _i32]),
+    "moe_tier_device_bytes": (_sz, [_dimsp, _i32, _i32]),
+    "moe_tier_init": (ctypes.c_int, [_dimsp, _i32, _i32, _i32, _vp, _sz, _vp, _sz]),
+    "moe_tier_layer_forward": (ctypes.c_int, [_vp, _i32, _layerp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "moe_tier_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(moe_tier_stats_t)]),
+    "moe_tier_lookup": (ctypes.c_int, [_vp, _i32, _i32, ctypes.POINTER(ctypes.c_int32)]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
@@ -204,3 +215,48 @@ def moe_stack_forward(dims, layers: Sequence[moe_layer_t], x, y, n_tokens: int, 
                   _lib.moe_stack_forward(ctypes.byref(dims_of(dims)), arr, len(layers), _addr(x), _addr(y),
                                          int(n_tokens), _addr(route_idx), _addr(route_w), _addr(workspace),
                                          nbytes, _stream(stream)))
+
+
+# tiered expert residency: `state` is pinned host memory (for example a uint8
+# tensor made with pin_memory=True), `device` device memory; layer.experts of
+# moe_tier_layer_forward is the host copy of the layer's packed experts
+def _nbytes(t, given: Optional[int]) -> int:
+    return given if given is not None else t.numel() * t.element_size()
+
+
+def moe_tier_state_bytes(dims, n_layers: int, n_slots: int, max_tokens: int) -> int:
+    return int(_lib.moe_tier_state_bytes(ctypes.byref(dims_of(dims)), int(n_layers), int(n_slots),
+                                         int(max_tokens)))
+
+
+def moe_tier_device_bytes(dims, n_slots: int, max_tokens: int) -> int:
+    return int(_lib.moe_tier_device_bytes(ctypes.byref(dims_of(dims)), int(n_slots), int(max_tokens)))
+
+
+def moe_tier_init(dims, n_layers: int, n_slots: int, max_tokens: int, state, device,
+                  state_bytes: Optional[int] = None, device_bytes: Optional[int] = None) -> int:
+    return _check("moe_tier_init",
+                  _lib.moe_tier_init(ctypes.byref(dims_of(dims)), int(n_layers), int(n_slots), int(max_tokens),
+                                     _addr(state), _nbytes(state, state_bytes), _addr(device),
+                                     _nbytes(device, device_bytes)))
+
+
+def moe_tier_layer_forward(state, layer_index: int, layer: moe_layer_t, x, y, n_tokens: int, route_idx, route_w,
+                           workspace, workspace_bytes: Optional[int] = None, stream=None) -> int:
+    return _check("moe_tier_layer_forward",
+                  _lib.moe_tier_layer_forward(_addr(state), int(layer_index), ctypes.byref(layer), _addr(x),
+                                              _addr(y), int(n_tokens), _addr(route_idx), _addr(route_w),
+                                              _addr(workspace), _nbytes(workspace, workspace_bytes),
+                                              _stream(stream)))
+
+
+def moe_tier_get_stats(state) -> moe_tier_stats_t:
+    out = moe_tier_stats_t()
+    _check("moe_tier_get_stats", _lib.moe_tier_get_stats(_addr(state), ctypes.byref(out)))
+    return out
+
+
+def moe_tier_lookup(state, layer_index: int, expert: int) -> int:
+    slot = ctypes.c_int32()
+    _check("moe_tier_lookup", _lib.moe_tier_lookup(_addr(state), int(layer_index), int(expert), ctypes.byref(slot)))
+    return slot.value

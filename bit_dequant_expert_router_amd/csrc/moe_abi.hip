@@ -7,6 +7,7 @@
 
 #include "../../include/moe.h"
 #include "moe_internal.h"
+#include "moe_tier.h"
 
 namespace {
 
@@ -86,6 +87,81 @@ int check_forward_common(const moe_dims_t *dims, const float *x, float *y, int32
     if (overlap_not_equal(x, y, (size_t)n_tokens * dims->hidden * sizeof(float))) return MOE_ERR_INVALID_ARG;
     if (workspace_bytes < workspace_bytes_checked(dims, n_tokens)) return MOE_ERR_WORKSPACE;
     return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// tiered expert residency: the state the caller holds in pinned host memory,
+// a header followed by int32 arrays (the LRU lists and key map, the routing
+// landing area and the slot-table staging area); pointers into it are derived
+// from its base on every call
+// ---------------------------------------------------------------------------
+constexpr uint64_t kTierMagic = 0x7265695465754d31ull;
+
+struct TierState {
+    uint64_t magic;
+    moe_dims_t dims;
+    int32_t n_layers, n_slots, max_tokens, pad;
+    uint64_t expert_bytes;
+    uint8_t *slots;      // device: n_slots packed experts
+    int32_t *table_dev;  // device: [max_tokens][K] slots of one call's selected experts
+    moe_tier_stats_t stats;
+    int32_t head, tail;  // of the LRU list
+};
+
+struct TierView {
+    TierState *st;
+    SlotLru lru;
+    int32_t *route;  // [max_tokens][K] host landing area of the selected experts
+    int32_t *table;  // [max_tokens][K] host staging area of their slots
+};
+
+constexpr size_t tier_header_bytes() { return (sizeof(TierState) + 255) / 256 * 256; }
+
+size_t tier_ints(const moe_dims_t *d, int32_t n_layers, int32_t n_slots, int32_t max_tokens) {
+    return SlotLru::ints(n_slots, n_layers * d->n_experts) + 2 * (size_t)max_tokens * d->top_k;
+}
+
+int check_tier_args(const moe_dims_t *dims, int32_t n_layers, int32_t n_slots, int32_t max_tokens) {
+    const int rc = check_dims_impl(dims);
+    if (rc != MOE_OK) return rc;
+    if (n_layers < 1 || max_tokens < 1 || max_tokens > 65535) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)n_layers * dims->n_experts >= ((int64_t)1 << 31)) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)n_slots < (int64_t)max_tokens * dims->top_k) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+size_t tier_table_bytes(const moe_dims_t *d, int32_t max_tokens) {
+    return ((size_t)max_tokens * d->top_k * sizeof(int32_t) + kAlign - 1) / kAlign * kAlign;
+}
+
+// the view of a state (the list is read back from the header; store_lru writes it)
+TierView tier_view(void *state) {
+    TierView v;
+    v.st = (TierState *)state;
+    int32_t *ints = (int32_t *)((uint8_t *)state + tier_header_bytes());
+    const int32_t ns = v.st->n_slots, nk = v.st->n_layers * v.st->dims.n_experts;
+    v.lru.n_slots = ns;
+    v.lru.n_keys = nk;
+    v.lru.key = ints;
+    v.lru.prev = ints + ns;
+    v.lru.next = ints + 2 * (size_t)ns;
+    v.lru.slot_of = ints + 3 * (size_t)ns;
+    v.lru.head = v.st->head;
+    v.lru.tail = v.st->tail;
+    v.route = ints + SlotLru::ints(ns, nk);
+    v.table = v.route + (size_t)v.st->max_tokens * v.st->dims.top_k;
+    return v;
+}
+
+void store_lru(TierView &v) {
+    v.st->head = v.lru.head;
+    v.st->tail = v.lru.tail;
+}
+
+const TierState *tier_header(const void *state) {
+    if (!state || !aligned(state, 8)) return nullptr;
+    const TierState *st = (const TierState *)state;
+    return st->magic == kTierMagic ? st : nullptr;
 }
 
 }  // namespace
@@ -225,6 +301,111 @@ int moe_stack_forward(const moe_dims_t *dims, const moe_layer_t *layers, int32_t
                                    route_w ? route_w + l * per_layer : nullptr, workspace);
         if (hip_status(launch_layer(a, (hipStream_t)stream)) != MOE_OK) return MOE_ERR_HIP;
     }
+    return MOE_OK;
+}
+
+size_t moe_tier_state_bytes(const moe_dims_t *dims, int32_t n_layers, int32_t n_slots, int32_t max_tokens) {
+    if (check_tier_args(dims, n_layers, n_slots, max_tokens) != MOE_OK) return 0;
+    return tier_header_bytes() + tier_ints(dims, n_layers, n_slots, max_tokens) * sizeof(int32_t);
+}
+
+size_t moe_tier_device_bytes(const moe_dims_t *dims, int32_t n_slots, int32_t max_tokens) {
+    if (check_tier_args(dims, 1, n_slots, max_tokens) != MOE_OK) return 0;
+    const size_t eb = make_layout(dims->hidden, dims->ffn, dims->bits).bytes;
+    return (size_t)n_slots * eb + tier_table_bytes(dims, max_tokens);
+}
+
+int moe_tier_init(const moe_dims_t *dims, int32_t n_layers, int32_t n_slots, int32_t max_tokens, void *state,
+                  size_t state_bytes, void *device, size_t device_bytes) {
+    const int rc = check_tier_args(dims, n_layers, n_slots, max_tokens);
+    if (rc != MOE_OK) return rc;
+    if (!state || !device) return MOE_ERR_INVALID_ARG;
+    if (!aligned(state, 8) || !aligned(device, kAlign)) return MOE_ERR_ALIGNMENT;
+    if (state_bytes < moe_tier_state_bytes(dims, n_layers, n_slots, max_tokens)) return MOE_ERR_WORKSPACE;
+    if (device_bytes < moe_tier_device_bytes(dims, n_slots, max_tokens)) return MOE_ERR_WORKSPACE;
+    TierState *st = (TierState *)state;
+    memset(st, 0, sizeof(TierState));
+    st->dims = *dims;
+    st->n_layers = n_layers;
+    st->n_slots = n_slots;
+    st->max_tokens = max_tokens;
+    st->expert_bytes = make_layout(dims->hidden, dims->ffn, dims->bits).bytes;
+    st->slots = (uint8_t *)device;
+    st->table_dev = (int32_t *)(st->slots + (size_t)n_slots * st->expert_bytes);
+    TierView v = tier_view(state);
+    v.lru.init(n_slots, n_layers * dims->n_experts, v.lru.key);
+    store_lru(v);
+    st->magic = kTierMagic;
+    return MOE_OK;
+}
+
+int moe_tier_layer_forward(void *state, int32_t layer_index, const moe_layer_t *layer, const float *x,
+                           float *y, int32_t n_tokens, int32_t *route_idx, float *route_w, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    if (!tier_header(state)) return MOE_ERR_INVALID_ARG;
+    TierView v = tier_view(state);
+    TierState *st = v.st;
+    const moe_dims_t *dims = &st->dims;
+    int rc = check_forward_common(dims, x, y, n_tokens, route_idx, route_w, workspace, workspace_bytes);
+    if (rc != MOE_OK) return rc;
+    if (n_tokens > st->max_tokens || layer_index < 0 || layer_index >= st->n_layers) return MOE_ERR_INVALID_ARG;
+    rc = check_layer(layer);
+    if (rc != MOE_OK) return rc;
+    const hipStream_t hs = (hipStream_t)stream;
+    FwdArgs a = make_fwd(dims, layer, x, y, n_tokens, route_idx, route_w, workspace);
+    const int K = dims->top_k, E = dims->n_experts, n = n_tokens * K;
+    // 1. norm, router and routing; 2. the selection to the host
+    if (hip_status(launch_forward_route(a, hs)) != MOE_OK) return MOE_ERR_HIP;
+    if (hip_status(hipMemcpyAsync(v.route, a.ws.sel, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost, hs)) !=
+        MOE_OK)
+        return MOE_ERR_HIP;
+    if (hip_status(hipStreamSynchronize(hs)) != MOE_OK) return MOE_ERR_HIP;
+    // 3. lookups in token order, then rank order; a miss copies the expert in
+    const uint8_t *host = (const uint8_t *)layer->experts;
+    const size_t eb = st->expert_bytes;
+    for (int i = 0; i < n; ++i) {
+        const int32_t e = v.route[i];
+        if (e < 0 || e >= E) return hip_status(hipErrorUnknown);  // cannot happen: routing selects valid experts
+        bool hit;
+        const int32_t slot = v.lru.acquire(layer_index * E + e, &hit);
+        store_lru(v);
+        v.table[i] = slot;
+        st->stats.lookups += 1;
+        if (hit) {
+            st->stats.hits += 1;
+            continue;
+        }
+        st->stats.misses += 1;
+        if (hip_status(hipMemcpyAsync(st->slots + (size_t)slot * eb, host + (size_t)e * eb, eb,
+                                      hipMemcpyHostToDevice, hs)) != MOE_OK)
+            return MOE_ERR_HIP;
+        st->stats.bytes_copied += eb;
+    }
+    // 4. the slot table, then the expert kernels reading from the slots
+    if (hip_status(hipMemcpyAsync(st->table_dev, v.table, (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice, hs)) !=
+        MOE_OK)
+        return MOE_ERR_HIP;
+    a.experts = st->slots;
+    a.slot_tk = st->table_dev;
+    if (hip_status(launch_forward_slots(a, hs)) != MOE_OK) return MOE_ERR_HIP;
+    st->stats.calls += 1;
+    return MOE_OK;
+}
+
+int moe_tier_get_stats(const void *state, moe_tier_stats_t *out) {
+    const TierState *st = tier_header(state);
+    if (!st || !out) return MOE_ERR_INVALID_ARG;
+    *out = st->stats;
+    return MOE_OK;
+}
+
+int moe_tier_lookup(const void *state, int32_t layer_index, int32_t expert, int32_t *slot) {
+    const TierState *st = tier_header(state);
+    if (!st || !slot) return MOE_ERR_INVALID_ARG;
+    if (layer_index < 0 || layer_index >= st->n_layers || expert < 0 || expert >= st->dims.n_experts)
+        return MOE_ERR_INVALID_ARG;
+    const TierView v = tier_view((void *)state);
+    *slot = v.lru.slot_of[layer_index * st->dims.n_experts + expert];
     return MOE_OK;
 }
 

@@ -356,7 +356,9 @@ __global__ __launch_bounds__(256) void k_router_tokens(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // LPR: lanes per row when the step's partial sums are reduced together (64);
 // 0: one reduction per row
-template <int BITS, int CPL, int RPW, int EPL, int LPR>
+// TIER: the selected experts' routing is already done (k_route) and their
+// weights sit in cache slots, a.slot_tk[t][rank] (a.experts = the slots' base)
+template <int BITS, int CPL, int RPW, int EPL, int LPR, bool TIER>
 __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
     using Q = QSlice<BITS, CPL>;
     const int t = blockIdx.y;
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
     const int rs0 = (blockIdx.x * 4 + wave) * RPW;
     const bool active = rs0 < nrs;
     // row-steps are slot-major: the block needs the routing iff its first row is routed
-    const bool block_routed = (blockIdx.x * 4 * RPW * rpi) / F < K;
+    const bool block_routed = !TIER && (blockIdx.x * 4 * RPW * rpi) / F < K;
     const bool wave_shared_only = (rs0 * rpi) / F >= K;
 
     __shared__ __align__(16) uint32_t s_hl[kLimbs * kMaxDim / 8];  // limbs of h, [kLimbs][H/8]
@@ -448,7 +450,16 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
     }
     __syncthreads();
     if (!active) return;
-    if (!wave_shared_only) {
+    if (TIER && !wave_shared_only) {
+        int er[RPW];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int rs = rs0 + i < nrs ? rs0 + i : nrs - 1;
+            const int s = (rs * rpi) / F;
+            er[i] = a.slot_tk[t * K + (s < K ? s : K - 1)];
+        }
+        issue_loads(er);
+    } else if (!wave_shared_only) {
         // every routed wave ranks the block's candidates itself
         const RouteSel rt = route_select(K, s_cand);
         if (blockIdx.x == 0 && wave == 0) {
@@ -536,7 +547,9 @@ constexpr int kDownStageValues = 5120;  // activations staged per batch (batch *
 // 0: one reduction per row
 // ONE: all K+1 slots in a single batch (straight-line code: no loop-header
 // wait holds back the first loads)
-template <int BITS, int CPL, int RPW, int LPR, bool ONE>
+// TIER: the selected experts sit in cache slots, a.slot_tk[t][rank] (a.experts
+// = the slots' base)
+template <int BITS, int CPL, int RPW, int LPR, bool ONE, bool TIER>
 __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_recip) {
     using Q = QSlice<BITS, CPL>;
     const int t = blockIdx.y;
@@ -568,7 +581,7 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_
     // lane s (s <= K) holds slot s: expert index (s < K) and combine
     // coefficient; only those lanes are ever read (unconditional loads, lanes
     // past the end read a valid entry)
-    const int my_e = a.ws.sel[t * K + (lane < K ? lane : K - 1)];
+    const int my_e = (TIER ? a.slot_tk : a.ws.sel)[t * K + (lane < K ? lane : K - 1)];
     const float my_c = a.ws.coef[t * (K + 1) + (lane <= K ? lane : K)];
 
     float acc[RPW];
@@ -606,8 +619,13 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_
         for (int si = 0; si < kDownBatch; ++si) {
             const int sc = si < nb ? si : nb - 1;
             const int s = (b0 + sc == 0) ? K : b0 + sc - 1;
-            const int e = (s == K) ? E : lane_bcast(my_e, s);
-            const uint8_t *ex = (e < E) ? a.experts + (size_t)e * a.L.bytes : a.shared;
+            const uint8_t *ex;
+            if constexpr (TIER) {
+                ex = (s == K) ? a.shared : a.experts + (size_t)lane_bcast(my_e, s) * a.L.bytes;
+            } else {
+                const int e = (s == K) ? E : lane_bcast(my_e, s);
+                ex = (e < E) ? a.experts + (size_t)e * a.L.bytes : a.shared;
+            }
 #pragma unroll
             for (int i = 0; i < RPW; ++i) {
                 const int rs = rs0 + i < nrs ? rs0 + i : nrs - 1;
@@ -680,12 +698,39 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_
     }
 }
 
+// k_route: softmax -> top-K -> renormalise of one token per block, from the
+// router's logits: the routing that k_gateup's routed blocks do for
+// themselves, as a kernel of its own for callers that need the selection
+// before the experts run (tiered residency copies the missing experts in
+// between).  Same functions, same results, same writes as k_gateup's block 0.
+template <int EPW>
+__global__ __launch_bounds__(256) void k_route(FwdArgs a) {
+    const int t = blockIdx.x, K = a.s.K, E = a.s.E;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ __align__(16) uint64_t s_cand[4 * kMaxTopK];
+    float zq[EPW];
+    load_logits_quarter<EPW>(a.ws.z + (size_t)t * E, E, zq);
+    const float gs = a.ws.gs[t];
+    route_candidates<EPW>(zq, E, K, s_cand);
+    __syncthreads();
+    if (wave == 0) {
+        const RouteSel rt = route_select(K, s_cand);
+        if (rt.rank < K) {
+            a.ws.sel[t * K + rt.rank] = rt.sel;
+            a.ws.coef[t * (K + 1) + rt.rank] = rt.w;
+            if (a.route_idx) a.route_idx[t * K + rt.rank] = rt.sel;
+            if (a.route_w) a.route_w[t * K + rt.rank] = rt.w;
+        }
+        if (lane == 0) a.ws.coef[t * (K + 1) + K] = sigmoidf_(gs);
+    }
+}
+
 constexpr int kRpwGateUp = 2;
 constexpr int kRouterTokens = 4;  // tokens per k_router_tokens block
 constexpr int kRpwDown4 = 2;  // 4-bit codes
 constexpr int kRpwDown2 = 1;  // 2-bit codes
 
-template <int BITS>
+template <int BITS, bool TIER>
 hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
     const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K, T = a.T;
     constexpr int RD = BITS == 4 ? kRpwDown4 : kRpwDown2;  // down row-steps per wave
@@ -727,12 +772,12 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
         const bool wide = E > 512;
         const bool full = G.lpr == 64;  // rows of 64 lanes: one butterfly for the whole step
         switch (G.cpl * 4 + (wide ? 2 : 0) + (full ? 1 : 0)) {
-            case 4: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 0>), grid, dim3(256), 0, st, a); break;
-            case 5: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 64>), grid, dim3(256), 0, st, a); break;
-            case 6: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 0>), grid, dim3(256), 0, st, a); break;
-            case 7: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 64>), grid, dim3(256), 0, st, a); break;
-            case 9: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 8, 64>), grid, dim3(256), 0, st, a); break;
-            case 11: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 16, 64>), grid, dim3(256), 0, st, a); break;
+            case 4: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 0, TIER>), grid, dim3(256), 0, st, a); break;
+            case 5: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 64, TIER>), grid, dim3(256), 0, st, a); break;
+            case 6: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 0, TIER>), grid, dim3(256), 0, st, a); break;
+            case 7: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 64, TIER>), grid, dim3(256), 0, st, a); break;
+            case 9: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 8, 64, TIER>), grid, dim3(256), 0, st, a); break;
+            case 11: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 16, 64, TIER>), grid, dim3(256), 0, st, a); break;
             default: return hipErrorInvalidValue;
         }
     } else if (stage == 2) {  // down + combine + residual
@@ -751,19 +796,19 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
         const bool one = K + 1 <= batch;
         const uint32_t f4r = (uint32_t)((0x100000000ull + F / 4 - 1) / (F / 4));
         if (Dm.cpl == 2) {
-            if (one) hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, true>), grid, dim3(256), lds, st, a, batch, f4r);
-            else hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, false>), grid, dim3(256), lds, st, a, batch, f4r);
+            if (one) hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r);
+            else hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r);
         } else if (Dm.cpl == 1) {
             const int key = (Dm.lpr == 64 ? 0 : Dm.lpr == 32 ? 1 : Dm.lpr == 16 ? 2 : 3) * 2 + (one ? 1 : 0);
             switch (key) {
-                case 0: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, false>), grid, dim3(256), lds, st, a, batch, f4r); break;
-                case 1: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, true>), grid, dim3(256), lds, st, a, batch, f4r); break;
-                case 2: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, false>), grid, dim3(256), lds, st, a, batch, f4r); break;
-                case 3: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, true>), grid, dim3(256), lds, st, a, batch, f4r); break;
-                case 4: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, false>), grid, dim3(256), lds, st, a, batch, f4r); break;
-                case 5: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, true>), grid, dim3(256), lds, st, a, batch, f4r); break;
-                case 6: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, false>), grid, dim3(256), lds, st, a, batch, f4r); break;
-                default: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, true>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                case 0: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                case 1: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                case 2: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                case 3: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                case 4: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                case 5: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                case 6: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                default: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
             }
         } else {
             return hipErrorInvalidValue;
@@ -778,14 +823,35 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
 
 hipError_t launch_forward_stage(const FwdArgs &a, int stage, hipStream_t stream) {
     (void)hipGetLastError();  // report only this call's launches
-    if (a.s.bits == 4) return launch_stage<4>(a, stage, stream);
-    if (a.s.bits == 2) return launch_stage<2>(a, stage, stream);
+    if (a.s.bits == 4) return launch_stage<4, false>(a, stage, stream);
+    if (a.s.bits == 2) return launch_stage<2, false>(a, stage, stream);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream) {
     for (int stage = 0; stage < kForwardStages; ++stage) {
         const hipError_t e = launch_forward_stage(a, stage, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_forward_route(const FwdArgs &a, hipStream_t stream) {
+    (void)hipGetLastError();
+    hipError_t e = a.s.bits == 4 ? launch_stage<4, false>(a, 0, stream) : launch_stage<2, false>(a, 0, stream);
+    if (e != hipSuccess) return e;
+    // experts per lane as in k_gateup: 8 up to 512 experts, else 16
+    if (a.s.E > 512) hipLaunchKernelGGL(k_route<4>, dim3(a.T), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(k_route<2>, dim3(a.T), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_forward_slots(const FwdArgs &a, hipStream_t stream) {
+    if (!a.slot_tk) return hipErrorInvalidValue;
+    (void)hipGetLastError();
+    for (int stage = 1; stage < kForwardStages; ++stage) {
+        const hipError_t e = a.s.bits == 4 ? launch_stage<4, true>(a, stage, stream)
+                                           : launch_stage<2, true>(a, stage, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -177,6 +177,9 @@ struct FwdArgs {
     int32_t *route_idx;
     float *route_w;
     Workspace ws;
+    // [T][K] device slots of the selected experts when they are read from a
+    // cache (experts = the slots' base), else null
+    const int32_t *slot_tk = nullptr;
 };
 
 constexpr int kForwardStages = 3;
@@ -200,6 +203,11 @@ hipError_t launch_grouped_stage(const FwdArgs &a, int stage, hipStream_t stream)
 hipError_t launch_batch_router(const FwdArgs &a, int stage, hipStream_t stream);
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_forward_stage(const FwdArgs &a, int stage, hipStream_t stream);
+// the per-token path with the selected experts read from cache slots (a.slot_tk):
+// stage 0 as above, then the routing alone, then (once the slots are filled)
+// stage 1 without routing and stage 2 with the slots' addresses
+hipError_t launch_forward_route(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_forward_slots(const FwdArgs &a, hipStream_t stream);
 
 struct PackArgs {
     ExpertLayout L;

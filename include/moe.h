@@ -22,8 +22,9 @@
  *
  * Conventions for every entry point:
  *  - Pointers named as device memory are HIP device pointers owned by the
- *    caller; the library never allocates, frees or synchronises.  It keeps no
- *    state between calls apart from the workspace the caller passes.
+ *    caller; the library never allocates or frees, and never synchronises
+ *    except in moe_tier_layer_forward.  It keeps no state between calls apart
+ *    from the workspace and the tier state the caller passes.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *    enqueue work; faults surface at the caller's next synchronisation.
  *  - Arguments are checked on the host before anything is enqueued; a negative
@@ -206,6 +207,84 @@ int moe_forward_stage_count(const moe_dims_t *dims, int32_t n_tokens);
 int moe_stack_forward(const moe_dims_t *dims, const moe_layer_t *layers, int32_t n_layers,
                       const float *x, float *y, int32_t n_tokens, int32_t *route_idx,
                       float *route_w, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Tiered expert residency.  The pages keep every expert on SSD and, once a
+ * layer's routing is known, read the K selected experts in parallel, leaving
+ * the operating system's LRU page cache to keep recently used experts in
+ * memory ("48GB内存运行397B模型", section "SSD流式加载：绕过统一内存瓶颈": 2.41 ms
+ * of a 4.28 ms layer is that read, about 71% of reads hit the cache; the
+ * compute and the reads run one after the other, never overlapped).  Here the
+ * backing store is host memory, HBM holds a cache of n_slots experts keyed by
+ * (layer, expert) with least-recently-used replacement, and a miss is one
+ * host-to-device DMA copy of the whole packed expert.  The dense weights
+ * (norm, router, shared gate) and the shared expert stay in device memory.
+ *
+ * A call runs the per-token kernels only (any n_tokens up to max_tokens):
+ *   1. RMSNorm + router GEMV, then softmax/top-K/renormalise on the device;
+ *   2. the selected indices are copied to the host and the calling thread
+ *      WAITS for them (the one entry point that synchronises: `stream` is
+ *      synchronised once per call);
+ *   3. cache lookups in token order, then rank order; each miss takes the
+ *      least recently used slot and enqueues a copy of the expert into it;
+ *   4. gate/up + SwiGLU and down + combine read the selected experts from
+ *      their slots.
+ * y, route_idx and route_w are bit for bit those of moe_layer_forward's
+ * per-token kernels with every expert resident.
+ *
+ * State: the cache's bookkeeping lives in host memory the caller allocates
+ * with hipHostMalloc (pinned: the indices and the slot table travel through
+ * it by DMA), moe_tier_state_bytes() bytes, 8-byte aligned; the slots live in
+ * device memory of moe_tier_device_bytes() bytes, 256-byte aligned.  Both
+ * belong to the state until the caller frees them; the library keeps no
+ * pointer elsewhere.  Calls on one state must come from one host thread at a
+ * time and use one stream.
+ */
+typedef struct moe_tier_stats {
+    uint64_t calls;        /* moe_tier_layer_forward calls that completed */
+    uint64_t lookups;      /* (token, rank) assignments looked up */
+    uint64_t hits;         /* assignments whose expert was already in a slot */
+    uint64_t misses;       /* assignments whose expert was copied in */
+    uint64_t bytes_copied; /* host-to-device bytes of those copies */
+} moe_tier_stats_t;
+
+/* Host bytes of the state for n_layers layers, n_slots device slots and calls
+ * of up to max_tokens tokens; 0 for invalid arguments (n_layers >= 1,
+ * max_tokens in 1 .. 65535, n_slots >= max_tokens * top_k so that one call's
+ * experts always fit, n_layers * n_experts < 2^31). */
+size_t moe_tier_state_bytes(const moe_dims_t *dims, int32_t n_layers, int32_t n_slots, int32_t max_tokens);
+
+/* Device bytes: n_slots packed experts (each moe_expert_bytes()) and the
+ * slot table of one call; 0 for invalid arguments. */
+size_t moe_tier_device_bytes(const moe_dims_t *dims, int32_t n_slots, int32_t max_tokens);
+
+/*
+ * Initialise a state: every slot empty, statistics zero.  `state` (pinned
+ * host, state_bytes) and `device` (device, device_bytes) as sized above.
+ * Enqueues nothing; makes no HIP call.
+ */
+int moe_tier_init(const moe_dims_t *dims, int32_t n_layers, int32_t n_slots, int32_t max_tokens,
+                  void *state, size_t state_bytes, void *device, size_t device_bytes);
+
+/*
+ * One layer through the cache.  `layer` as for moe_layer_forward except that
+ * layer->experts is HOST memory (pinned for full DMA speed) holding the layer's
+ * n_experts packed experts, expert e at byte offset e * moe_expert_bytes();
+ * layer_index (0 .. n_layers-1) names the layer in the cache's keys, so each
+ * index must always come with the same experts.  Other arguments as for
+ * moe_layer_forward, n_tokens <= max_tokens.  Returns after the copies and the
+ * expert kernels are enqueued (the routing has completed).  On MOE_ERR_HIP the
+ * state's slots may be stale: re-initialise it.
+ */
+int moe_tier_layer_forward(void *state, int32_t layer_index, const moe_layer_t *layer, const float *x,
+                           float *y, int32_t n_tokens, int32_t *route_idx, float *route_w,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Statistics since moe_tier_init. */
+int moe_tier_get_stats(const void *state, moe_tier_stats_t *out);
+
+/* *slot = the slot holding (layer_index, expert), or -1 when it is not cached. */
+int moe_tier_lookup(const void *state, int32_t layer_index, int32_t expert, int32_t *slot);
 
 /* Static text for a status code. */
 const char *moe_status_string(int status);

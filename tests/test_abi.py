@@ -229,3 +229,76 @@ def test_status_strings():
     for s in range(0, -6, -1):
         assert moe.moe_status_string(s) not in ("", "unknown status")
     assert moe.moe_status_string(-99) == "unknown status"
+
+
+# --------------------------------------------------------------------------- #
+# tiered expert residency: sizes, initialisation and argument checks (host only)
+# --------------------------------------------------------------------------- #
+def test_tier_sizes():
+    dims = d()
+    eb = moe.moe_expert_bytes(dims)
+    for ns, T in ((4, 1), (64, 16), (4096, 3)):
+        assert moe.moe_tier_device_bytes(dims, ns, T) == ns * eb + (T * 4 * 4 + 255) // 256 * 256
+    base = moe.moe_tier_state_bytes(dims, 1, 4, 1)
+    assert base > 0
+    # int32 bookkeeping: 3 per slot, 1 per (layer, expert), 2 per assignment of one call
+    assert moe.moe_tier_state_bytes(dims, 1, 5, 1) - base == 12
+    assert moe.moe_tier_state_bytes(dims, 3, 4, 1) - base == 2 * 512 * 4
+    assert moe.moe_tier_state_bytes(dims, 1, 8, 2) - moe.moe_tier_state_bytes(dims, 1, 8, 1) == 2 * 4 * 4
+    for args in ((0, 4, 1), (1, 3, 1), (1, 7, 2), (1, 4, 0), (1, 70000 * 4, 70000), (1 << 22, 4, 1)):
+        assert moe.moe_tier_state_bytes(dims, *args) == 0, args
+    assert moe.moe_tier_device_bytes(dims, 3, 1) == 0
+    assert moe.moe_tier_state_bytes(d(bits=3), 1, 4, 1) == 0
+
+
+def _tier_state(dims, n_layers, n_slots, max_tokens):
+    import numpy as np
+    buf = np.zeros(moe.moe_tier_state_bytes(dims, n_layers, n_slots, max_tokens) + 8, np.uint8)
+    addr = buf.ctypes.data
+    addr += (-addr) % 8
+    return buf, addr
+
+
+def test_tier_init_lookup_and_rejects():
+    dims = d()
+    n_layers, n_slots, max_tokens = 2, 16, 2
+    buf, st = _tier_state(dims, n_layers, n_slots, max_tokens)
+    sb = moe.moe_tier_state_bytes(dims, n_layers, n_slots, max_tokens)
+    db = moe.moe_tier_device_bytes(dims, n_slots, max_tokens)
+    f = moe._lib.moe_tier_init
+    # the device memory is never touched by init: a fake address is enough
+    assert f(ctypes.byref(dims), n_layers, n_slots, max_tokens, st, sb - 4, A, db) == moe.MOE_ERR_WORKSPACE
+    assert f(ctypes.byref(dims), n_layers, n_slots, max_tokens, st, sb, A, db - 1) == moe.MOE_ERR_WORKSPACE
+    assert f(ctypes.byref(dims), n_layers, n_slots, max_tokens, st + 4, sb, A, db) == moe.MOE_ERR_ALIGNMENT
+    assert f(ctypes.byref(dims), n_layers, n_slots, max_tokens, st, sb, A + 64, db) == moe.MOE_ERR_ALIGNMENT
+    assert f(ctypes.byref(dims), n_layers, n_slots, max_tokens, None, sb, A, db) == moe.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(dims), n_layers, 7, max_tokens, st, sb, A, db) == moe.MOE_ERR_INVALID_ARG
+    # not initialised yet: no entry point accepts the state
+    assert moe._lib.moe_tier_get_stats(st, ctypes.byref(moe.moe_tier_stats_t())) == moe.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(dims), n_layers, n_slots, max_tokens, st, sb, A, db) == moe.MOE_OK
+    s = moe.moe_tier_get_stats(st)
+    assert (s.calls, s.lookups, s.hits, s.misses, s.bytes_copied) == (0, 0, 0, 0, 0)
+    for layer in range(n_layers):
+        for e in (0, 7, 511):
+            assert moe.moe_tier_lookup(st, layer, e) == -1
+    slot = ctypes.c_int32()
+    lk = moe._lib.moe_tier_lookup
+    assert lk(st, 2, 0, ctypes.byref(slot)) == moe.MOE_ERR_INVALID_ARG
+    assert lk(st, 0, 512, ctypes.byref(slot)) == moe.MOE_ERR_INVALID_ARG
+    assert lk(st, 0, 0, None) == moe.MOE_ERR_INVALID_ARG
+    # forward: every check precedes the first HIP call
+    fw = moe._lib.moe_tier_layer_forward
+    wsb = moe.moe_workspace_bytes(dims, max_tokens + 1)
+    lay = _layer()
+
+    def call(state=st, li=0, layer=lay, T=1, ws=A + 0x500000):
+        return fw(state, li, ctypes.byref(layer) if layer else None, A + 0x300000, A + 0x400000, T, None, None,
+                  ws, wsb, None)
+
+    assert call(state=st + 8) == moe.MOE_ERR_INVALID_ARG  # not a state
+    assert call(li=-1) == moe.MOE_ERR_INVALID_ARG
+    assert call(li=n_layers) == moe.MOE_ERR_INVALID_ARG
+    assert call(T=max_tokens + 1) == moe.MOE_ERR_INVALID_ARG
+    assert call(layer=_layer(experts=None)) == moe.MOE_ERR_INVALID_ARG
+    assert call(ws=A + 0x500010) == moe.MOE_ERR_ALIGNMENT
+    assert moe.moe_tier_get_stats(st).calls == 0
