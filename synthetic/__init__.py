@@ -143,6 +143,9 @@ WORKLOADS: Dict[str, Workload] = {
                         "60 chained 4-bit layers of hidden 4096 / FFN 1024 / 512 experts, top-4, 1 token"),
     "batch32": Workload("batch32", Dims(4096, 1024, 512, 10, 4), 32, 1, 0,
                         "32 tokens, hidden 4096, FFN 1024, 512 4-bit experts, top-10 + shared"),
+    "tier4": Workload("tier4", Dims(4096, 1024, 512, 4, 4), 1, 4, 0,
+                      "4 chained 4-bit layers of hidden 4096 / FFN 1024 / 512 experts, top-4, 1 token, "
+                      "experts in pinned host memory behind an LRU cache of device slots"),
 }
 
 
