@@ -91,8 +91,8 @@ int check_forward_common(const moe_dims_t *dims, const float *x, float *y, int32
 
 // ---------------------------------------------------------------------------
 // tiered expert residency: the state the caller holds in pinned host memory,
-// a header followed by int32 arrays (the LRU lists and key map, the routing
-// landing area and the slot-table staging area); pointers into it are derived
+// a header followed by int32 arrays (the LRU lists and key map, the landing
+// area of the selection and one flag per token); pointers into it are derived
 // from its base on every call
 // ---------------------------------------------------------------------------
 constexpr uint64_t kTierMagic = 0x7265695465754d31ull;
@@ -103,7 +103,7 @@ struct TierState {
     int32_t n_layers, n_slots, max_tokens, pad;
     uint64_t expert_bytes;
     uint8_t *slots;      // device: n_slots packed experts
-    int32_t *table_dev;  // device: [max_tokens][K] slots of one call's selected experts
+    int32_t *route_dev;  // the landing area as the device addresses it (set by the first call)
     moe_tier_stats_t stats;
     int32_t head, tail;  // of the LRU list
 };
@@ -112,13 +112,13 @@ struct TierView {
     TierState *st;
     SlotLru lru;
     int32_t *route;  // [max_tokens][K] host landing area of the selected experts
-    int32_t *table;  // [max_tokens][K] host staging area of their slots
 };
 
 constexpr size_t tier_header_bytes() { return (sizeof(TierState) + 255) / 256 * 256; }
 
 size_t tier_ints(const moe_dims_t *d, int32_t n_layers, int32_t n_slots, int32_t max_tokens) {
-    return SlotLru::ints(n_slots, n_layers * d->n_experts) + 2 * (size_t)max_tokens * d->top_k;
+    // the LRU, the selection of one call and one flag per token
+    return SlotLru::ints(n_slots, n_layers * d->n_experts) + (size_t)max_tokens * d->top_k + max_tokens;
 }
 
 int check_tier_args(const moe_dims_t *dims, int32_t n_layers, int32_t n_slots, int32_t max_tokens) {
@@ -127,11 +127,8 @@ int check_tier_args(const moe_dims_t *dims, int32_t n_layers, int32_t n_slots, i
     if (n_layers < 1 || max_tokens < 1 || max_tokens > 65535) return MOE_ERR_INVALID_ARG;
     if ((int64_t)n_layers * dims->n_experts >= ((int64_t)1 << 31)) return MOE_ERR_INVALID_ARG;
     if ((int64_t)n_slots < (int64_t)max_tokens * dims->top_k) return MOE_ERR_INVALID_ARG;
+    if (max_tokens * dims->top_k > kSlotArgs) return MOE_ERR_UNSUPPORTED;  // the slots travel as kernel arguments
     return MOE_OK;
-}
-
-size_t tier_table_bytes(const moe_dims_t *d, int32_t max_tokens) {
-    return ((size_t)max_tokens * d->top_k * sizeof(int32_t) + kAlign - 1) / kAlign * kAlign;
 }
 
 // the view of a state (the list is read back from the header; store_lru writes it)
@@ -149,7 +146,6 @@ TierView tier_view(void *state) {
     v.lru.head = v.st->head;
     v.lru.tail = v.st->tail;
     v.route = ints + SlotLru::ints(ns, nk);
-    v.table = v.route + (size_t)v.st->max_tokens * v.st->dims.top_k;
     return v;
 }
 
@@ -312,7 +308,7 @@ size_t moe_tier_state_bytes(const moe_dims_t *dims, int32_t n_layers, int32_t n_
 size_t moe_tier_device_bytes(const moe_dims_t *dims, int32_t n_slots, int32_t max_tokens) {
     if (check_tier_args(dims, 1, n_slots, max_tokens) != MOE_OK) return 0;
     const size_t eb = make_layout(dims->hidden, dims->ffn, dims->bits).bytes;
-    return (size_t)n_slots * eb + tier_table_bytes(dims, max_tokens);
+    return (size_t)n_slots * eb;
 }
 
 int moe_tier_init(const moe_dims_t *dims, int32_t n_layers, int32_t n_slots, int32_t max_tokens, void *state,
@@ -331,7 +327,7 @@ int moe_tier_init(const moe_dims_t *dims, int32_t n_layers, int32_t n_slots, int
     st->max_tokens = max_tokens;
     st->expert_bytes = make_layout(dims->hidden, dims->ffn, dims->bits).bytes;
     st->slots = (uint8_t *)device;
-    st->table_dev = (int32_t *)(st->slots + (size_t)n_slots * st->expert_bytes);
+    st->route_dev = nullptr;
     TierView v = tier_view(state);
     v.lru.init(n_slots, n_layers * dims->n_experts, v.lru.key);
     store_lru(v);
@@ -354,22 +350,50 @@ int moe_tier_layer_forward(void *state, int32_t layer_index, const moe_layer_t *
     const hipStream_t hs = (hipStream_t)stream;
     FwdArgs a = make_fwd(dims, layer, x, y, n_tokens, route_idx, route_w, workspace);
     const int K = dims->top_k, E = dims->n_experts, n = n_tokens * K;
-    // 1. norm, router and routing; 2. the selection to the host
+    // 1. norm, router and routing; the routing kernel also writes the selection
+    // into the state (pinned host memory, mapped into the device's address space)
+    if (!st->route_dev) {
+        void *p = nullptr;
+        if (hipHostGetDevicePointer(&p, v.route, 0) != hipSuccess || !p) return MOE_ERR_INVALID_ARG;  // not pinned
+        st->route_dev = (int32_t *)p;
+    }
+    // each token's block then raises its flag (after the state's selection
+    // area); flags are cleared before the launch and raised to an odd value
+    // that changes from call to call
+    a.sel_host = st->route_dev;
+    a.flag_host = st->route_dev + n_tokens * K;
+    a.flag_value = (int32_t)(st->stats.calls + 1) * 2 + 1;
+    volatile int32_t *flags = (volatile int32_t *)(v.route + n_tokens * K);
+    for (int t = 0; t < n_tokens; ++t) flags[t] = 0;
     if (hip_status(launch_forward_route(a, hs)) != MOE_OK) return MOE_ERR_HIP;
-    if (hip_status(hipMemcpyAsync(v.route, a.ws.sel, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost, hs)) !=
-        MOE_OK)
-        return MOE_ERR_HIP;
-    if (hip_status(hipStreamSynchronize(hs)) != MOE_OK) return MOE_ERR_HIP;
+    // 2. wait for it by polling the flags: the thread sees the selection as soon
+    // as it lands, where a stream synchronisation would add the runtime's
+    // completion signal and the thread's wake-up to every layer.  A flag that
+    // never rises (a failed launch) ends the spin after ~1e8 polls: the stream
+    // is then synchronised, which reports the error.
+    {
+        long spins = 0;
+        for (int t = 0; t < n_tokens; ++t) {
+            while (flags[t] != a.flag_value) {
+                if (++spins > 100000000L) {
+                    if (hip_status(hipStreamSynchronize(hs)) != MOE_OK) return MOE_ERR_HIP;
+                    if (flags[t] != a.flag_value) return hip_status(hipErrorUnknown);
+                }
+            }
+        }
+        __atomic_thread_fence(__ATOMIC_ACQUIRE);
+    }
     // 3. lookups in token order, then rank order; a miss copies the expert in
     const uint8_t *host = (const uint8_t *)layer->experts;
     const size_t eb = st->expert_bytes;
+    SlotArgs sl;
     for (int i = 0; i < n; ++i) {
-        const int32_t e = v.route[i];
+        const int32_t e = ((volatile const int32_t *)v.route)[i];
         if (e < 0 || e >= E) return hip_status(hipErrorUnknown);  // cannot happen: routing selects valid experts
         bool hit;
         const int32_t slot = v.lru.acquire(layer_index * E + e, &hit);
         store_lru(v);
-        v.table[i] = slot;
+        sl.s[i] = slot;
         st->stats.lookups += 1;
         if (hit) {
             st->stats.hits += 1;
@@ -381,13 +405,12 @@ int moe_tier_layer_forward(void *state, int32_t layer_index, const moe_layer_t *
             return MOE_ERR_HIP;
         st->stats.bytes_copied += eb;
     }
-    // 4. the slot table, then the expert kernels reading from the slots
-    if (hip_status(hipMemcpyAsync(st->table_dev, v.table, (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice, hs)) !=
-        MOE_OK)
-        return MOE_ERR_HIP;
+    // 4. the expert kernels, reading the selected experts from their slots
+    // (passed as kernel arguments)
+    a.sel_host = nullptr;
+    a.flag_host = nullptr;
     a.experts = st->slots;
-    a.slot_tk = st->table_dev;
-    if (hip_status(launch_forward_slots(a, hs)) != MOE_OK) return MOE_ERR_HIP;
+    if (hip_status(launch_forward_slots(a, sl, hs)) != MOE_OK) return MOE_ERR_HIP;
     st->stats.calls += 1;
     return MOE_OK;
 }

@@ -357,9 +357,9 @@ __global__ __launch_bounds__(256) void k_router_tokens(FwdArgs a) {
 // LPR: lanes per row when the step's partial sums are reduced together (64);
 // 0: one reduction per row
 // TIER: the selected experts' routing is already done (k_route) and their
-// weights sit in cache slots, a.slot_tk[t][rank] (a.experts = the slots' base)
+// weights sit in cache slots, sl.s[t * K + rank] (a.experts = the slots' base)
 template <int BITS, int CPL, int RPW, int EPL, int LPR, bool TIER>
-__global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
+__global__ __launch_bounds__(256) void k_gateup(FwdArgs a, SlotParam<TIER> sl) {
     using Q = QSlice<BITS, CPL>;
     const int t = blockIdx.y;
     const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K;
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a) {
         for (int i = 0; i < RPW; ++i) {
             const int rs = rs0 + i < nrs ? rs0 + i : nrs - 1;
             const int s = (rs * rpi) / F;
-            er[i] = a.slot_tk[t * K + (s < K ? s : K - 1)];
+            if constexpr (TIER) er[i] = sl.s[t * K + (s < K ? s : K - 1)];
         }
         issue_loads(er);
     } else if (!wave_shared_only) {
@@ -547,10 +547,10 @@ constexpr int kDownStageValues = 5120;  // activations staged per batch (batch *
 // 0: one reduction per row
 // ONE: all K+1 slots in a single batch (straight-line code: no loop-header
 // wait holds back the first loads)
-// TIER: the selected experts sit in cache slots, a.slot_tk[t][rank] (a.experts
+// TIER: the selected experts sit in cache slots, sl.s[t * K + rank] (a.experts
 // = the slots' base)
 template <int BITS, int CPL, int RPW, int LPR, bool ONE, bool TIER>
-__global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_recip) {
+__global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_recip, SlotParam<TIER> sl) {
     using Q = QSlice<BITS, CPL>;
     const int t = blockIdx.y;
     const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K;
@@ -581,7 +581,9 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_
     // lane s (s <= K) holds slot s: expert index (s < K) and combine
     // coefficient; only those lanes are ever read (unconditional loads, lanes
     // past the end read a valid entry)
-    const int my_e = (TIER ? a.slot_tk : a.ws.sel)[t * K + (lane < K ? lane : K - 1)];
+    int my_e;
+    if constexpr (TIER) my_e = sl.s[t * K + (lane < K ? lane : K - 1)];
+    else my_e = a.ws.sel[t * K + (lane < K ? lane : K - 1)];
     const float my_c = a.ws.coef[t * (K + 1) + (lane <= K ? lane : K)];
 
     float acc[RPW];
@@ -720,8 +722,14 @@ __global__ __launch_bounds__(256) void k_route(FwdArgs a) {
             a.ws.coef[t * (K + 1) + rt.rank] = rt.w;
             if (a.route_idx) a.route_idx[t * K + rt.rank] = rt.sel;
             if (a.route_w) a.route_w[t * K + rt.rank] = rt.w;
+            if (a.sel_host) a.sel_host[t * K + rt.rank] = rt.sel;
         }
         if (lane == 0) a.ws.coef[t * (K + 1) + K] = sigmoidf_(gs);
+        if (a.flag_host) {  // the selection first, then the flag, both pushed out to the host
+            __threadfence_system();
+            if (lane == 0) a.flag_host[t] = a.flag_value;
+            __threadfence_system();
+        }
     }
 }
 
@@ -731,7 +739,7 @@ constexpr int kRpwDown4 = 2;  // 4-bit codes
 constexpr int kRpwDown2 = 1;  // 2-bit codes
 
 template <int BITS, bool TIER>
-hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
+hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st, const SlotParam<TIER> &sl = {}) {
     const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K, T = a.T;
     constexpr int RD = BITS == 4 ? kRpwDown4 : kRpwDown2;  // down row-steps per wave
     if (stage == 0 && (H == 2048 || H == 4096)) {  // RMSNorm + router + limbs of h, H split over 4 waves
@@ -772,12 +780,12 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
         const bool wide = E > 512;
         const bool full = G.lpr == 64;  // rows of 64 lanes: one butterfly for the whole step
         switch (G.cpl * 4 + (wide ? 2 : 0) + (full ? 1 : 0)) {
-            case 4: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 0, TIER>), grid, dim3(256), 0, st, a); break;
-            case 5: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 64, TIER>), grid, dim3(256), 0, st, a); break;
-            case 6: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 0, TIER>), grid, dim3(256), 0, st, a); break;
-            case 7: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 64, TIER>), grid, dim3(256), 0, st, a); break;
-            case 9: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 8, 64, TIER>), grid, dim3(256), 0, st, a); break;
-            case 11: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 16, 64, TIER>), grid, dim3(256), 0, st, a); break;
+            case 4: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 0, TIER>), grid, dim3(256), 0, st, a, sl); break;
+            case 5: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 64, TIER>), grid, dim3(256), 0, st, a, sl); break;
+            case 6: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 0, TIER>), grid, dim3(256), 0, st, a, sl); break;
+            case 7: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 64, TIER>), grid, dim3(256), 0, st, a, sl); break;
+            case 9: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 8, 64, TIER>), grid, dim3(256), 0, st, a, sl); break;
+            case 11: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 16, 64, TIER>), grid, dim3(256), 0, st, a, sl); break;
             default: return hipErrorInvalidValue;
         }
     } else if (stage == 2) {  // down + combine + residual
@@ -796,19 +804,19 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st) {
         const bool one = K + 1 <= batch;
         const uint32_t f4r = (uint32_t)((0x100000000ull + F / 4 - 1) / (F / 4));
         if (Dm.cpl == 2) {
-            if (one) hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r);
-            else hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r);
+            if (one) hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl);
+            else hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl);
         } else if (Dm.cpl == 1) {
             const int key = (Dm.lpr == 64 ? 0 : Dm.lpr == 32 ? 1 : Dm.lpr == 16 ? 2 : 3) * 2 + (one ? 1 : 0);
             switch (key) {
-                case 0: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
-                case 1: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
-                case 2: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
-                case 3: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
-                case 4: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
-                case 5: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
-                case 6: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
-                default: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r); break;
+                case 0: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
+                case 1: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
+                case 2: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
+                case 3: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
+                case 4: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
+                case 5: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
+                case 6: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
+                default: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
             }
         } else {
             return hipErrorInvalidValue;
@@ -846,12 +854,12 @@ hipError_t launch_forward_route(const FwdArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_forward_slots(const FwdArgs &a, hipStream_t stream) {
-    if (!a.slot_tk) return hipErrorInvalidValue;
+hipError_t launch_forward_slots(const FwdArgs &a, const SlotArgs &slots, hipStream_t stream) {
+    if (a.T * a.s.K > kSlotArgs) return hipErrorInvalidValue;
     (void)hipGetLastError();
     for (int stage = 1; stage < kForwardStages; ++stage) {
-        const hipError_t e = a.s.bits == 4 ? launch_stage<4, true>(a, stage, stream)
-                                           : launch_stage<2, true>(a, stage, stream);
+        const hipError_t e = a.s.bits == 4 ? launch_stage<4, true>(a, stage, stream, slots)
+                                           : launch_stage<2, true>(a, stage, stream, slots);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe_layout.h"
 
 namespace moe {
@@ -177,10 +179,24 @@ struct FwdArgs {
     int32_t *route_idx;
     float *route_w;
     Workspace ws;
-    // [T][K] device slots of the selected experts when they are read from a
-    // cache (experts = the slots' base), else null
-    const int32_t *slot_tk = nullptr;
+    // k_route only: where the selection also goes (host memory mapped into the
+    // device's address space), or null; flag_host[t] is set to flag_value once
+    // token t's selection is visible there
+    int32_t *sel_host = nullptr;
+    int32_t *flag_host = nullptr;
+    int32_t flag_value = 0;
 };
+
+// Slots of one call's selected experts, [T][K] with T*K <= kSlotArgs, passed
+// by value to the expert kernels when the experts are read from cache slots
+// (tiered residency); the kernels of the resident path take an empty one.
+constexpr int kSlotArgs = 64;
+struct SlotArgs {
+    int32_t s[kSlotArgs];
+};
+struct NoSlotArgs {};
+template <bool TIER>
+using SlotParam = typename std::conditional<TIER, SlotArgs, NoSlotArgs>::type;
 
 constexpr int kForwardStages = 3;
 // Batches of at least kGroupMinAssign assignments (tokens x top-K) and at most
@@ -203,11 +219,12 @@ hipError_t launch_grouped_stage(const FwdArgs &a, int stage, hipStream_t stream)
 hipError_t launch_batch_router(const FwdArgs &a, int stage, hipStream_t stream);
 hipError_t launch_forward(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_forward_stage(const FwdArgs &a, int stage, hipStream_t stream);
-// the per-token path with the selected experts read from cache slots (a.slot_tk):
-// stage 0 as above, then the routing alone, then (once the slots are filled)
-// stage 1 without routing and stage 2 with the slots' addresses
+// the per-token path with the selected experts read from cache slots: stage 0
+// as above, then the routing alone (launch_forward_route), then, once the slots
+// are filled, stage 1 without routing and stage 2, both addressing the experts
+// as a.experts + slot * bytes (launch_forward_slots, T*K <= kSlotArgs)
 hipError_t launch_forward_route(const FwdArgs &a, hipStream_t stream);
-hipError_t launch_forward_slots(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_forward_slots(const FwdArgs &a, const SlotArgs &slots, hipStream_t stream);
 
 struct PackArgs {
     ExpertLayout L;

@@ -220,22 +220,26 @@ int moe_stack_forward(const moe_dims_t *dims, const moe_layer_t *layers, int32_t
  * host-to-device DMA copy of the whole packed expert.  The dense weights
  * (norm, router, shared gate) and the shared expert stay in device memory.
  *
- * A call runs the per-token kernels only (any n_tokens up to max_tokens):
- *   1. RMSNorm + router GEMV, then softmax/top-K/renormalise on the device;
- *   2. the selected indices are copied to the host and the calling thread
- *      WAITS for them (the one entry point that synchronises: `stream` is
- *      synchronised once per call);
+ * A call runs the per-token kernels only (n_tokens up to max_tokens):
+ *   1. RMSNorm + router GEMV, then softmax/top-K/renormalise on the device,
+ *      which also writes the selected indices into the state and raises a
+ *      flag there per token;
+ *   2. the calling thread WAITS for them, spinning on those flags (the one
+ *      entry point that synchronises; a flag that does not rise within ~1e8
+ *      polls, as after a failed launch, makes it synchronise `stream` and
+ *      report the error);
  *   3. cache lookups in token order, then rank order; each miss takes the
  *      least recently used slot and enqueues a copy of the expert into it;
  *   4. gate/up + SwiGLU and down + combine read the selected experts from
- *      their slots.
+ *      their slots, whose numbers travel in the kernel arguments (hence at
+ *      most 64 assignments, max_tokens * top_k <= 64, per call).
  * y, route_idx and route_w are bit for bit those of moe_layer_forward's
  * per-token kernels with every expert resident.
  *
  * State: the cache's bookkeeping lives in host memory the caller allocates
- * with hipHostMalloc (pinned: the indices and the slot table travel through
- * it by DMA), moe_tier_state_bytes() bytes, 8-byte aligned; the slots live in
- * device memory of moe_tier_device_bytes() bytes, 256-byte aligned.  Both
+ * with hipHostMalloc (pinned and mapped: the routing kernel writes the
+ * indices into it), moe_tier_state_bytes() bytes, 8-byte aligned; the slots
+ * live in device memory of moe_tier_device_bytes() bytes, 256-byte aligned.  Both
  * belong to the state until the caller frees them; the library keeps no
  * pointer elsewhere.  Calls on one state must come from one host thread at a
  * time and use one stream.
@@ -249,19 +253,21 @@ typedef struct moe_tier_stats {
 } moe_tier_stats_t;
 
 /* Host bytes of the state for n_layers layers, n_slots device slots and calls
- * of up to max_tokens tokens; 0 for invalid arguments (n_layers >= 1,
- * max_tokens in 1 .. 65535, n_slots >= max_tokens * top_k so that one call's
- * experts always fit, n_layers * n_experts < 2^31). */
+ * of up to max_tokens tokens; 0 for invalid or unsupported arguments
+ * (n_layers >= 1, max_tokens >= 1 with max_tokens * top_k <= 64,
+ * n_slots >= max_tokens * top_k so that one call's experts always fit,
+ * n_layers * n_experts < 2^31). */
 size_t moe_tier_state_bytes(const moe_dims_t *dims, int32_t n_layers, int32_t n_slots, int32_t max_tokens);
 
-/* Device bytes: n_slots packed experts (each moe_expert_bytes()) and the
- * slot table of one call; 0 for invalid arguments. */
+/* Device bytes: n_slots packed experts, n_slots * moe_expert_bytes(); 0 for
+ * invalid or unsupported arguments. */
 size_t moe_tier_device_bytes(const moe_dims_t *dims, int32_t n_slots, int32_t max_tokens);
 
 /*
  * Initialise a state: every slot empty, statistics zero.  `state` (pinned
  * host, state_bytes) and `device` (device, device_bytes) as sized above.
- * Enqueues nothing; makes no HIP call.
+ * Enqueues nothing; makes no HIP call.  max_tokens * top_k > 64 is
+ * MOE_ERR_UNSUPPORTED.
  */
 int moe_tier_init(const moe_dims_t *dims, int32_t n_layers, int32_t n_slots, int32_t max_tokens,
                   void *state, size_t state_bytes, void *device, size_t device_bytes);
@@ -273,8 +279,9 @@ int moe_tier_init(const moe_dims_t *dims, int32_t n_layers, int32_t n_slots, int
  * layer_index (0 .. n_layers-1) names the layer in the cache's keys, so each
  * index must always come with the same experts.  Other arguments as for
  * moe_layer_forward, n_tokens <= max_tokens.  Returns after the copies and the
- * expert kernels are enqueued (the routing has completed).  On MOE_ERR_HIP the
- * state's slots may be stale: re-initialise it.
+ * expert kernels are enqueued (the routing has completed).  A state whose
+ * memory is not pinned host memory is MOE_ERR_INVALID_ARG.  On MOE_ERR_HIP
+ * the state's slots may be stale: re-initialise it.
  */
 int moe_tier_layer_forward(void *state, int32_t layer_index, const moe_layer_t *layer, const float *x,
                            float *y, int32_t n_tokens, int32_t *route_idx, float *route_w,

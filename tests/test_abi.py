@@ -238,16 +238,20 @@ def test_tier_sizes():
     dims = d()
     eb = moe.moe_expert_bytes(dims)
     for ns, T in ((4, 1), (64, 16), (4096, 3)):
-        assert moe.moe_tier_device_bytes(dims, ns, T) == ns * eb + (T * 4 * 4 + 255) // 256 * 256
+        assert moe.moe_tier_device_bytes(dims, ns, T) == ns * eb
     base = moe.moe_tier_state_bytes(dims, 1, 4, 1)
     assert base > 0
-    # int32 bookkeeping: 3 per slot, 1 per (layer, expert), 2 per assignment of one call
+    # int32 bookkeeping: 3 per slot, 1 per (layer, expert), 1 per assignment of one call, 1 per token
     assert moe.moe_tier_state_bytes(dims, 1, 5, 1) - base == 12
     assert moe.moe_tier_state_bytes(dims, 3, 4, 1) - base == 2 * 512 * 4
-    assert moe.moe_tier_state_bytes(dims, 1, 8, 2) - moe.moe_tier_state_bytes(dims, 1, 8, 1) == 2 * 4 * 4
+    assert moe.moe_tier_state_bytes(dims, 1, 8, 2) - moe.moe_tier_state_bytes(dims, 1, 8, 1) == 5 * 4
+    # at most 64 assignments per call (the slots travel as kernel arguments)
+    assert moe.moe_tier_state_bytes(dims, 1, 64, 16) > 0
+    assert moe.moe_tier_state_bytes(dims, 1, 68, 17) == 0
     for args in ((0, 4, 1), (1, 3, 1), (1, 7, 2), (1, 4, 0), (1, 70000 * 4, 70000), (1 << 22, 4, 1)):
         assert moe.moe_tier_state_bytes(dims, *args) == 0, args
     assert moe.moe_tier_device_bytes(dims, 3, 1) == 0
+    assert moe.moe_tier_device_bytes(dims, 68, 17) == 0
     assert moe.moe_tier_state_bytes(d(bits=3), 1, 4, 1) == 0
 
 
@@ -273,6 +277,7 @@ def test_tier_init_lookup_and_rejects():
     assert f(ctypes.byref(dims), n_layers, n_slots, max_tokens, st, sb, A + 64, db) == moe.MOE_ERR_ALIGNMENT
     assert f(ctypes.byref(dims), n_layers, n_slots, max_tokens, None, sb, A, db) == moe.MOE_ERR_INVALID_ARG
     assert f(ctypes.byref(dims), n_layers, 7, max_tokens, st, sb, A, db) == moe.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(dims), n_layers, 68, 17, st, sb, A, db) == moe.MOE_ERR_UNSUPPORTED
     # not initialised yet: no entry point accepts the state
     assert moe._lib.moe_tier_get_stats(st, ctypes.byref(moe.moe_tier_stats_t())) == moe.MOE_ERR_INVALID_ARG
     assert f(ctypes.byref(dims), n_layers, n_slots, max_tokens, st, sb, A, db) == moe.MOE_OK

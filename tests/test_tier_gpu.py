@@ -127,3 +127,10 @@ def test_full_size_layers(moe):
     # two 4096/1024 layers of 512 experts (7.1 GB of pinned host memory)
     dims = syn.WORKLOADS["layer4"].dims
     _run(moe, dims, 2, 20, 4, [1, 4, 2, 1, 3, 1], oracle_first=True)
+
+
+def test_sixty_four_assignments(moe):
+    # the most a call carries (64 slots in the kernel arguments): 16 tokens x
+    # top-4, and 4 tokens x top-16
+    _run(moe, syn.Dims(256, 128, 64, 4, 4), 1, 80, 16, [16, 5, 16, 1, 16])
+    _run(moe, syn.Dims(256, 128, 64, 16, 4), 2, 64, 4, [4, 1, 4, 3])
