@@ -444,22 +444,24 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a, SlotParam<TIER> sl) {
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    if (active && wave_shared_only) {
+    if constexpr (TIER) {  // the slots are known: every wave issues its loads now
+        if (active) {
+            int er[RPW];
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) {
+                const int rs = rs0 + i < nrs ? rs0 + i : nrs - 1;
+                const int s = (rs * rpi) / F;
+                er[i] = sl.s[t * K + (s < K ? s : K - 1)];
+            }
+            issue_loads(er);
+        }
+    } else if (active && wave_shared_only) {
         const int none[RPW] = {};
         issue_loads(none);
     }
     __syncthreads();
     if (!active) return;
-    if (TIER && !wave_shared_only) {
-        int er[RPW];
-#pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-            const int rs = rs0 + i < nrs ? rs0 + i : nrs - 1;
-            const int s = (rs * rpi) / F;
-            if constexpr (TIER) er[i] = sl.s[t * K + (s < K ? s : K - 1)];
-        }
-        issue_loads(er);
-    } else if (!wave_shared_only) {
+    if (!TIER && !wave_shared_only) {
         // every routed wave ranks the block's candidates itself
         const RouteSel rt = route_select(K, s_cand);
         if (blockIdx.x == 0 && wave == 0) {
