@@ -40,14 +40,14 @@ HBM_PEAK_BPS = 8.0e12  # MI355X HBM3E peak
 # was measured on.  FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0, the ratios
 # of bytes moved to counts reported for a 256 MiB copy.
 KERNEL_TRAFFIC = {
-    ("layer4", "k_gateup"): {"source_sha256_prefix": "55187462176ef0e0", "fetch_kib": 11640.0, "write_kib": 20.1,
+    ("layer4", "k_gateup"): {"source_sha256_prefix": "306036de03c785e1", "fetch_kib": 11638.5, "write_kib": 20.1,
                              "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer4", "k_down"): {"source_sha256_prefix": "55187462176ef0e0", "fetch_kib": 5929.5, "write_kib": 16.0,
+    ("layer4", "k_down"): {"source_sha256_prefix": "306036de03c785e1", "fetch_kib": 5929.5, "write_kib": 16.0,
                            "fetch_scale": 2.0, "write_scale": 1.0},
-    ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "a48b728bce8341ee", "fetch_kib": 576624.5,
-                                      "write_kib": 3622.4, "fetch_scale": 2.0, "write_scale": 1.0},
-    ("batch32", "k_grouped_down"): {"source_sha256_prefix": "a48b728bce8341ee", "fetch_kib": 289856.0,
-                                    "write_kib": 6144.9, "fetch_scale": 2.0, "write_scale": 1.0},
+    ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "5e1f1a738532520d", "fetch_kib": 576521.5,
+                                      "write_kib": 3621.6, "fetch_scale": 2.0, "write_scale": 1.0},
+    ("batch32", "k_grouped_down"): {"source_sha256_prefix": "5e1f1a738532520d", "fetch_kib": 289807.9,
+                                    "write_kib": 6144.7, "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
 
