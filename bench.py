@@ -40,9 +40,9 @@ HBM_PEAK_BPS = 8.0e12  # MI355X HBM3E peak
 # was measured on.  FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0, the ratios
 # of bytes moved to counts reported for a 256 MiB copy.
 KERNEL_TRAFFIC = {
-    ("layer4", "k_gateup"): {"source_sha256_prefix": "306036de03c785e1", "fetch_kib": 11638.5, "write_kib": 20.1,
+    ("layer4", "k_gateup"): {"source_sha256_prefix": "378d3af22b5eb1f8", "fetch_kib": 11638.5, "write_kib": 20.1,
                              "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer4", "k_down"): {"source_sha256_prefix": "306036de03c785e1", "fetch_kib": 5929.5, "write_kib": 16.0,
+    ("layer4", "k_down"): {"source_sha256_prefix": "378d3af22b5eb1f8", "fetch_kib": 5929.5, "write_kib": 16.0,
                            "fetch_scale": 2.0, "write_scale": 1.0},
     ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "5e1f1a738532520d", "fetch_kib": 576521.5,
                                       "write_kib": 3621.6, "fetch_scale": 2.0, "write_scale": 1.0},

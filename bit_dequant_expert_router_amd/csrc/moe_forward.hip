@@ -7,12 +7,17 @@
 //   k_gateup : per block, softmax/top-K/renormalise from the logits, then the
 //              fused gate+up dequant GEMV of the selected experts and the
 //              shared expert with SwiGLU in registers
-//
-// A batch runs one row of blocks per token (grid.y); batches from 100
-// assignments (tokens x top-K) take the grouped kernels instead.
 //   k_down   : down-projection dequant GEMV of all K+1 experts for a set of
 //              output rows, weighted combine, sigmoid-gated shared expert and
 //              residual, written once per row (no atomics, deterministic)
+//
+// A batch runs one row of blocks per token (grid.y); batches from 100
+// assignments (tokens x top-K) take the grouped kernels instead.
+//
+// Tiered residency (experts read from cache slots) runs k_router, then
+// k_route (the routing alone, its selection also written to host memory),
+// then, once the host has filled the slots, the TIER variants of k_gateup
+// (no routing) and k_down, which address the selected experts by slot.
 //
 // Sources of each step: RMSNorm in two passes, the FMA form of the 4-bit
 // dequant mat-vec, fused SwiGLU, fused combine + residual + sigmoid gate:

@@ -149,3 +149,24 @@ def test_nan_token(moe):
     # outputs are NaN, the other tokens' are finite, all as on the resident path
     dims = syn.WORKLOADS["tiny"].dims
     _run(moe, dims, 2, 6, 3, [3, 1, 3], nan_token=1)
+
+
+def test_state_not_pinned_is_rejected(moe):
+    # the routing kernel writes into the state, so pageable memory is refused
+    # before anything is launched
+    dims = syn.WORKLOADS["tiny"].dims
+    lws, hosts = _layers(dims, 1, 0)
+    state = torch.zeros(moe.moe_tier_state_bytes(dims, 1, 4, 1), dtype=torch.uint8)  # pageable
+    dev = torch.empty(moe.moe_tier_device_bytes(dims, 4, 1), dtype=torch.uint8, device="cuda")
+    moe.moe_tier_init(dims, 1, 4, 1, state, dev)
+    ws = torch.empty(moe.moe_workspace_bytes(dims, 1), dtype=torch.uint8, device="cuda")
+    moe.moe_workspace_init(ws)
+    x = torch.from_numpy(syn.tokens(0, 1, dims.hidden)).cuda()
+    y = torch.empty_like(x)
+    lw = lws[0]
+    layer = moe.make_layer(lw.norm_weight, lw.router_weight, lw.shared_gate, hosts[0], lw.shared)
+    with pytest.raises(moe.MoeError) as err:
+        moe.moe_tier_layer_forward(state, 0, layer, x, y, 1, None, None, ws)
+    assert err.value.status == moe.MOE_ERR_INVALID_ARG
+    assert moe.moe_tier_get_stats(state).calls == 0
+    torch.cuda.synchronize()
