@@ -383,10 +383,15 @@ int moe_tier_layer_forward(void *state, int32_t layer_index, const moe_layer_t *
         }
         __atomic_thread_fence(__ATOMIC_ACQUIRE);
     }
-    // 3. lookups in token order, then rank order; a miss copies the expert in
+    // 3. lookups in token order, then rank order; a miss takes a slot and is
+    // listed for copying
     const uint8_t *host = (const uint8_t *)layer->experts;
     const size_t eb = st->expert_bytes;
     SlotArgs sl;
+    FetchArgs fa;
+    fa.n = 0;
+    fa.dst = st->slots;
+    fa.bytes = eb;
     for (int i = 0; i < n; ++i) {
         const int32_t e = ((volatile const int32_t *)v.route)[i];
         if (e < 0 || e >= E) return hip_status(hipErrorUnknown);  // cannot happen: routing selects valid experts
@@ -400,10 +405,27 @@ int moe_tier_layer_forward(void *state, int32_t layer_index, const moe_layer_t *
             continue;
         }
         st->stats.misses += 1;
-        if (hip_status(hipMemcpyAsync(st->slots + (size_t)slot * eb, host + (size_t)e * eb, eb,
-                                      hipMemcpyHostToDevice, hs)) != MOE_OK)
-            return MOE_ERR_HIP;
+        fa.expert[fa.n] = e;
+        fa.slot[fa.n] = slot;
+        fa.n += 1;
         st->stats.bytes_copied += eb;
+    }
+    // the misses' copies: one kernel reading the host store over the link
+    // (56.9 GB/s per miss, against 52.9 for one DMA copy per expert, whose
+    // engine idles between copies); a store that is not mapped pinned memory
+    // is copied by DMA instead
+    if (fa.n > 0) {
+        void *p = nullptr;
+        if (hipHostGetDevicePointer(&p, (void *)host, 0) == hipSuccess && p) {
+            fa.src = (const uint8_t *)p;
+            if (hip_status(launch_fetch(fa, hs)) != MOE_OK) return MOE_ERR_HIP;
+        } else {
+            (void)hipGetLastError();
+            for (int i = 0; i < fa.n; ++i)
+                if (hip_status(hipMemcpyAsync(st->slots + (size_t)fa.slot[i] * eb, host + (size_t)fa.expert[i] * eb,
+                                              eb, hipMemcpyHostToDevice, hs)) != MOE_OK)
+                    return MOE_ERR_HIP;
+        }
     }
     // 4. the expert kernels, reading the selected experts from their slots
     // (passed as kernel arguments)

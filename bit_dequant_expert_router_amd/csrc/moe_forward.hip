@@ -16,8 +16,9 @@
 //
 // Tiered residency (experts read from cache slots) runs k_router, then
 // k_route (the routing alone, its selection also written to host memory),
-// then, once the host has filled the slots, the TIER variants of k_gateup
-// (no routing) and k_down, which address the selected experts by slot.
+// then, once the host has chosen the slots, k_fetch (the missing experts
+// from host memory into their slots) and the TIER variants of k_gateup (no
+// routing) and k_down, which address the selected experts by slot.
 //
 // Sources of each step: RMSNorm in two passes, the FMA form of the 4-bit
 // dequant mat-vec, fused SwiGLU, fused combine + residual + sigmoid gate:
@@ -740,6 +741,21 @@ __global__ __launch_bounds__(256) void k_route(FwdArgs a) {
     }
 }
 
+// k_fetch: whole experts from host memory into cache slots over the host
+// link; each block copies its share of every listed expert (a few dozen
+// blocks keep the link busy; more only add contention)
+__global__ __launch_bounds__(256) void k_fetch(FetchArgs f) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const uint64_t n16 = f.bytes / 16;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (int i = 0; i < f.n; ++i) {
+        const v4u *src = (const v4u *)(f.src + (uint64_t)f.expert[i] * f.bytes);
+        v4u *dst = (v4u *)(f.dst + (uint64_t)f.slot[i] * f.bytes);
+        for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n16; j += stride)
+            dst[j] = __builtin_nontemporal_load(src + j);
+    }
+}
+
 constexpr int kRpwGateUp = 2;
 constexpr int kRouterTokens = 4;  // tokens per k_router_tokens block
 constexpr int kRpwDown4 = 2;  // 4-bit codes
@@ -849,6 +865,13 @@ hipError_t launch_forward(const FwdArgs &a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_fetch(const FetchArgs &f, hipStream_t stream) {
+    if (f.n < 1 || f.n > kSlotArgs || f.bytes % 16 != 0) return hipErrorInvalidValue;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_fetch, dim3(64), dim3(256), 0, stream, f);
+    return hipGetLastError();
 }
 
 hipError_t launch_forward_route(const FwdArgs &a, hipStream_t stream) {

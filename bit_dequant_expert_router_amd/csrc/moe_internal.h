@@ -224,6 +224,17 @@ hipError_t launch_forward_stage(const FwdArgs &a, int stage, hipStream_t stream)
 // are filled, stage 1 without routing and stage 2, both addressing the experts
 // as a.experts + slot * bytes (launch_forward_slots, T*K <= kSlotArgs)
 hipError_t launch_forward_route(const FwdArgs &a, hipStream_t stream);
+// copies n whole packed experts, expert[i] of src (host memory mapped into the
+// device's address space) into slot[i] of dst, with one launch
+struct FetchArgs {
+    const uint8_t *src;
+    uint8_t *dst;
+    uint64_t bytes;  // of one expert, a multiple of 16
+    int32_t n;
+    int32_t expert[kSlotArgs];
+    int32_t slot[kSlotArgs];
+};
+hipError_t launch_fetch(const FetchArgs &f, hipStream_t stream);
 hipError_t launch_forward_slots(const FwdArgs &a, const SlotArgs &slots, hipStream_t stream);
 
 struct PackArgs {

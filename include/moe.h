@@ -216,8 +216,8 @@ int moe_stack_forward(const moe_dims_t *dims, const moe_layer_t *layers, int32_t
  * of a 4.28 ms layer is that read, about 71% of reads hit the cache; the
  * compute and the reads run one after the other, never overlapped).  Here the
  * backing store is host memory, HBM holds a cache of n_slots experts keyed by
- * (layer, expert) with least-recently-used replacement, and a miss is one
- * host-to-device DMA copy of the whole packed expert.  The dense weights
+ * (layer, expert) with least-recently-used replacement, and a miss is a copy
+ * of the whole packed expert over the host link.  The dense weights
  * (norm, router, shared gate) and the shared expert stay in device memory.
  *
  * A call runs the per-token kernels only (n_tokens up to max_tokens):
@@ -229,7 +229,9 @@ int moe_stack_forward(const moe_dims_t *dims, const moe_layer_t *layers, int32_t
  *      polls, as after a failed launch, makes it synchronise `stream` and
  *      report the error);
  *   3. cache lookups in token order, then rank order; each miss takes the
- *      least recently used slot and enqueues a copy of the expert into it;
+ *      least recently used slot; one kernel then copies the missing experts
+ *      into their slots, reading the host memory directly (a host store that
+ *      is not pinned, mapped memory is copied by DMA instead);
  *   4. gate/up + SwiGLU and down + combine read the selected experts from
  *      their slots, whose numbers travel in the kernel arguments (hence at
  *      most 64 assignments, max_tokens * top_k <= 64, per call).

@@ -29,12 +29,15 @@ def moe():
     return m
 
 
-def _layers(dims, n_layers, seed):
+def _layers(dims, n_layers, seed, pinned=True):
     from bit_dequant_expert_router_amd.weights import layer_generated
     lws = [layer_generated(dims, syn.layer_dense(seed, l, dims), seed, l) for l in range(n_layers)]
     hosts = []
     for lw in lws:
-        h = torch.empty(lw.experts.numel(), dtype=torch.uint8, pin_memory=True)
+        n = lw.experts.numel()
+        raw = torch.empty(n + 256, dtype=torch.uint8, pin_memory=pinned)
+        off = (-raw.data_ptr()) % 256  # the store must be 256-byte aligned
+        h = raw[off:off + n]
         h.copy_(lw.experts)
         hosts.append(h)
     torch.cuda.synchronize()
@@ -47,10 +50,11 @@ def _same(a, b):
                                                                        torch.nan_to_num(b, nan=7.0))
 
 
-def _run(moe, dims, n_layers, n_slots, max_tokens, calls, seed=0, oracle_first=False, nan_token=None):
+def _run(moe, dims, n_layers, n_slots, max_tokens, calls, seed=0, oracle_first=False, nan_token=None,
+         pinned_store=True):
     K, E = dims.top_k, dims.n_experts
     log(f"tier: {dims}, {n_layers} layers, {n_slots} slots, calls {calls}")
-    lws, hosts = _layers(dims, n_layers, seed)
+    lws, hosts = _layers(dims, n_layers, seed, pinned_store)
     eb = moe.moe_expert_bytes(dims)
     state = torch.zeros(moe.moe_tier_state_bytes(dims, n_layers, n_slots, max_tokens), dtype=torch.uint8,
                         pin_memory=True)
@@ -170,3 +174,11 @@ def test_state_not_pinned_is_rejected(moe):
     assert err.value.status == moe.MOE_ERR_INVALID_ARG
     assert moe.moe_tier_get_stats(state).calls == 0
     torch.cuda.synchronize()
+
+
+def test_pageable_store(moe):
+    # a host store that is not pinned: the misses are copied by DMA instead of
+    # the copy kernel, with the same results
+    dims = syn.WORKLOADS["tiny"].dims
+    st = _run(moe, dims, 2, 5, 2, [2, 1, 2, 2, 1], pinned_store=False)
+    assert st.misses > 0
