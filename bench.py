@@ -44,10 +44,10 @@ KERNEL_TRAFFIC = {
                              "fetch_scale": 2.0, "write_scale": 1.0},
     ("layer4", "k_down"): {"source_sha256_prefix": "5271af809b8e5ad3", "fetch_kib": 5929.5, "write_kib": 16.0,
                            "fetch_scale": 2.0, "write_scale": 1.0},
-    ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "5e1f1a738532520d", "fetch_kib": 576521.5,
-                                      "write_kib": 3621.6, "fetch_scale": 2.0, "write_scale": 1.0},
-    ("batch32", "k_grouped_down"): {"source_sha256_prefix": "5e1f1a738532520d", "fetch_kib": 289807.9,
-                                    "write_kib": 6144.7, "fetch_scale": 2.0, "write_scale": 1.0},
+    ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "8bcffc6967ec026c", "fetch_kib": 576830.0,
+                                      "write_kib": 3622.5, "fetch_scale": 2.0, "write_scale": 1.0},
+    ("batch32", "k_grouped_down"): {"source_sha256_prefix": "8bcffc6967ec026c", "fetch_kib": 289846.8,
+                                    "write_kib": 6145.0, "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
 
