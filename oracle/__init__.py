@@ -14,6 +14,10 @@ the sigmoid-gated shared expert and the residual).  Steps are cited in
 Parity status of each function (what pins it is listed in
 ``tests/test_oracle_pins.py``): all pinned except absolute end-to-end values of
 the original trained model, which the pages do not print (parity unpinned).
+
+``oracle/lru.py`` (pure Python) holds the expert-cache policy of tiered
+residency, a plain least-recently-used cache, pinned in
+``tests/test_tier_oracle.py``.
 """
 from __future__ import annotations
 
