@@ -276,8 +276,11 @@ int moe_tier_init(const moe_dims_t *dims, int32_t n_layers, int32_t n_slots, int
 
 /*
  * One layer through the cache.  `layer` as for moe_layer_forward except that
- * layer->experts is HOST memory (pinned for full DMA speed) holding the layer's
- * n_experts packed experts, expert e at byte offset e * moe_expert_bytes();
+ * layer->experts is HOST memory, 256-byte aligned, holding the layer's
+ * n_experts packed experts, expert e at byte offset e * moe_expert_bytes().
+ * Pinned memory (hipHostMalloc) is read directly by the copy kernel; other
+ * host memory is copied by DMA, more slowly.  It must stay valid and unchanged
+ * until the work this call enqueues on `stream` has completed;
  * layer_index (0 .. n_layers-1) names the layer in the cache's keys, so each
  * index must always come with the same experts.  Other arguments as for
  * moe_layer_forward, n_tokens <= max_tokens.  Returns after the copies and the
