@@ -74,6 +74,7 @@ _SIGS = {
     "moe_tier_device_bytes": (_sz, [_dimsp, _i32, _i32]),
     "moe_tier_init": (ctypes.c_int, [_dimsp, _i32, _i32, _i32, _vp, _sz, _vp, _sz]),
     "moe_tier_layer_forward": (ctypes.c_int, [_vp, _i32, _layerp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "moe_tier_stack_forward": (ctypes.c_int, [_vp, _layerp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "moe_tier_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(moe_tier_stats_t)]),
     "moe_tier_lookup": (ctypes.c_int, [_vp, _i32, _i32, ctypes.POINTER(ctypes.c_int32)]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -248,6 +249,15 @@ def moe_tier_layer_forward(state, layer_index: int, layer: moe_layer_t, x, y, n_
                                               _addr(y), int(n_tokens), _addr(route_idx), _addr(route_w),
                                               _addr(workspace), _nbytes(workspace, workspace_bytes),
                                               _stream(stream)))
+
+
+def moe_tier_stack_forward(state, layers: Sequence[moe_layer_t], x, y, n_tokens: int, route_idx, route_w,
+                           workspace, workspace_bytes: Optional[int] = None, stream=None) -> int:
+    arr = (moe_layer_t * len(layers))(*layers)
+    return _check("moe_tier_stack_forward",
+                  _lib.moe_tier_stack_forward(_addr(state), arr, len(layers), _addr(x), _addr(y), int(n_tokens),
+                                              _addr(route_idx), _addr(route_w), _addr(workspace),
+                                              _nbytes(workspace, workspace_bytes), _stream(stream)))
 
 
 def moe_tier_get_stats(state) -> moe_tier_stats_t:

@@ -437,6 +437,22 @@ int moe_tier_layer_forward(void *state, int32_t layer_index, const moe_layer_t *
     return MOE_OK;
 }
 
+int moe_tier_stack_forward(void *state, const moe_layer_t *layers, int32_t n_layers, const float *x, float *y,
+                           int32_t n_tokens, int32_t *route_idx, float *route_w, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    const TierState *st = tier_header(state);
+    if (!st || !layers || n_layers < 1 || n_layers > st->n_layers || n_tokens < 1) return MOE_ERR_INVALID_ARG;
+    const size_t per_layer = (size_t)n_tokens * st->dims.top_k;
+    for (int l = 0; l < n_layers; ++l) {
+        const int rc = moe_tier_layer_forward(state, l, &layers[l], l == 0 ? x : y, y, n_tokens,
+                                              route_idx ? route_idx + l * per_layer : nullptr,
+                                              route_w ? route_w + l * per_layer : nullptr, workspace,
+                                              workspace_bytes, stream);
+        if (rc != MOE_OK) return rc;
+    }
+    return MOE_OK;
+}
+
 int moe_tier_get_stats(const void *state, moe_tier_stats_t *out) {
     const TierState *st = tier_header(state);
     if (!st || !out) return MOE_ERR_INVALID_ARG;

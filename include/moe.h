@@ -292,6 +292,18 @@ int moe_tier_layer_forward(void *state, int32_t layer_index, const moe_layer_t *
                            float *y, int32_t n_tokens, int32_t *route_idx, float *route_w,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * n_layers layers through the cache, chained as in moe_stack_forward: layer l
+ * uses layers[l] (a HOST array; experts in host memory as above) and cache
+ * layer index l, for l = 0 .. n_layers-1 (n_layers at most the state's).
+ * route_idx / route_w (device or NULL): [n_layers][n_tokens][K].  Waits once
+ * per layer for its routing, as moe_tier_layer_forward does; stops at the
+ * first error and returns it.
+ */
+int moe_tier_stack_forward(void *state, const moe_layer_t *layers, int32_t n_layers, const float *x, float *y,
+                           int32_t n_tokens, int32_t *route_idx, float *route_w, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 /* Statistics since moe_tier_init. */
 int moe_tier_get_stats(const void *state, moe_tier_stats_t *out);
 

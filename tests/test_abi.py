@@ -306,4 +306,12 @@ def test_tier_init_lookup_and_rejects():
     assert call(T=max_tokens + 1) == moe.MOE_ERR_INVALID_ARG
     assert call(layer=_layer(experts=None)) == moe.MOE_ERR_INVALID_ARG
     assert call(ws=A + 0x500010) == moe.MOE_ERR_ALIGNMENT
+    sf = moe._lib.moe_tier_stack_forward
+    lays = (moe.moe_layer_t * 3)(lay, lay, lay)
+    assert sf(st, lays, 3, A + 0x300000, A + 0x400000, 1, None, None, A + 0x500000, wsb, None) == \
+        moe.MOE_ERR_INVALID_ARG  # more layers than the state holds
+    assert sf(st, lays, 0, A + 0x300000, A + 0x400000, 1, None, None, A + 0x500000, wsb, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert sf(st + 8, lays, 1, A + 0x300000, A + 0x400000, 1, None, None, A + 0x500000, wsb, None) == \
+        moe.MOE_ERR_INVALID_ARG
     assert moe.moe_tier_get_stats(st).calls == 0

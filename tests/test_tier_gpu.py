@@ -182,3 +182,32 @@ def test_pageable_store(moe):
     dims = syn.WORKLOADS["tiny"].dims
     st = _run(moe, dims, 2, 5, 2, [2, 1, 2, 2, 1], pinned_store=False)
     assert st.misses > 0
+
+
+def test_stack_equals_resident_stack(moe):
+    # three chained layers through the cache in one call == moe_stack_forward
+    # with every expert resident, bit for bit, including the routing records
+    dims = syn.WORKLOADS["tiny"].dims
+    L, T, K = 3, 2, dims.top_k
+    lws, hosts = _layers(dims, L, 0)
+    state = torch.zeros(moe.moe_tier_state_bytes(dims, L, 6, T), dtype=torch.uint8, pin_memory=True)
+    dev = torch.empty(moe.moe_tier_device_bytes(dims, 6, T), dtype=torch.uint8, device="cuda")
+    moe.moe_tier_init(dims, L, 6, T, state, dev)
+    ws = torch.empty(moe.moe_workspace_bytes(dims, T), dtype=torch.uint8, device="cuda")
+    ws_ref = torch.empty_like(ws)
+    moe.moe_workspace_init(ws)
+    moe.moe_workspace_init(ws_ref)
+    tier_layers = [moe.make_layer(lw.norm_weight, lw.router_weight, lw.shared_gate, h, lw.shared)
+                   for lw, h in zip(lws, hosts)]
+    for c in range(4):
+        x = torch.from_numpy(syn.tokens(40 + c, T, dims.hidden)).cuda()
+        yt, yr = torch.empty_like(x), torch.empty_like(x)
+        it = torch.full((L, T, K), -1, dtype=torch.int32, device="cuda")
+        ir = torch.full_like(it, -2)
+        wt = torch.full((L, T, K), -1.0, dtype=torch.float32, device="cuda")
+        wr = torch.full_like(wt, -2.0)
+        moe.moe_tier_stack_forward(state, tier_layers, x, yt, T, it, wt, ws)
+        moe.moe_stack_forward(dims, [lw.descriptor() for lw in lws], x, yr, T, ir, wr, ws_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(it, ir) and _same(wt, wr) and _same(yt, yr), c
+    assert moe.moe_tier_get_stats(state).calls == 4 * L
