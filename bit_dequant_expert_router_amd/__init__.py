@@ -78,6 +78,12 @@ _SIGS = {
     "moe_tier_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(moe_tier_stats_t)]),
     "moe_tier_lookup": (ctypes.c_int, [_vp, _i32, _i32, ctypes.POINTER(ctypes.c_int32)]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    # measurement kernels (include/moe_microbench.h)
+    "moe_mb_stream_read": (ctypes.c_int, [_vp, _sz, _i32, _i32, _vp, _vp]),
+    "moe_mb_empty": (ctypes.c_int, [_i32, _vp]),
+    "moe_mb_exchange": (ctypes.c_int, [_i32, _i32, _i32, _vp, _sz, _vp]),
+    "moe_mb_exchange_bytes": (_sz, [_i32, _i32]),
+    "moe_mb_exchange_failures": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_uint32)]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -270,3 +276,28 @@ def moe_tier_lookup(state, layer_index: int, expert: int) -> int:
     slot = ctypes.c_int32()
     _check("moe_tier_lookup", _lib.moe_tier_lookup(_addr(state), int(layer_index), int(expert), ctypes.byref(slot)))
     return slot.value
+
+
+# measurement kernels (include/moe_microbench.h): no part of the layer
+def moe_mb_stream_read(src, nbytes: int, blocks: int, in_flight: int, sink, stream=None) -> int:
+    return _check("moe_mb_stream_read", _lib.moe_mb_stream_read(_addr(src), int(nbytes), int(blocks),
+                                                                int(in_flight), _addr(sink), _stream(stream)))
+
+
+def moe_mb_empty(blocks: int, stream=None) -> int:
+    return _check("moe_mb_empty", _lib.moe_mb_empty(int(blocks), _stream(stream)))
+
+
+def moe_mb_exchange_bytes(blocks: int, groups: int) -> int:
+    return int(_lib.moe_mb_exchange_bytes(int(blocks), int(groups)))
+
+
+def moe_mb_exchange(kind: int, blocks: int, groups: int, buf, buf_bytes: Optional[int] = None, stream=None) -> int:
+    return _check("moe_mb_exchange", _lib.moe_mb_exchange(int(kind), int(blocks), int(groups), _addr(buf),
+                                                          _nbytes(buf, buf_bytes), _stream(stream)))
+
+
+def moe_mb_exchange_failures(buf) -> int:
+    out = ctypes.c_uint32()
+    _check("moe_mb_exchange_failures", _lib.moe_mb_exchange_failures(_addr(buf), ctypes.byref(out)))
+    return int(out.value)

@@ -145,7 +145,7 @@ int moe_pack_expert(const moe_dims_t *dims, const uint8_t *const codes[3],
  * uniform in [-0.1, 0), all drawn from counter-based SplitMix64 streams keyed by
  * (seed, layer, expert, matrix, kind).  The result equals moe_pack_expert of the
  * canonical tensors that the same streams define (the stream definition is
- * stated in the library's DESIGN notes and in the generator's source).
+ * stated in the generator's source, moe_pack.hip).
  *   experts        E packed experts (NULL: skip), shared_expert: 1 (NULL: skip).
  */
 int moe_generate_layer(const moe_dims_t *dims, uint64_t seed, uint32_t layer, void *experts,

@@ -106,7 +106,7 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------- #
-# configurations (shapes from the pages; see the design doc for the recipe)
+# configurations (shapes from the pages; value distributions as stated above)
 # --------------------------------------------------------------------------- #
 @dataclasses.dataclass(frozen=True)
 class Dims:

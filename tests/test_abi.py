@@ -13,13 +13,16 @@ import bit_dequant_expert_router_amd as moe
 import synthetic as syn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe.h")
+HEADERS = [os.path.join(ROOT, "include", n) for n in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if n.endswith(".h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
@@ -152,6 +155,25 @@ def test_forward_rejects(kw, status):
         assert rc == status
         return
     assert _fwd(**kw) == status
+
+
+def test_microbench_rejects():
+    """Argument checks of the measurement kernels (host only)."""
+    assert moe._lib.moe_mb_stream_read(None, 1024, 4, 2, A, None) == moe.MOE_ERR_INVALID_ARG
+    assert moe._lib.moe_mb_stream_read(A, 1000, 4, 2, A, None) == moe.MOE_ERR_INVALID_ARG
+    assert moe._lib.moe_mb_stream_read(A, 1024, 4, 3, A, None) == moe.MOE_ERR_INVALID_ARG
+    assert moe._lib.moe_mb_stream_read(A, 1024, 0, 2, A, None) == moe.MOE_ERR_INVALID_ARG
+    assert moe._lib.moe_mb_stream_read(A + 8, 1024, 4, 2, A, None) == moe.MOE_ERR_ALIGNMENT
+    assert moe._lib.moe_mb_empty(0, None) == moe.MOE_ERR_INVALID_ARG
+    assert moe.moe_mb_exchange_bytes(256, 8) > 256 * 8
+    assert moe.moe_mb_exchange_bytes(256, 7) == 0  # blocks not a multiple of groups
+    assert moe.moe_mb_exchange_bytes(4096, 8) == 0
+    n = moe.moe_mb_exchange_bytes(256, 8)
+    f = moe._lib.moe_mb_exchange
+    assert f(4, 256, 8, A, n, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(1, 256, 8, A + 64, n, None) == moe.MOE_ERR_ALIGNMENT
+    assert f(1, 256, 8, A, n - 4, None) == moe.MOE_ERR_WORKSPACE
+    assert f(1, 256, 8, None, n, None) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_stage_rejects():
