@@ -67,6 +67,7 @@ _SIGS = {
     "moe_pack_expert": (ctypes.c_int, [_dimsp, _vp * 3, _vp * 3, _vp * 3, _vp, _vp]),
     "moe_generate_layer": (ctypes.c_int, [_dimsp, ctypes.c_uint64, ctypes.c_uint32, _vp, _vp, _vp]),
     "moe_layer_forward": (ctypes.c_int, [_dimsp, _layerp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "moe_layer_forward_noalloc": (ctypes.c_int, [_dimsp, _layerp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "moe_layer_forward_stage": (ctypes.c_int, [_dimsp, _layerp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _i32, _vp]),
     "moe_forward_stage_count": (ctypes.c_int, [_dimsp, _i32]),
     "moe_stack_forward": (ctypes.c_int, [_dimsp, _layerp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
@@ -196,6 +197,17 @@ def moe_layer_forward(dims, layer: moe_layer_t, x, y, n_tokens: int, route_idx, 
                   _lib.moe_layer_forward(ctypes.byref(dims_of(dims)), ctypes.byref(layer), _addr(x), _addr(y),
                                          int(n_tokens), _addr(route_idx), _addr(route_w), _addr(workspace),
                                          nbytes, _stream(stream)))
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 16 << 20  # include/moe.h
+
+
+def moe_layer_forward_noalloc(dims, layer: moe_layer_t, x, y, n_tokens: int, route_idx, route_w,
+                              stream=None) -> int:
+    return _check("moe_layer_forward_noalloc",
+                  _lib.moe_layer_forward_noalloc(ctypes.byref(dims_of(dims)), ctypes.byref(layer), _addr(x),
+                                                 _addr(y), int(n_tokens), _addr(route_idx), _addr(route_w),
+                                                 _stream(stream)))
 
 
 def moe_layer_forward_stage(dims, layer: moe_layer_t, x, y, n_tokens: int, route_idx, route_w, workspace,

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "moe_internal.h"
 #include "moe_tier.h"
@@ -76,17 +78,59 @@ bool overlap_not_equal(const void *a, const void *b, size_t bytes) {
     return x < y + bytes && y < x + bytes;
 }
 
-int check_forward_common(const moe_dims_t *dims, const float *x, float *y, int32_t n_tokens,
-                         int32_t *route_idx, float *route_w, void *workspace, size_t workspace_bytes) {
+// the checks of a forward call that do not concern its workspace
+int check_forward_io(const moe_dims_t *dims, const float *x, float *y, int32_t n_tokens, int32_t *route_idx,
+                     float *route_w) {
     int rc = check_dims_impl(dims);
     if (rc != MOE_OK) return rc;
     if (n_tokens < 1 || n_tokens > 65535) return MOE_ERR_INVALID_ARG;
-    if (!x || !y || !workspace) return MOE_ERR_INVALID_ARG;
-    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, kAlign)) return MOE_ERR_ALIGNMENT;
+    if (!x || !y) return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16)) return MOE_ERR_ALIGNMENT;
     if ((route_idx && !aligned(route_idx, 4)) || (route_w && !aligned(route_w, 4))) return MOE_ERR_ALIGNMENT;
     if (overlap_not_equal(x, y, (size_t)n_tokens * dims->hidden * sizeof(float))) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+int check_forward_common(const moe_dims_t *dims, const float *x, float *y, int32_t n_tokens,
+                         int32_t *route_idx, float *route_w, void *workspace, size_t workspace_bytes) {
+    const int rc = check_forward_io(dims, x, y, n_tokens, route_idx, route_w);
+    if (rc != MOE_OK) return rc;
+    if (!workspace) return MOE_ERR_INVALID_ARG;
+    if (!aligned(workspace, kAlign)) return MOE_ERR_ALIGNMENT;
     if (workspace_bytes < workspace_bytes_checked(dims, n_tokens)) return MOE_ERR_WORKSPACE;
     return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// the library's own workspace, for moe_layer_forward_noalloc: one fixed array
+// per GPU (each device that loads the library holds its own copy until the
+// process ends).  Its name is a host-side stand-in, not a device address: host
+// code uses only the address that hipGetSymbolAddress returns on each device,
+// looked up once per device and kept in g_scratch_ptr.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices];
+
+// the array's address on the current device (first call per device: looked up)
+hipError_t scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p || !aligned(p, kAlign)) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------
@@ -257,6 +301,23 @@ int moe_layer_forward(const moe_dims_t *dims, const moe_layer_t *layer, const fl
     if (rc != MOE_OK) return rc;
     const FwdArgs a = make_fwd(dims, layer, x, y, n_tokens, route_idx, route_w, workspace);
     return hip_status(launch_layer(a, (hipStream_t)stream));
+}
+
+int moe_layer_forward_noalloc(const moe_dims_t *dims, const moe_layer_t *layer, const float *x, float *y,
+                              int32_t n_tokens, int32_t *route_idx, float *route_w, void *stream) {
+    int rc = check_forward_io(dims, x, y, n_tokens, route_idx, route_w);
+    if (rc != MOE_OK) return rc;
+    rc = check_layer(layer);
+    if (rc != MOE_OK) return rc;
+    if (workspace_bytes_checked(dims, n_tokens) > kScratchBytes) return MOE_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (hip_status(scratch_address(&ws)) != MOE_OK) return MOE_ERR_HIP;
+    const hipStream_t hs = (hipStream_t)stream;
+    const FwdArgs a = make_fwd(dims, layer, x, y, n_tokens, route_idx, route_w, ws);
+    // the grouped kernels claim work through counters in the control block,
+    // which must start at zero: cleared by a kernel (no memset node under capture)
+    if (uses_grouped(a.s, n_tokens) && hip_status(launch_clear_ctrl(a.ws.ctrl, hs)) != MOE_OK) return MOE_ERR_HIP;
+    return hip_status(launch_layer(a, hs));
 }
 
 int moe_layer_forward_stage(const moe_dims_t *dims, const moe_layer_t *layer, const float *x, float *y,

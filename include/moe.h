@@ -24,7 +24,8 @@
  *  - Pointers named as device memory are HIP device pointers owned by the
  *    caller; the library never allocates or frees, and never synchronises
  *    except in moe_tier_layer_forward.  It keeps no state between calls apart
- *    from the workspace and the tier state the caller passes.
+ *    from the workspace and the tier state the caller passes, and the one
+ *    fixed device array per GPU that moe_layer_forward_noalloc works in.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *    enqueue work; faults surface at the caller's next synchronisation.
  *  - Arguments are checked on the host before anything is enqueued; a negative
@@ -170,6 +171,30 @@ int moe_generate_layer(const moe_dims_t *dims, uint64_t seed, uint32_t layer, vo
 int moe_layer_forward(const moe_dims_t *dims, const moe_layer_t *layer, const float *x, float *y,
                       int32_t n_tokens, int32_t *route_idx, float *route_w, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/*
+ * moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The workspace is a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes of device memory inside the library, one
+ * per GPU, held from the library's load until the process ends; its address on
+ * the current device is looked up on the first call there.  The call
+ * allocates nothing and calls no allocating routine.
+ *  - `stream` must belong to the current device.
+ *  - Every call on one GPU uses that GPU's one array: calls that may overlap
+ *    on one GPU (different streams, or different threads without ordering)
+ *    race and give wrong results.  Stream-ordered calls are safe; each call
+ *    starts from what it needs to be zero (the grouped path's control block
+ *    is cleared by a kernel first).
+ *  - A batch whose workspace, moe_workspace_bytes(dims, n_tokens), exceeds
+ *    MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_WORKSPACE before anything is
+ *    enqueued.  16 MiB holds every single-token call of the built shapes and
+ *    up to 32 tokens with top-10 at hidden 4096, FFN 1024, 512 experts.
+ * Other arguments, checks and results as for moe_layer_forward (bit for bit).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int moe_layer_forward_noalloc(const moe_dims_t *dims, const moe_layer_t *layer, const float *x, float *y,
+                              int32_t n_tokens, int32_t *route_idx, float *route_w, void *stream);
 
 /*
  * Enqueue one stage of the layer, for profiling or for interleaving other work

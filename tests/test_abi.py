@@ -157,6 +157,25 @@ def test_forward_rejects(kw, status):
     assert _fwd(**kw) == status
 
 
+def test_noalloc_rejects_before_any_launch():
+    """The no-alloc variant checks its arguments like moe_layer_forward and
+    refuses a batch whose workspace exceeds its fixed array, all on the host."""
+    f = moe._lib.moe_layer_forward_noalloc
+    lay = _layer()
+    big = d(top_k=10)
+    assert moe.moe_workspace_bytes(big, 32) <= moe.MOE_NOALLOC_SCRATCH_BYTES < moe.moe_workspace_bytes(big, 64)
+    assert f(ctypes.byref(big), ctypes.byref(lay), A + 0x300000, A + 0x300000, 64, None, None,
+             None) == moe.MOE_ERR_WORKSPACE
+    dims = d()
+    assert f(ctypes.byref(dims), None, A + 0x300000, A + 0x400000, 1, None, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(dims), ctypes.byref(lay), A + 0x300004, A + 0x400000, 1, None, None,
+             None) == moe.MOE_ERR_ALIGNMENT
+    assert f(ctypes.byref(dims), ctypes.byref(lay), A + 0x300000, A + 0x400000, 0, None, None,
+             None) == moe.MOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(d(bits=3)), ctypes.byref(lay), A + 0x300000, A + 0x400000, 1, None, None,
+             None) == moe.MOE_ERR_UNSUPPORTED
+
+
 def test_microbench_rejects():
     """Argument checks of the measurement kernels (host only)."""
     assert moe._lib.moe_mb_stream_read(None, 1024, 4, 2, A, None) == moe.MOE_ERR_INVALID_ARG
