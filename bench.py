@@ -97,6 +97,8 @@ def parse_args(argv=None):
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="before timing, copy a buffer of this many MiB 8 times (a kernel of known traffic "
                         "for scaling profiler byte counters)")
+    p.add_argument("--no-stages", action="store_true",
+                   help="skip the per-kernel timing graphs and the roofline (for profiler runs)")
     p.add_argument("--quiet", action="store_true")
     a = p.parse_args(argv)
     if a.steps is None:
@@ -304,6 +306,12 @@ def bench_layer(args, wl):
     ms_per_step = elapsed * 1e3 / nsteps
     tokens_per_s = nsteps * T / elapsed
 
+    if args.no_stages:
+        print(json.dumps({"metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+                          "steps": nsteps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+                          "note": "profiler run: no per-kernel timing, no roofline"}), flush=True)
+        return
+
     # per-kernel durations, marginal: NW steps (token j, layer j mod R) get a
     # workspace each, filled by one full forward
     NW = min(P, 64)
@@ -452,6 +460,11 @@ def bench_stack(args, wl):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     del graph
+    if args.no_stages:
+        print(json.dumps({"metric": METRIC, "value": round(nsteps / elapsed, 2), "unit": "tokens/s",
+                          "n_gpus": 1, "steps": nsteps, "ms_per_step": round(elapsed * 1e3 / nsteps, 6),
+                          "note": "profiler run: no per-kernel timing, no roofline"}), flush=True)
+        return
     idx_all = ridx.cpu().numpy()
     rows = sorted({i % P for i in range(nsteps)})
     per_token = {j: sum(distinct_experts(idx_all[j, l]) for l in range(L)) * eb for j in rows}
