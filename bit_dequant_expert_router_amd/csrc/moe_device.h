@@ -349,6 +349,104 @@ __device__ __forceinline__ void load_logits_quarter(const float *__restrict__ z,
 }
 
 // ---------------------------------------------------------------------------
+// routing by one wave over all E logits of a token (E <= 64 EPL), without LDS
+// or barriers.  Lane l holds the keys of experts EPL l .. EPL l + EPL - 1 (the
+// high word of route_key; 0 = absent or already taken).  A round takes the wave
+// maximum of the lanes' best keys.  Among equal keys the lowest lane holds the
+// lowest expert, and inside a lane the lowest position does (the first maximum
+// is kept), so the key order (logit descending, index ascending) needs no
+// second comparison.  The winner's key is cleared.  The expert of slot s is the
+// winner of round s: a wave that serves slot s stops after s + 1 rounds.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t logit_key(float z) { return (uint32_t)(route_key(z, 0) >> 32); }
+__device__ __forceinline__ float logit_of_key(uint32_t m) { return route_key_value((uint64_t)m << 32); }
+
+// the lane's EPL logits of one token, from a row of ZS floats (a multiple of
+// 16, 32-byte aligned) with 16-byte loads; a lane whose experts all lie past
+// the row reads its last EPL entries instead (read, never used as logits)
+template <int EPL>
+__device__ __forceinline__ void load_logits_lane(const float *__restrict__ z, int ZS, float (&v)[EPL]) {
+    const int lane = threadIdx.x & 63;
+    const int base = EPL * lane < ZS - EPL ? EPL * lane : ZS - EPL;
+#pragma unroll
+    for (int i = 0; i < EPL / 4; ++i) {
+        const float4 f = *(const float4 *)(z + base + 4 * i);
+        v[4 * i] = f.x;
+        v[4 * i + 1] = f.y;
+        v[4 * i + 2] = f.z;
+        v[4 * i + 3] = f.w;
+    }
+}
+
+template <int EPL>
+__device__ __forceinline__ void logit_keys(const float (&v)[EPL], int E, uint32_t (&key)[EPL]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) key[q] = (EPL * lane + q < E) ? logit_key(v[q]) : 0u;
+}
+
+// one round: the expert holding the wave's largest remaining key (wave-uniform,
+// clamped below E), whose key is then cleared; m receives that key
+template <int EPL>
+__device__ __forceinline__ int route_round(uint32_t (&key)[EPL], int E, uint32_t &m) {
+    const int lane = threadIdx.x & 63;
+    uint32_t best = key[0];
+    int bq = 0;
+#pragma unroll
+    for (int q = 1; q < EPL; ++q) {
+        const bool gt = key[q] > best;
+        best = gt ? key[q] : best;
+        bq = gt ? q : bq;
+    }
+    m = wave_max_u32(best);
+    const int w = __ffsll((unsigned long long)__ballot(best == m)) - 1;
+    const int qw = __builtin_amdgcn_readlane(bq, w);
+    const uint32_t clear = (lane == w) ? (1u << qw) : 0u;
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) key[q] = ((clear >> q) & 1u) ? 0u : key[q];
+    const int e = w * EPL + qw;
+    return e < E ? e : E - 1;
+}
+
+// the expert of slot s (s + 1 rounds; the keys are consumed)
+template <int EPL>
+__device__ __forceinline__ int route_slot(uint32_t (&key)[EPL], int E, int s) {
+    int e = 0;
+    uint32_t m;
+    for (int r = 0; r <= s; ++r) e = route_round<EPL>(key, E, m);
+    return e;
+}
+
+// softmax -> top-K -> renormalise: lane k < K ends with the k-th selected
+// expert (key order) and its weight, the softmax restricted to the selection
+// (which equals the full softmax renormalised over it); other lanes hold w = 0
+struct RouteK {
+    int sel;
+    float w;
+};
+
+template <int EPL>
+__device__ __forceinline__ RouteK route_all(uint32_t (&key)[EPL], int E, int K) {
+    const int lane = threadIdx.x & 63;
+    uint32_t my_m = 0;
+    int my_e = 0;
+    for (int r = 0; r < K; ++r) {
+        uint32_t m;
+        const int e = route_round<EPL>(key, E, m);
+        my_m = (lane == r) ? m : my_m;
+        my_e = (lane == r) ? e : my_e;
+    }
+    const bool in = lane < K;
+    const float z = in ? logit_of_key(my_m) : 0.0f;
+    const float zmax = lane_bcast(z, 0);  // round 0 took the largest logit
+    const float p = in ? expf(z - zmax) : 0.0f;
+    RouteK r;
+    r.sel = my_e;
+    r.w = p / lane_sum<64>(p);
+    return r;
+}
+
+// ---------------------------------------------------------------------------
 // dequantised dot product of one row slice with a lane's limb slice
 // ---------------------------------------------------------------------------
 template <int BITS, int CPL>
@@ -437,6 +535,97 @@ __device__ __forceinline__ void rows_dot_lds(const uint4 (&c)[NR][CPL], const fl
 #pragma unroll
         for (int hh = 0; hh < Q::GL / 32; ++hh) xs += Xh[g * 2 + hh];
         const float Sg = S[g];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const float f = fmaf((float)hi[r], 65536.0f, (float)lo[r]);
+            out[r] = fmaf(s[r][g] * Sg, f, out[r]);
+            out[r] = fmaf(o[r][g], xs, out[r]);
+        }
+    }
+}
+
+// The lane's slice of a vector in limb form, held in registers: limbs
+// [kLimbs][NV/8] words (limb x of entries k0 + 8 i .. k0 + 8 i + 7 in word i),
+// group scales S [NGL] and half-group sums Xh [NV/32].
+template <int BITS, int CPL>
+struct LimbSlice {
+    using Q = QSlice<BITS, CPL>;
+    static constexpr int ND = Q::NV / 8;
+    uint32_t L[kLimbs][ND];
+    float S[Q::NGL];
+    float Xh[Q::NV / 32];
+};
+
+// load the slice at k0 of a vector of n entries whose limbs are [kLimbs][n/8]
+// words, scales [n/64], half-group sums [n/32]
+template <int BITS, int CPL>
+__device__ __forceinline__ void load_limb_slice(const uint32_t *__restrict__ limbs, const float *__restrict__ S_all,
+                                                const float *__restrict__ Xh_all, int n, int k0,
+                                                LimbSlice<BITS, CPL> &v) {
+    using LS = LimbSlice<BITS, CPL>;
+    static_assert(LS::ND % 4 == 0, "whole 16-byte limb loads");
+#pragma unroll
+    for (int x = 0; x < kLimbs; ++x)
+#pragma unroll
+        for (int i = 0; i < LS::ND / 4; ++i) {
+            const uint4 w = *(const uint4 *)(limbs + (size_t)x * (n / 8) + k0 / 8 + 4 * i);
+            v.L[x][4 * i] = w.x;
+            v.L[x][4 * i + 1] = w.y;
+            v.L[x][4 * i + 2] = w.z;
+            v.L[x][4 * i + 3] = w.w;
+        }
+#pragma unroll
+    for (int g = 0; g < QSlice<BITS, CPL>::NGL; ++g) v.S[g] = S_all[k0 / 64 + g];
+#pragma unroll
+    for (int h = 0; h < QSlice<BITS, CPL>::NV / 32; ++h) v.Xh[h] = Xh_all[k0 / 32 + h];
+}
+
+// rows_dot_lds with the lane's limb slice in registers
+template <int BITS, int CPL, int NR>
+__device__ __forceinline__ void rows_dot_reg(const uint4 (&c)[NR][CPL], const float (&s)[NR][QSlice<BITS, CPL>::NGL],
+                                             const float (&o)[NR][QSlice<BITS, CPL>::NGL],
+                                             const LimbSlice<BITS, CPL> &v, float (&out)[NR]) {
+    using Q = QSlice<BITS, CPL>;
+    constexpr int ND = BITS == 4 ? CPL * 4 : CPL * 8;  // limb words per limb in the slice
+    constexpr int DPG = ND / Q::NGL;                    // ... per group
+#pragma unroll
+    for (int r = 0; r < NR; ++r) out[r] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < Q::NGL; ++g) {
+        int hi[NR], lo[NR];
+        auto limb = [&](int x, int (&acc)[NR], bool first) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                int a = first ? 0 : (acc[r] << 4);
+#pragma unroll
+                for (int i = 0; i < DPG; ++i) {
+                    const int di = g * DPG + i;  // limb word of the slice
+                    int op;
+                    if constexpr (BITS == 4) {
+                        const uint4 cj = c[r][di / 4];
+                        const uint32_t w[4] = {cj.x, cj.y, cj.z, cj.w};
+                        op = (int)w[di % 4];
+                    } else {
+                        const uint4 cj = c[r][di / 8];
+                        const uint32_t w[4] = {cj.x, cj.y, cj.z, cj.w};
+                        const uint32_t d = w[(di % 8) / 2];
+                        op = (int)((di & 1) ? ((d >> 2) & 0x33333333u) : (d & 0x33333333u));
+                    }
+                    a = __builtin_amdgcn_sdot8(op, (int)v.L[x][di], a, false);
+                }
+                acc[r] = a;
+            }
+        };
+        limb(kLimbs - 1, hi, true);
+#pragma unroll
+        for (int x = kLimbs - 2; x >= 4; --x) limb(x, hi, false);
+        limb(3, lo, true);
+#pragma unroll
+        for (int x = 2; x >= 0; --x) limb(x, lo, false);
+        float xs = 0.0f;
+#pragma unroll
+        for (int hh = 0; hh < Q::GL / 32; ++hh) xs += v.Xh[g * (Q::GL / 32) + hh];
+        const float Sg = v.S[g];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             const float f = fmaf((float)hi[r], 65536.0f, (float)lo[r]);

@@ -4,9 +4,10 @@
 //              a few blocks also store h in the fixed-point limb form below
 //              (k_router_split for H = 2048 / 4096, one token per block;
 //              k_router_tokens from 4 tokens, four per block; k_router else)
-//   k_gateup : per block, softmax/top-K/renormalise from the logits, then the
-//              fused gate+up dequant GEMV of the selected experts and the
-//              shared expert with SwiGLU in registers
+//   k_gateup : per wave, the routing rounds its slot needs (block 0 also
+//              the whole softmax/top-K/renormalise), then the fused gate+up
+//              dequant GEMV of its rows of the selected or the shared expert
+//              with SwiGLU in registers
 //   k_down   : down-projection dequant GEMV of all K+1 experts for a set of
 //              output rows, weighted combine, sigmoid-gated shared expert and
 //              residual, written once per row (no atomics, deterministic)
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router(FwdArgs a) {
     acc = lane_group_sum(acc, lpr);
     if (has_row && lr == 0) {
         if (r < E)
-            a.ws.z[(size_t)t * E + r] = acc;
+            a.ws.z[(size_t)t * logit_stride(E) + r] = acc;
         else
             a.ws.gs[t] = acc;
     }
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(256) void k_router_split(FwdArgs a) {
         const float z = (((s_part[0][threadIdx.x] + s_part[1][threadIdx.x]) + s_part[2][threadIdx.x]) +
                          s_part[3][threadIdx.x]) * inv;
         if (row < E)
-            a.ws.z[(size_t)t * E + row] = z;
+            a.ws.z[(size_t)t * logit_stride(E) + row] = z;
         else if (row == E)
             a.ws.gs[t] = z;
     }
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(256) void k_router_tokens(FwdArgs a) {
         const int tt = threadIdx.x, t = t0 + tt;
         const float z = (((s_part[0][tt] + s_part[1][tt]) + s_part[2][tt]) + s_part[3][tt]) * inv_of(tt);
         if (r0 < E)
-            a.ws.z[(size_t)t * E + r0] = z;
+            a.ws.z[(size_t)t * logit_stride(E) + r0] = z;
         else if (r0 == E)
             a.ws.gs[t] = z;
     }
@@ -358,7 +359,17 @@ __global__ __launch_bounds__(256) void k_router_tokens(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_gateup: RPW row-steps per wave over the (K+1) x F gate/up row pairs
+// k_gateup: RPW row-steps per wave over the (K+1) x F gate/up row pairs.
+// A wave's row-steps belong to one slot (F / rows-per-step is a multiple of
+// RPW).  A wave of a routed slot s loads all E logits of the token (EPL per
+// lane, two or four 16-byte loads) and runs s + 1 routing rounds (route_slot)
+// to find its expert; a wave of the shared expert needs none, and its blocks
+// are dispatched first.  Each wave issues its weight loads as soon as its
+// expert is known, with no barrier before them.
+// The limb form of h is staged in LDS once per block, and the block's one
+// barrier comes after every wave has issued its weight loads, so it only
+// orders the staging before the products.  Block 0's wave 0 finally takes all
+// K rounds and writes the selection, the renormalised weights and sigmoid(g_s).
 // ---------------------------------------------------------------------------
 // LPR: lanes per row when the step's partial sums are reduced together (64);
 // 0: one reduction per row
@@ -375,163 +386,149 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a, SlotParam<TIER> sl) {
     const int lpr = G.lpr, rpi = 64 / lpr;
     const int lr = lane % lpr, rsub = lane / lpr;
     const int nrs = (K + 1) * F / rpi;
-    const int rs0 = (blockIdx.x * 4 + wave) * RPW;
+    // the blocks of the shared expert (the last slot) run first: their loads
+    // need no routing and keep HBM busy while the routed waves route
+    const int nbs = (F / rpi + 4 * RPW - 1) / (4 * RPW);
+    const int lb = blockIdx.x < nbs ? blockIdx.x + gridDim.x - nbs : blockIdx.x - nbs;
+    const int rs0 = (lb * 4 + wave) * RPW;
     const bool active = rs0 < nrs;
-    // row-steps are slot-major: the block needs the routing iff its first row is routed
-    const bool block_routed = !TIER && (blockIdx.x * 4 * RPW * rpi) / F < K;
-    const bool wave_shared_only = (rs0 * rpi) / F >= K;
+    // slot of every row-step of the wave (waves past the end take the last one)
+    const int slot = ((active ? rs0 : nrs - 1) * rpi) / F;
 
     __shared__ __align__(16) uint32_t s_hl[kLimbs * kMaxDim / 8];  // limbs of h, [kLimbs][H/8]
     __shared__ float s_hs[kMaxDim / 64];
     __shared__ float s_hx[kMaxDim / 32];
 
-    // the block's four waves route together, a quarter of the logits each
-    // (route_candidates, then route_select after the block's barrier): the
-    // logit loads go first (loads complete in order)
-    constexpr int EPW = EPL / 4;
-    __shared__ __align__(16) uint64_t s_cand[4 * kMaxTopK];
-    float zq[EPW];
-    if (block_routed) load_logits_quarter<EPW>(a.ws.z + (size_t)t * E, E, zq);
-    const float gs = a.ws.gs[t];  // shared-gate logit (block 0 writes its coefficient)
-
-    // stage the limb form of h in LDS, once per block
+    // 1. loads that do not depend on the routing: the logits (resident path),
+    //    the shared-gate logit and this thread's share of h's limb form
+    float zv[EPL];
+    if constexpr (!TIER) load_logits_lane<EPL>(a.ws.z + (size_t)t * logit_stride(E), logit_stride(E), zv);
+    const float gs = a.ws.gs[t];
+    // kStage 16-byte pieces per thread (a native vector type: an array of
+    // int4 can keep dead copies in scratch memory)
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    constexpr int kStage = (kLimbs * kMaxDim / 32 + 255) / 256;
+    const int n16 = kLimbs * H / 32;
+    i32x4 st[kStage];
     {
-        // kStage 16-byte pieces per thread (a native vector type: an array of
-        // int4 can keep dead copies in scratch memory)
-        typedef int i32x4 __attribute__((ext_vector_type(4)));
         const i32x4 *src = (const i32x4 *)((const uint32_t *)a.ws.hl + (size_t)t * kLimbs * (H / 8));
-        const int n16 = kLimbs * H / 32;
-        constexpr int kStage = (kLimbs * kMaxDim / 32 + 255) / 256;
-        i32x4 st[kStage];
 #pragma unroll
         for (int j = 0; j < kStage; ++j) {
             const int i = threadIdx.x + 256 * j;
             st[j] = src[i < n16 ? i : 0];
         }
-        float hs = 0.0f, hx = 0.0f;
-        if (threadIdx.x < H / 64) hs = a.ws.hs[(size_t)t * (H / 64) + threadIdx.x];
-        if (threadIdx.x < H / 32) hx = a.ws.hx[(size_t)t * (H / 32) + threadIdx.x];
-        if (block_routed) route_candidates<EPW>(zq, E, K, s_cand);
-        {
-            i32x4 *dst = (i32x4 *)s_hl;
-#pragma unroll
-            for (int j = 0; j < kStage; ++j) {
-                const int i = threadIdx.x + 256 * j;
-                if (i < n16) dst[i] = st[j];
-            }
+    }
+    const float hs = a.ws.hs[(size_t)t * (H / 64) + (threadIdx.x < H / 64 ? threadIdx.x : 0)];
+    const float hx = a.ws.hx[(size_t)t * (H / 32) + (threadIdx.x < H / 32 ? threadIdx.x : 0)];
+
+    // 2. the wave's expert (the shared expert's waves do not wait for the logits)
+    const uint8_t *ex;
+    if constexpr (TIER) {
+        ex = (slot < K) ? a.experts + (size_t)sl.s[t * K + slot] * a.L.bytes : a.shared;
+    } else {
+        if (slot < K) {
+            uint32_t key[EPL];
+            logit_keys<EPL>(zv, E, key);
+            ex = a.experts + (size_t)route_slot<EPL>(key, E, slot) * a.L.bytes;
+        } else {
+            ex = a.shared;
         }
-        if (threadIdx.x < H / 64) s_hs[threadIdx.x] = hs;
-        if (threadIdx.x < H / 32) s_hx[threadIdx.x] = hx;
     }
 
-    // weight loads: shared-only waves issue theirs before the routing is known
+    // 3. weight loads, all unconditional (row-steps past the end re-read the
+    //    last one), addresses first, then every load back to back
     uint4 gc[RPW][CPL], uc[RPW][CPL];
     uint32_t gsb[RPW][Q::NGL], usb[RPW][Q::NGL];
-    // every row's loads unconditional (rows past the end re-read the last
-    // row), so that they are all in flight before the first wait
-    // (addresses first, then every load back to back)
-    // er[i]: the expert of row-step i when its slot is routed
-    auto issue_loads = [&](const int (&er)[RPW]) {
-        const uint8_t *exr[RPW];
+    {
         int jr[RPW];
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const int rs = rs0 + i < nrs ? rs0 + i : nrs - 1;
             const int p = rs * rpi + rsub;
-            const int s = p / F;
-            jr[i] = p - s * F;
-            exr[i] = (s < K) ? a.experts + (size_t)er[i] * a.L.bytes : a.shared;
+            jr[i] = p - (p / F) * F;
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
-            load_row<BITS, CPL>(exr[i], G, jr[i], lr, gc[i], gsb[i]);
-            load_row<BITS, CPL>(exr[i], U, jr[i], lr, uc[i], usb[i]);
+            load_row<BITS, CPL>(ex, G, jr[i], lr, gc[i], gsb[i]);
+            load_row<BITS, CPL>(ex, U, jr[i], lr, uc[i], usb[i]);
         }
         __builtin_amdgcn_sched_barrier(0);
-    };
-    if constexpr (TIER) {  // the slots are known: every wave issues its loads now
-        if (active) {
-            int er[RPW];
+    }
+
+    // 4. h's limbs into LDS (the staged loads were issued before the weights,
+    //    so this waits for them only), then the block's barrier
+    {
+        i32x4 *dst = (i32x4 *)s_hl;
 #pragma unroll
-            for (int i = 0; i < RPW; ++i) {
-                const int rs = rs0 + i < nrs ? rs0 + i : nrs - 1;
-                const int s = (rs * rpi) / F;
-                er[i] = sl.s[t * K + (s < K ? s : K - 1)];
-            }
-            issue_loads(er);
+        for (int j = 0; j < kStage; ++j) {
+            const int i = threadIdx.x + 256 * j;
+            if (i < n16) dst[i] = st[j];
         }
-    } else if (active && wave_shared_only) {
-        const int none[RPW] = {};
-        issue_loads(none);
+        if (threadIdx.x < H / 64) s_hs[threadIdx.x] = hs;
+        if (threadIdx.x < H / 32) s_hx[threadIdx.x] = hx;
     }
     __syncthreads();
-    if (!active) return;
-    if (!TIER && !wave_shared_only) {
-        // every routed wave ranks the block's candidates itself
-        const RouteSel rt = route_select(K, s_cand);
-        if (blockIdx.x == 0 && wave == 0) {
-            if (rt.rank < K) {
-                a.ws.sel[t * K + rt.rank] = rt.sel;
-                a.ws.coef[t * (K + 1) + rt.rank] = rt.w;
-                if (a.route_idx) a.route_idx[t * K + rt.rank] = rt.sel;
-                if (a.route_w) a.route_w[t * K + rt.rank] = rt.w;
+
+    // 5. codes prepared once, then every row against the lane's limb slice of h
+    //    in LDS, limb-major
+    if (active) {
+        constexpr int NV = 2 * RPW;  // entries 2i (gate) and 2i + 1 (up) of row-step i
+        const int k0 = lr * Q::NV;
+        uint4 cl[NV][CPL];
+        float sc[NV][Q::NGL], of[NV][Q::NGL];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            prep_codes<BITS, CPL>(gc[i]);
+            prep_codes<BITS, CPL>(uc[i]);
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                cl[2 * i][j] = gc[i][j];
+                cl[2 * i + 1][j] = uc[i][j];
             }
-            if (lane == 0) a.ws.coef[t * (K + 1) + K] = sigmoidf_(gs);
-        }
-        int er[RPW];
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-            const int rs = rs0 + i < nrs ? rs0 + i : nrs - 1;
-            const int s = (rs * rpi) / F;  // uniform: a row-step's rows share their slot
-            er[i] = routed_expert(rt, s < K ? s : K - 1);
+            for (int g = 0; g < Q::NGL; ++g) {
+                sc[2 * i][g] = bf16_lo(gsb[i][g]);
+                of[2 * i][g] = fmaf(Q::kCodeOffset, sc[2 * i][g], bf16_hi(gsb[i][g]));
+                sc[2 * i + 1][g] = bf16_lo(usb[i][g]);
+                of[2 * i + 1][g] = fmaf(Q::kCodeOffset, sc[2 * i + 1][g], bf16_hi(usb[i][g]));
+            }
         }
-        issue_loads(er);
-    }
+        float part[NV];
+        rows_dot_lds<BITS, CPL, NV>(cl, sc, of, s_hl, s_hs, s_hx, H, k0, part);
 
-    // codes prepared once, then every row against the lane's limb slice of h
-    // in LDS, limb-major
-    constexpr int NV = 2 * RPW;  // entries 2i (gate) and 2i + 1 (up) of row-step i
-    const int k0 = lr * Q::NV;
-    uint4 cl[NV][CPL];
-    float sc[NV][Q::NGL], of[NV][Q::NGL];
+        float *act = a.ws.act + (size_t)t * (K + 1) * F;
+        if constexpr (LPR != 0) {
+            // rows past the end are computed on re-read registers and not written
+            const float r = multi_reduce<NV, LPR>(part);
+            constexpr int DL = LPR / NV;  // lanes sharing one reduced entry
+            const int rs = rs0 + multi_index<NV, LPR>(lane) / 2;
+            const float up = xchg<DL>(r);  // the up sum sits across the last halving bit
+            if ((lane & (2 * DL - 1)) == 0 && rs < nrs) act[rs * rpi + rsub] = r * sigmoidf_(r) * up;
+        } else {
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        prep_codes<BITS, CPL>(gc[i]);
-        prep_codes<BITS, CPL>(uc[i]);
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            cl[2 * i][j] = gc[i][j];
-            cl[2 * i + 1][j] = uc[i][j];
-        }
-#pragma unroll
-        for (int g = 0; g < Q::NGL; ++g) {
-            sc[2 * i][g] = bf16_lo(gsb[i][g]);
-            of[2 * i][g] = fmaf(Q::kCodeOffset, sc[2 * i][g], bf16_hi(gsb[i][g]));
-            sc[2 * i + 1][g] = bf16_lo(usb[i][g]);
-            of[2 * i + 1][g] = fmaf(Q::kCodeOffset, sc[2 * i + 1][g], bf16_hi(usb[i][g]));
-        }
-    }
-    float part[NV];
-    rows_dot_lds<BITS, CPL, NV>(cl, sc, of, s_hl, s_hs, s_hx, H, k0, part);
-
-    float *act = a.ws.act + (size_t)t * (K + 1) * F;
-    if constexpr (LPR != 0) {
-        // rows past the end are computed on unloaded registers and not written
-        const float r = multi_reduce<NV, LPR>(part);
-        constexpr int DL = LPR / NV;  // lanes sharing one reduced entry
-        const int rs = rs0 + multi_index<NV, LPR>(lane) / 2;
-        const float up = xchg<DL>(r);  // the up sum sits across the last halving bit
-        if ((lane & (2 * DL - 1)) == 0 && rs < nrs) act[rs * rpi + rsub] = r * sigmoidf_(r) * up;
-    } else {
-#pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-            const int rs = rs0 + i;
-            if (rs < nrs) {
+            for (int i = 0; i < RPW; ++i) {
+                const int rs = rs0 + i;
                 const float g = lane_group_sum(part[2 * i], lpr);
                 const float u = lane_group_sum(part[2 * i + 1], lpr);
-                if (lr == 0) act[rs * rpi + rsub] = g * sigmoidf_(g) * u;
+                if (rs < nrs && lr == 0) act[rs * rpi + rsub] = g * sigmoidf_(g) * u;
             }
+        }
+    }
+
+    // 6. block 0, wave 0: the whole routing of the token (k_down reads it)
+    if constexpr (!TIER) {
+        if (blockIdx.x == 0 && wave == 0) {
+            uint32_t key[EPL];
+            logit_keys<EPL>(zv, E, key);
+            const RouteK rt = route_all<EPL>(key, E, K);
+            if (lane < K) {
+                a.ws.sel[t * K + lane] = rt.sel;
+                a.ws.coef[t * (K + 1) + lane] = rt.w;
+                if (a.route_idx) a.route_idx[t * K + lane] = rt.sel;
+                if (a.route_w) a.route_w[t * K + lane] = rt.w;
+            }
+            if (lane == 0) a.ws.coef[t * (K + 1) + K] = sigmoidf_(gs);
         }
     }
 }
@@ -555,14 +552,21 @@ constexpr int kDownStageValues = 5120;  // activations staged per batch (batch *
 // 0: one reduction per row
 // ONE: all K+1 slots in a single batch (straight-line code: no loop-header
 // wait holds back the first loads)
+// SPLIT: wave groups per block (1 or 2).  Group g of 4 waves takes the slot
+// positions g, g + SPLIT, ... of every batch for the block's rows, so that a
+// SIMD runs SPLIT waves (one alone exposes its LDS and VALU latencies: the
+// products are VALU-bound once the weights land).  The groups' row sums are
+// added in group order through LDS before the one write per row.
 // TIER: the selected experts sit in cache slots, sl.s[t * K + rank] (a.experts
 // = the slots' base)
-template <int BITS, int CPL, int RPW, int LPR, bool ONE, bool TIER>
-__global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_recip, SlotParam<TIER> sl) {
+template <int BITS, int CPL, int RPW, int LPR, bool ONE, bool TIER, int SPLIT>
+__global__ __launch_bounds__(256 * SPLIT) void k_down(FwdArgs a, int batch, uint32_t f4_recip, SlotParam<TIER> sl) {
     using Q = QSlice<BITS, CPL>;
+    constexpr int NT = 256 * SPLIT;                                  // threads per block
+    constexpr int kPer = (kDownBatch + SPLIT - 1) / SPLIT;          // slot positions per wave group
     const int t = blockIdx.y;
     const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3, grp = threadIdx.x >> 8;
     const QMat &Dm = a.L.m[2];
     const int lpr = LPR ? LPR : Dm.lpr, rpi = 64 / lpr;
     const int lr = lane % lpr, rsub = lane / lpr;
@@ -599,7 +603,7 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_
     for (int i = 0; i < RPW; ++i) acc[i] = 0.0f;
 
     // slot positions run shared, 0, 1, ..., K-1: the shared expert's loads need no routing
-    constexpr int kStageMax = kDownStageValues / 1024;  // float4 pieces per thread and batch
+    constexpr int kStageMax = (kDownStageValues + 4 * NT - 1) / (4 * NT);  // float4 pieces per thread and batch
     auto run_batch = [&](int b0) {
         const int nb = (K + 1 - b0) < batch ? (K + 1 - b0) : batch;
         // this batch's activations first: the staging then waits on them only
@@ -607,14 +611,14 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_
         // every load below is unconditional (indices past the end are
         // clamped to valid ones and their results unused), so that all of
         // them are in flight before the first wait
-        // float4 piece p = tid + 256 r: slot p / (F/4) by a multiply-high
+        // float4 piece p = tid + NT r: slot p / (F/4) by a multiply-high
         // with f4_recip = ceil(2^32 / (F/4)) (exact: p (F/4) < 2^32)
         float4 stv[kStageMax];
         uint32_t sti[kStageMax], stj[kStageMax];
         const float *act_t = a.ws.act + (size_t)t * (K + 1) * F;
 #pragma unroll
         for (int r = 0; r < kStageMax; ++r) {
-            const uint32_t p = threadIdx.x + 256 * r;
+            const uint32_t p = threadIdx.x + NT * r;
             const uint32_t pc = p < (uint32_t)(nb * F4) ? p : 0u;
             const uint32_t si = __umulhi(pc, f4_recip), j = (pc - __umul24(si, F4)) * 4;
             const uint32_t s = (b0 + si == 0) ? K : b0 + si - 1;
@@ -622,11 +626,13 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_
             stj[r] = j;
             stv[r] = *(const float4 *)(act_t + (__umul24(s, (uint32_t)F) + j));
         }
-        // weights of up to kDownBatch slots of this batch, all in flight together
-        uint4 wc[kDownBatch][RPW][CPL];
-        uint32_t wsb[kDownBatch][RPW][Q::NGL];
+        // weights of this group's slot positions grp, grp + SPLIT, ... of
+        // the batch, all in flight together
+        uint4 wc[kPer][RPW][CPL];
+        uint32_t wsb[kPer][RPW][Q::NGL];
 #pragma unroll
-        for (int si = 0; si < kDownBatch; ++si) {
+        for (int u = 0; u < kPer; ++u) {
+            const int si = grp + SPLIT * u;
             const int sc = si < nb ? si : nb - 1;
             const int s = (b0 + sc == 0) ? K : b0 + sc - 1;
             const uint8_t *ex;
@@ -639,15 +645,15 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_
 #pragma unroll
             for (int i = 0; i < RPW; ++i) {
                 const int rs = rs0 + i < nrs ? rs0 + i : nrs - 1;
-                load_row<BITS, CPL>(ex, Dm, rs * rpi + rsub, lr, wc[si][i], wsb[si][i]);
+                load_row<BITS, CPL>(ex, Dm, rs * rpi + rsub, lr, wc[u][i], wsb[u][i]);
             }
         }
         // stage this batch's activations and half-group sums
         if (b0 > 0) __syncthreads();  // the previous batch is done with the LDS
 #pragma unroll
         for (int r = 0; r < kStageMax; ++r) {
-            const int v0 = threadIdx.x * 4 + 1024 * r;
-            if (1024 * r < batch * F) {  // uniform: whole 8-thread groups are live or not
+            const int v0 = threadIdx.x * 4 + 4 * NT * r;
+            if (4 * NT * r < batch * F) {  // uniform: whole 8-thread groups are live or not
                 const bool live = v0 < nb * F;
                 const uint32_t si = sti[r], j = stj[r];
                 if (live) *(float4 *)(s_act + si * FP + j / Q::NV * NVP + j % Q::NV) = stv[r];
@@ -659,7 +665,8 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_
         __syncthreads();
         if (active) {
 #pragma unroll
-            for (int si = 0; si < kDownBatch; ++si) {
+            for (int u = 0; u < kPer; ++u) {
+                const int si = grp + SPLIT * u;
                 if (si < nb) {
                     const int s = (b0 + si == 0) ? K : b0 + si - 1;
                     const float c = lane_bcast(my_c, s);
@@ -679,7 +686,7 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_
                     }
 #pragma unroll
                     for (int i = 0; i < RPW; ++i)
-                        if (rs0 + i < nrs) acc[i] = fmaf(c, qdot_f32<BITS, CPL>(wc[si][i], wsb[si][i], av, X), acc[i]);
+                        if (rs0 + i < nrs) acc[i] = fmaf(c, qdot_f32<BITS, CPL>(wc[u][i], wsb[u][i], av, X), acc[i]);
                 }
             }
         }
@@ -689,16 +696,27 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_
     } else {
         for (int b0 = 0; b0 <= K; b0 += batch) run_batch(b0);
     }
-    if (!active) return;
+    // row sums; with SPLIT groups, group g > 0 hands its sums to group 0 through LDS
     if constexpr (LPR != 0 && RPW <= LPR) {
-        const float v = multi_reduce<RPW, LPR>(acc);
+        float v = multi_reduce<RPW, LPR>(acc);
         const int i = multi_index<RPW, LPR>(lane);
         constexpr int DL = LPR / RPW;  // lanes sharing one reduced row
+        if constexpr (SPLIT > 1) {
+            __shared__ float s_part[SPLIT - 1][4][64];
+            if (grp > 0) s_part[grp - 1][wave][lane] = v;
+            __syncthreads();
+            if (grp > 0) return;
+#pragma unroll
+            for (int q = 0; q < SPLIT - 1; ++q) v += s_part[q][wave][lane];
+        }
+        if (!active) return;
         float xr = xres[0];
 #pragma unroll
         for (int q = 1; q < RPW; ++q) xr = (i == q) ? xres[q] : xr;
         if ((lane & (DL - 1)) == 0 && rs0 + i < nrs) a.y[(size_t)t * H + (rs0 + i) * rpi + rsub] = xr + v;
     } else {
+        static_assert(SPLIT == 1, "split slots need the one-butterfly reduction");
+        if (!active) return;
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const int rs = rs0 + i;
@@ -708,36 +726,33 @@ __global__ __launch_bounds__(256) void k_down(FwdArgs a, int batch, uint32_t f4_
     }
 }
 
-// k_route: softmax -> top-K -> renormalise of one token per block, from the
-// router's logits: the routing that k_gateup's routed blocks do for
+// k_route: softmax -> top-K -> renormalise of one token per one-wave block,
+// from the router's logits: the routing that k_gateup's waves do for
 // themselves, as a kernel of its own for callers that need the selection
 // before the experts run (tiered residency copies the missing experts in
 // between).  Same functions, same results, same writes as k_gateup's block 0.
-template <int EPW>
-__global__ __launch_bounds__(256) void k_route(FwdArgs a) {
+template <int EPL>
+__global__ __launch_bounds__(64) void k_route(FwdArgs a) {
     const int t = blockIdx.x, K = a.s.K, E = a.s.E;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    __shared__ __align__(16) uint64_t s_cand[4 * kMaxTopK];
-    float zq[EPW];
-    load_logits_quarter<EPW>(a.ws.z + (size_t)t * E, E, zq);
+    const int lane = threadIdx.x & 63;
+    float zv[EPL];
+    load_logits_lane<EPL>(a.ws.z + (size_t)t * logit_stride(E), logit_stride(E), zv);
     const float gs = a.ws.gs[t];
-    route_candidates<EPW>(zq, E, K, s_cand);
-    __syncthreads();
-    if (wave == 0) {
-        const RouteSel rt = route_select(K, s_cand);
-        if (rt.rank < K) {
-            a.ws.sel[t * K + rt.rank] = rt.sel;
-            a.ws.coef[t * (K + 1) + rt.rank] = rt.w;
-            if (a.route_idx) a.route_idx[t * K + rt.rank] = rt.sel;
-            if (a.route_w) a.route_w[t * K + rt.rank] = rt.w;
-            if (a.sel_host) a.sel_host[t * K + rt.rank] = rt.sel;
-        }
-        if (lane == 0) a.ws.coef[t * (K + 1) + K] = sigmoidf_(gs);
-        if (a.flag_host) {  // the selection first, then the flag, both pushed out to the host
-            __threadfence_system();
-            if (lane == 0) a.flag_host[t] = a.flag_value;
-            __threadfence_system();
-        }
+    uint32_t key[EPL];
+    logit_keys<EPL>(zv, E, key);
+    const RouteK rt = route_all<EPL>(key, E, K);
+    if (lane < K) {
+        a.ws.sel[t * K + lane] = rt.sel;
+        a.ws.coef[t * (K + 1) + lane] = rt.w;
+        if (a.route_idx) a.route_idx[t * K + lane] = rt.sel;
+        if (a.route_w) a.route_w[t * K + lane] = rt.w;
+        if (a.sel_host) a.sel_host[t * K + lane] = rt.sel;
+    }
+    if (lane == 0) a.ws.coef[t * (K + 1) + K] = sigmoidf_(gs);
+    if (a.flag_host) {  // the selection first, then the flag, both pushed out to the host
+        __threadfence_system();
+        if (lane == 0) a.flag_host[t] = a.flag_value;
+        __threadfence_system();
     }
 }
 
@@ -797,6 +812,7 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st, const SlotP
     } else if (stage == 1) {  // routing + gate/up + SwiGLU
         const QMat &G = a.L.m[0];
         const int rpi = 64 / G.lpr;
+        if ((F / rpi) % kRpwGateUp != 0) return hipErrorInvalidValue;  // a wave's row-steps share one slot
         const int nrs = (K + 1) * F / rpi;
         const int blocks = (nrs + 4 * kRpwGateUp - 1) / (4 * kRpwGateUp);
         dim3 grid(blocks, T);
@@ -826,20 +842,28 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st, const SlotP
         const size_t lds = per_slot * batch;
         const bool one = K + 1 <= batch;
         const uint32_t f4r = (uint32_t)((0x100000000ull + F / 4 - 1) / (F / 4));
+        // two wave groups per block (slots split between them) when all slots
+        // fit one batch and there are at least two of them
+        const bool split = one && K + 1 >= 2;
+        const dim3 b1(256), b2(512);
         if (Dm.cpl == 2) {
-            if (one) hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl);
-            else hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl);
+            if (split) hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, true, TIER, 2>), grid, b2, lds, st, a, batch, f4r, sl);
+            else if (one) hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, true, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl);
+            else hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, false, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl);
         } else if (Dm.cpl == 1) {
-            const int key = (Dm.lpr == 64 ? 0 : Dm.lpr == 32 ? 1 : Dm.lpr == 16 ? 2 : 3) * 2 + (one ? 1 : 0);
+            const int key = (Dm.lpr == 64 ? 0 : Dm.lpr == 32 ? 1 : Dm.lpr == 16 ? 2 : 3) * 3 + (split ? 2 : one ? 1 : 0);
             switch (key) {
-                case 0: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
-                case 1: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
-                case 2: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
-                case 3: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
-                case 4: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
-                case 5: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
-                case 6: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, false, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
-                default: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, true, TIER>), grid, dim3(256), lds, st, a, batch, f4r, sl); break;
+                case 0: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, false, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
+                case 1: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, true, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
+                case 2: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, true, TIER, 2>), grid, b2, lds, st, a, batch, f4r, sl); break;
+                case 3: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, false, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
+                case 4: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, true, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
+                case 5: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, true, TIER, 2>), grid, b2, lds, st, a, batch, f4r, sl); break;
+                case 6: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, false, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
+                case 7: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, true, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
+                case 8: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, true, TIER, 2>), grid, b2, lds, st, a, batch, f4r, sl); break;
+                case 9: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, false, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
+                default: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, true, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
             }
         } else {
             return hipErrorInvalidValue;
@@ -879,8 +903,8 @@ hipError_t launch_forward_route(const FwdArgs &a, hipStream_t stream) {
     hipError_t e = a.s.bits == 4 ? launch_stage<4, false>(a, 0, stream) : launch_stage<2, false>(a, 0, stream);
     if (e != hipSuccess) return e;
     // experts per lane as in k_gateup: 8 up to 512 experts, else 16
-    if (a.s.E > 512) hipLaunchKernelGGL(k_route<4>, dim3(a.T), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(k_route<2>, dim3(a.T), dim3(256), 0, stream, a);
+    if (a.s.E > 512) hipLaunchKernelGGL(k_route<16>, dim3(a.T), dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL(k_route<8>, dim3(a.T), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 

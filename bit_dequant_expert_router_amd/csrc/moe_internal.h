@@ -20,7 +20,7 @@ struct Workspace {
     uint32_t *ctrl;  // control block, kCtrlBytes, zeroed by moe_workspace_init: the streaming
                      // launches' run and exit counters (each launch leaves them at zero)
     float *h;        // [T][H]   normalised tokens
-    float *z;        // [T][E]   router logits
+    float *z;        // [T][logit_stride(E)] router logits
     float *gs;       // [T]      shared-gate logits
     int32_t *sel;    // [T][K]   selected experts
     float *coef;     // [T][K+1] combine coefficients (renormalised weights, sigmoid(gs))
@@ -45,6 +45,11 @@ struct Workspace {
     int32_t *sched;  // passes of the two streaming launches (gate/up, down), each
                      // sched_launch_ints(T, K) ints: head, then kPassRecord ints per pass
 };
+
+// row stride (floats) of the router logits in the workspace: a multiple of 16,
+// so that a lane reads its 8 or 16 logits with 16-byte loads (the padding is
+// never read as a logit)
+MOE_HD int logit_stride(int E) { return (E + 15) & ~15; }
 
 // k-splits of the batched router GEMM: 512 reduction entries per block when H >= 512
 constexpr int kMaxKsplit = kMaxDim / 512;
@@ -98,7 +103,7 @@ inline size_t grouped_ints(const Shape &s, int T) {
 inline size_t workspace_bytes(const Shape &s, int T) {
     size_t b = kCtrlBytes;
     b += align_up((size_t)T * s.H * 4);
-    b += align_up((size_t)T * s.E * 4);
+    b += align_up((size_t)T * logit_stride(s.E) * 4);
     b += align_up((size_t)T * 4);
     b += align_up((size_t)T * s.K * 4);
     b += align_up((size_t)T * (s.K + 1) * 4);
@@ -127,7 +132,7 @@ inline Workspace carve_workspace(void *base, const Shape &s, int T) {
     w.h = (float *)p;
     p += align_up((size_t)T * s.H * 4);
     w.z = (float *)p;
-    p += align_up((size_t)T * s.E * 4);
+    p += align_up((size_t)T * logit_stride(s.E) * 4);
     w.gs = (float *)p;
     p += align_up((size_t)T * 4);
     w.sel = (int32_t *)p;
