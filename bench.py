@@ -604,26 +604,27 @@ def bench_micro(args):
         empty_us = time_replay(g) / R * 1e6
         del g
         fails = 0
-        for kind, what in ((0, "arrivals"), (1, "barrier"), (2, "barrier, replicated release"),
-                           (3, "all-to-all tagged words")):
-            for blocks in (256, 512):
-                for groups in (1, 8, 32):
-                    nb = moe.moe_mb_exchange_bytes(blocks, groups)
-                    buf = torch.zeros(nb, dtype=torch.uint8, device=dev)
-                    g = graph_of(lambda: [moe.moe_mb_exchange(kind, blocks, groups, buf) for _ in range(R)])
-                    us = time_replay(g) / R * 1e6
-                    f = moe.moe_mb_exchange_failures(buf)
-                    fails += f
-                    rows.append({"kind": kind, "pattern": what, "blocks": blocks, "groups": groups,
-                                 "us": round(us, 3), "over_empty_kernel_us": round(us - empty_us, 3),
-                                 "gave_up": f})
-                    del g, buf
+        cases = [(kind, blocks, groups) for kind in (0, 1, 2, 3) for blocks in (256, 512) for groups in (1, 8, 32)]
+        cases += [(4, blocks, groups) for blocks in (512, 1024, 1152) for groups in (8, 32)]
+        names = {0: "arrivals", 1: "barrier", 2: "barrier, replicated release", 3: "all-to-all tagged words",
+                 4: "producers then consumers"}
+        for kind, blocks, groups in cases:
+            nb = moe.moe_mb_exchange_bytes(blocks, groups)
+            buf = torch.zeros(nb, dtype=torch.uint8, device=dev)
+            g = graph_of(lambda: [moe.moe_mb_exchange(kind, blocks, groups, buf) for _ in range(R)])
+            us = time_replay(g) / R * 1e6
+            f = moe.moe_mb_exchange_failures(buf)
+            fails += f
+            rows.append({"kind": kind, "pattern": names[kind], "blocks": blocks, "groups": groups,
+                         "us": round(us, 3), "over_empty_kernel_us": round(us - empty_us, 3), "gave_up": f})
+            del g, buf
         result = dict(base, metric="grid-wide exchange inside one kernel",
                       value=round(min(r["over_empty_kernel_us"] for r in rows if r["kind"] == 1), 3),
                       unit="us over an empty kernel (best grid barrier)", higher_is_better=False,
                       ms_per_step=None, dtype="none",
                       config={"workload": "exchange: arrivals, two-level grid barriers and an all-to-all of "
-                                          "tagged words over 256 and 512 blocks, 1-32 first-level counters"},
+                                          "tagged words over 256 and 512 blocks, 1-32 first-level counters; "
+                                          "producer/consumer halves of 512-1152 blocks"},
                       empty_kernel_us=round(empty_us, 3), waits_given_up=fails, table=rows)
     print(json.dumps(result), flush=True)
 

@@ -544,97 +544,6 @@ __device__ __forceinline__ void rows_dot_lds(const uint4 (&c)[NR][CPL], const fl
     }
 }
 
-// The lane's slice of a vector in limb form, held in registers: limbs
-// [kLimbs][NV/8] words (limb x of entries k0 + 8 i .. k0 + 8 i + 7 in word i),
-// group scales S [NGL] and half-group sums Xh [NV/32].
-template <int BITS, int CPL>
-struct LimbSlice {
-    using Q = QSlice<BITS, CPL>;
-    static constexpr int ND = Q::NV / 8;
-    uint32_t L[kLimbs][ND];
-    float S[Q::NGL];
-    float Xh[Q::NV / 32];
-};
-
-// load the slice at k0 of a vector of n entries whose limbs are [kLimbs][n/8]
-// words, scales [n/64], half-group sums [n/32]
-template <int BITS, int CPL>
-__device__ __forceinline__ void load_limb_slice(const uint32_t *__restrict__ limbs, const float *__restrict__ S_all,
-                                                const float *__restrict__ Xh_all, int n, int k0,
-                                                LimbSlice<BITS, CPL> &v) {
-    using LS = LimbSlice<BITS, CPL>;
-    static_assert(LS::ND % 4 == 0, "whole 16-byte limb loads");
-#pragma unroll
-    for (int x = 0; x < kLimbs; ++x)
-#pragma unroll
-        for (int i = 0; i < LS::ND / 4; ++i) {
-            const uint4 w = *(const uint4 *)(limbs + (size_t)x * (n / 8) + k0 / 8 + 4 * i);
-            v.L[x][4 * i] = w.x;
-            v.L[x][4 * i + 1] = w.y;
-            v.L[x][4 * i + 2] = w.z;
-            v.L[x][4 * i + 3] = w.w;
-        }
-#pragma unroll
-    for (int g = 0; g < QSlice<BITS, CPL>::NGL; ++g) v.S[g] = S_all[k0 / 64 + g];
-#pragma unroll
-    for (int h = 0; h < QSlice<BITS, CPL>::NV / 32; ++h) v.Xh[h] = Xh_all[k0 / 32 + h];
-}
-
-// rows_dot_lds with the lane's limb slice in registers
-template <int BITS, int CPL, int NR>
-__device__ __forceinline__ void rows_dot_reg(const uint4 (&c)[NR][CPL], const float (&s)[NR][QSlice<BITS, CPL>::NGL],
-                                             const float (&o)[NR][QSlice<BITS, CPL>::NGL],
-                                             const LimbSlice<BITS, CPL> &v, float (&out)[NR]) {
-    using Q = QSlice<BITS, CPL>;
-    constexpr int ND = BITS == 4 ? CPL * 4 : CPL * 8;  // limb words per limb in the slice
-    constexpr int DPG = ND / Q::NGL;                    // ... per group
-#pragma unroll
-    for (int r = 0; r < NR; ++r) out[r] = 0.0f;
-#pragma unroll
-    for (int g = 0; g < Q::NGL; ++g) {
-        int hi[NR], lo[NR];
-        auto limb = [&](int x, int (&acc)[NR], bool first) {
-#pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                int a = first ? 0 : (acc[r] << 4);
-#pragma unroll
-                for (int i = 0; i < DPG; ++i) {
-                    const int di = g * DPG + i;  // limb word of the slice
-                    int op;
-                    if constexpr (BITS == 4) {
-                        const uint4 cj = c[r][di / 4];
-                        const uint32_t w[4] = {cj.x, cj.y, cj.z, cj.w};
-                        op = (int)w[di % 4];
-                    } else {
-                        const uint4 cj = c[r][di / 8];
-                        const uint32_t w[4] = {cj.x, cj.y, cj.z, cj.w};
-                        const uint32_t d = w[(di % 8) / 2];
-                        op = (int)((di & 1) ? ((d >> 2) & 0x33333333u) : (d & 0x33333333u));
-                    }
-                    a = __builtin_amdgcn_sdot8(op, (int)v.L[x][di], a, false);
-                }
-                acc[r] = a;
-            }
-        };
-        limb(kLimbs - 1, hi, true);
-#pragma unroll
-        for (int x = kLimbs - 2; x >= 4; --x) limb(x, hi, false);
-        limb(3, lo, true);
-#pragma unroll
-        for (int x = 2; x >= 0; --x) limb(x, lo, false);
-        float xs = 0.0f;
-#pragma unroll
-        for (int hh = 0; hh < Q::GL / 32; ++hh) xs += v.Xh[g * (Q::GL / 32) + hh];
-        const float Sg = v.S[g];
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const float f = fmaf((float)hi[r], 65536.0f, (float)lo[r]);
-            out[r] = fmaf(s[r][g] * Sg, f, out[r]);
-            out[r] = fmaf(o[r][g], xs, out[r]);
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // several partial sums reduced at once over aligned groups of W lanes
 // (N <= W, both powers of two).  The first log2(N) exchange steps halve the

@@ -67,26 +67,35 @@ struct XLayout {
     __host__ __device__ size_t words(int blocks) const { return (size_t)slots() + 2 * (size_t)blocks; }
 };
 
-__device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+// polls are relaxed agent-scope loads (they bypass the caches that are not
+// coherent across XCDs); a wait that succeeds is followed by one acquire
+// fence (an acquire load in the loop would invalidate the L2 on every poll)
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v) {
+__device__ __forceinline__ void st_release(uint32_t *p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t add_agent(uint32_t *p, uint32_t v) {
+__device__ __forceinline__ uint32_t add_acq_rel(uint32_t *p, uint32_t v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void acquire_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 // two-level arrival: returns true in the block that arrives last of all
 // (both levels' counters are reset by their last arrivals)
 __device__ __forceinline__ bool arrive_last(uint32_t *w, int c_first, int c_top, int g, int members, int groups) {
-    const uint32_t old = add_agent(w + c_first + 64 * g, 1u);
+    const uint32_t old = add_acq_rel(w + c_first + 64 * g, 1u);
     if (old + 1 != (uint32_t)members) return false;
-    st_agent(w + c_first + 64 * g, 0u);
-    const uint32_t old2 = add_agent(w + c_top, 1u);
+    st_release(w + c_first + 64 * g, 0u);
+    const uint32_t old2 = add_acq_rel(w + c_top, 1u);
     if (old2 + 1 != (uint32_t)groups) return false;
-    st_agent(w + c_top, 0u);
+    st_release(w + c_top, 0u);
     return true;
+}
+
+// the generation advances once every block has left (two-level exit counters)
+__device__ __forceinline__ void leave(uint32_t *w, const XLayout &L, int g, int members, int groups, uint32_t next) {
+    if (arrive_last(w, L.exitc(0), L.exit_top(), g, members, groups)) st_release(w + L.gen(), next);
 }
 
 __global__ __launch_bounds__(kMbThreads) void k_mb_exchange(int kind, int groups, uint32_t *w) {
@@ -101,26 +110,27 @@ __global__ __launch_bounds__(kMbThreads) void k_mb_exchange(int kind, int groups
         __syncthreads();
         return;
     }
-    const uint32_t gen0 = ld_agent(w + L.gen());
+    const uint32_t gen0 = ld_relaxed(w + L.gen());
+    uint64_t *slot = (uint64_t *)(w + L.slots());
     if (kind == 1 || kind == 2) {
         if (lane == 0) {
             if (arrive_last(w, L.ctr(0), L.top(), g, members, groups)) {
                 if (kind == 2)
-                    for (int r = 0; r < groups; ++r) st_agent(w + L.rep(r), gen0 + 1);
-                st_agent(w + L.gen(), gen0 + 1);
+                    for (int r = 0; r < groups; ++r) st_release(w + L.rep(r), gen0 + 1);
+                st_release(w + L.gen(), gen0 + 1);
             }
             const uint32_t *poll = (kind == 2) ? w + L.rep(g) : w + L.gen();
             uint32_t spins = 0;
-            while (ld_agent(poll) == gen0) {
+            while (ld_relaxed(poll) == gen0) {
                 if (++spins > kSpinLimit) {
-                    add_agent(w, 1u);
+                    add_acq_rel(w, 1u);
                     break;
                 }
             }
+            acquire_fence();
         }
-    } else {  // kind 3
+    } else if (kind == 3) {
         const uint32_t tag = gen0 + 1;
-        uint64_t *slot = (uint64_t *)(w + L.slots());
         if (lane == 0)
             __hip_atomic_store(slot + b, ((uint64_t)tag << 32) | (uint32_t)b, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
@@ -133,12 +143,43 @@ __global__ __launch_bounds__(kMbThreads) void k_mb_exchange(int kind, int groups
             }
             if (__all(ok)) break;
             if (++spins > kSpinLimit) {
-                if (lane == 0) add_agent(w, 1u);
+                if (lane == 0) add_acq_rel(w, 1u);
                 break;
             }
         }
-        // the generation advances once every block has seen every slot
-        if (lane == 0 && arrive_last(w, L.exitc(0), L.exit_top(), g, members, groups)) st_agent(w + L.gen(), tag);
+        if (lane == 0) leave(w, L, g, members, groups, tag);
+    } else {  // kind 4: the first half of the blocks produce, the second half consume
+        const int P = gridDim.x / 2;
+        const uint32_t tag = gen0 + 1;
+        if (b < P) {
+            if (lane == 0) {
+                __hip_atomic_store(slot + b, ((uint64_t)tag << 32) | (uint32_t)b, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                add_acq_rel(w + L.ctr(b % groups), 1u);  // release: the slot before the count
+            }
+        } else {
+            // lanes g < groups poll counter g until the producers have all arrived
+            uint32_t spins = 0;
+            while (true) {
+                const uint32_t c = lane < groups ? ld_relaxed(w + L.ctr(lane)) : 0u;
+                uint32_t tot = c;
+                for (int d = 1; d < 64; d <<= 1) tot += __shfl_xor(tot, d);
+                if (tot >= (uint32_t)P * tag) break;
+                if (++spins > kSpinLimit) {
+                    if (lane == 0) add_acq_rel(w, 1u);
+                    break;
+                }
+            }
+            acquire_fence();
+            // then every producer's word, which must carry this call's tag
+            bool ok = true;
+            for (int i = lane; i < P; i += 64) {
+                const uint64_t v = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = ok && (uint32_t)(v >> 32) == tag;
+            }
+            if (!__all(ok) && lane == 0) add_acq_rel(w, 1u);
+        }
+        if (lane == 0) leave(w, L, g, members, groups, tag);
     }
     __syncthreads();
 }
@@ -186,7 +227,8 @@ size_t moe_mb_exchange_bytes(int32_t blocks, int32_t groups) {
 }
 
 int moe_mb_exchange(int32_t kind, int32_t blocks, int32_t groups, void *buf, size_t buf_bytes, void *stream) {
-    if (kind < 0 || kind > 3 || !exchange_args_ok(blocks, groups) || !buf) return MOE_ERR_INVALID_ARG;
+    if (kind < 0 || kind > 4 || !exchange_args_ok(blocks, groups) || !buf) return MOE_ERR_INVALID_ARG;
+    if (kind == 4 && (blocks < 2 || blocks % 2 != 0 || groups > 64)) return MOE_ERR_INVALID_ARG;
     if (!aligned(buf, 256)) return MOE_ERR_ALIGNMENT;
     if (buf_bytes < moe_mb_exchange_bytes(blocks, groups)) return MOE_ERR_WORKSPACE;
     (void)hipGetLastError();

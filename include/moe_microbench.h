@@ -57,8 +57,17 @@ int moe_mb_empty(int32_t blocks, void *stream);
  *           block polling line b % groups (fewer pollers per address).
  *   kind 3  all-to-all: each block publishes one 64-bit word tagged with the
  *           call's generation; every block polls all of them until each
- *           carries that generation (a router's logits reaching every expert
- *           block).  The generation advances when the last block leaves.
+ *           carries that generation.  The generation advances when the last
+ *           block leaves.
+ *   kind 4  producers and consumers in one grid (blocks even, groups <= 64):
+ *           the first blocks/2 blocks each publish a tagged word and then add
+ *           1 to one of `groups` counters (release); each of the other blocks
+ *           polls the counters until every producer has arrived, then reads
+ *           and checks every producer's word (a router's logits reaching the
+ *           expert blocks of the same launch).  Producers never wait, so the
+ *           grid need not be resident all at once.
+ * Polls are relaxed agent-scope loads, followed by one acquire fence once the
+ * wait succeeds.
  * `buf`: device memory of at least moe_mb_exchange_bytes(blocks, groups)
  * bytes, 256-byte aligned, zeroed once before the first call (for example by
  * hipMemset); every call leaves it valid for the next.  Calls on one `buf`
@@ -66,7 +75,8 @@ int moe_mb_empty(int32_t blocks, void *stream);
  * that gives up raises a flag in the first word of `buf` (read it with
  * moe_mb_exchange_failures after synchronising) and the kernel ends normally.
  * The blocks must be resident together for kinds 1-3 to complete without
- * giving up: at most 2 blocks per compute unit.
+ * giving up: at most 2 blocks per compute unit.  A word that kind 4 finds
+ * without its tag also counts as a give-up.
  */
 int moe_mb_exchange(int32_t kind, int32_t blocks, int32_t groups, void *buf, size_t buf_bytes, void *stream);
 

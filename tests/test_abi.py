@@ -189,7 +189,9 @@ def test_microbench_rejects():
     assert moe.moe_mb_exchange_bytes(4096, 8) == 0
     n = moe.moe_mb_exchange_bytes(256, 8)
     f = moe._lib.moe_mb_exchange
-    assert f(4, 256, 8, A, n, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(5, 256, 8, A, n, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(4, 256, 128, A, moe.moe_mb_exchange_bytes(256, 128), None) == moe.MOE_ERR_INVALID_ARG  # > 64 counters
+    assert f(4, 3, 1, A, moe.moe_mb_exchange_bytes(3, 1), None) == moe.MOE_ERR_INVALID_ARG  # odd grid
     assert f(1, 256, 8, A + 64, n, None) == moe.MOE_ERR_ALIGNMENT
     assert f(1, 256, 8, A, n - 4, None) == moe.MOE_ERR_WORKSPACE
     assert f(1, 256, 8, None, n, None) == moe.MOE_ERR_INVALID_ARG
