@@ -17,7 +17,9 @@ the original trained model, which the pages do not print (parity unpinned).
 
 ``oracle/lru.py`` (pure Python) holds the expert-cache policy of tiered
 residency, a plain least-recently-used cache, pinned in
-``tests/test_tier_oracle.py``.
+``tests/test_tier_oracle.py``.  ``oracle/gdn.py`` (numpy, fp64) holds the
+GatedDeltaNet recurrent-state update of the linear-attention layers, pinned in
+``tests/test_gdn_oracle.py``.
 """
 from __future__ import annotations
 
