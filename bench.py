@@ -18,6 +18,8 @@ Workloads (``--workload``):
   stack60  60 chained 4-bit layers resident in HBM (218 GB); a step is one
            token through all 60 layers, one moe_stack_forward call.
   tier4    tiered expert residency (experts in pinned host memory).
+  gdn      the GatedDeltaNet recurrent-state update of the linear-attention
+           layers: 64 heads x 128 x 128 fp32 state, one token per step.
   stream, gap, exchange   measurement kernels of the library: HBM streaming
            read rate, dependent kernel boundaries, grid-wide exchanges.
 
@@ -62,7 +64,7 @@ KERNEL_TRAFFIC = {
 }
 
 DEFAULT_STEPS = {"layer4": 2048, "layer2": 2048, "tiny": 2048, "batch32": 256, "stack60": 64, "tier4": 512,
-                 "stream": 100, "gap": 200, "exchange": 200}
+                 "gdn": 2048, "stream": 100, "gap": 200, "exchange": 200}
 LAYER_WORKLOADS = ("layer4", "layer2", "tiny", "batch32")
 MICRO_WORKLOADS = ("stream", "gap", "exchange")
 
@@ -84,7 +86,7 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=None, help="timed steps (default: per workload)")
     p.add_argument("--warmup", type=int, default=64)
     p.add_argument("--workload", default="layer4",
-                   choices=list(LAYER_WORKLOADS) + ["stack60", "tier4"] + list(MICRO_WORKLOADS))
+                   choices=list(LAYER_WORKLOADS) + ["stack60", "tier4", "gdn"] + list(MICRO_WORKLOADS))
     p.add_argument("--tier-cache", type=float, default=0.71,
                    help="tier4: device slots as a fraction of the layers' experts")
     p.add_argument("--layers", type=int, default=32, help="resident layers the steps rotate over")
@@ -185,6 +187,8 @@ def main(argv=None):
     refuse_multi_gpu(args)
     if args.workload in MICRO_WORKLOADS:
         return bench_micro(args)
+    if args.workload == "gdn":
+        return bench_gdn(args)
     import synthetic as syn
     wl = syn.WORKLOADS[args.workload]
     if wl.name == "tier4":
@@ -626,6 +630,93 @@ def bench_micro(args):
                                           "tagged words over 256 and 512 blocks, 1-32 first-level counters; "
                                           "producer/consumer halves of 512-1152 blocks"},
                       empty_kernel_us=round(empty_us, 3), waits_given_up=fails, table=rows)
+    print(json.dumps(result), flush=True)
+
+
+# --------------------------------------------------------------------------- #
+# GatedDeltaNet state update
+# --------------------------------------------------------------------------- #
+def gdn_step_bytes(n_heads, d, T=1):
+    """Algorithmic HBM bytes of one call: the fp32 state read and written once,
+    q, k, v, the output and the two gates per token."""
+    return 2 * n_heads * d * d * 4 + T * n_heads * (4 * d * 4 + 2 * 4)
+
+
+def bench_gdn(args):
+    """One token per step through one layer's 64 x 128 x 128 state; the steps
+    rotate over --layers states (default 128: 512 MiB, more than the 256 MB
+    memory-side cache) and a pool of tokens."""
+    import numpy as np
+    import torch
+
+    import bit_dequant_expert_router_amd as moe
+    import synthetic as syn
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    Hh, D = 64, 128
+    L = args.layers if args.layers != 32 else 128
+    P = min(max(1, args.pool), 256)
+    log(args, f"[bench] gdn: {Hh} heads x {D} x {D} fp32 state, {L} layer states, {P} tokens")
+    x = syn.gdn_inputs(0, Hh, D, P)
+    states = torch.from_numpy(np.tile(x["state"], (L, 1, 1, 1))).to(dev)
+    for l in range(L):  # distinct states per layer (scaled copies)
+        states[l].mul_(1.0 + 0.001 * l)
+    q, k, v, alpha, beta = (torch.from_numpy(x[n]).to(dev) for n in ("q", "k", "v", "alpha", "beta"))
+    out = torch.empty((P, Hh, D), dtype=torch.float32, device=dev)
+
+    def step(i):
+        j = i % P
+        moe.moe_gdn_update(Hh, D, D, 1, states[i % L], q[j], k[j], v[j], alpha[j], beta[j], out[j])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    nsteps = args.steps
+    g = graph_of(lambda: [step(i) for i in range(nsteps)])
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # the kernel's own time, between events around a graph of the same launches
+    launch_s = time_replay(g) / nsteps
+    nb = gdn_step_bytes(Hh, D)
+    roof = roofline_entry("k_gdn", nb, launch_s)
+    roof["traffic"] = None
+    result = {
+        "metric": "GatedDeltaNet state updates per second (one token through one layer) and state GB/s",
+        "value": round(nsteps / elapsed, 1),
+        "unit": "layer-tokens/s",
+        "n_gpus": 1,
+        "steps": nsteps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / nsteps, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"gdn: {Hh} heads x {D} x {D} fp32 state, one token per step, {L} layer states",
+                   "n_heads": Hh, "d_k": D, "d_v": D, "layer_states": L, "token_pool": P, "mode": "graph"},
+        "bytes_per_step": nb,
+        "effective_GBps": round(nb * nsteps / elapsed / 1e9, 1),
+        "pct_of_hbm_peak": round(100.0 * nb * nsteps / elapsed / HBM_PEAK_BPS, 2),
+        "roofline": roof,
+    }
+    if args.cpu_sample > 0:
+        import oracle.gdn as og
+        xs = [{n: x[n][j:j + 1] for n in ("q", "k", "v", "alpha", "beta")} for j in range(min(P, 8))]
+        done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 1.5:
+            j = done % len(xs)
+            og.gdn_layer(x["state"], xs[j]["q"], xs[j]["k"], xs[j]["v"], xs[j]["alpha"], xs[j]["beta"])
+            done += 1
+        el = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(done / el, 3), "unit": "layer-tokens/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"{done} single-token updates of the {Hh}-head state, fp64 numpy "
+                                            f"oracle (one head at a time), {el:.1f} s wall"}
     print(json.dumps(result), flush=True)
 
 

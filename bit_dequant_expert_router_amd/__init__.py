@@ -79,6 +79,8 @@ _SIGS = {
     "moe_tier_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(moe_tier_stats_t)]),
     "moe_tier_lookup": (ctypes.c_int, [_vp, _i32, _i32, ctypes.POINTER(ctypes.c_int32)]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    # GatedDeltaNet state update (include/moe_gdn.h)
+    "moe_gdn_update": (ctypes.c_int, [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     # measurement kernels (include/moe_microbench.h)
     "moe_mb_stream_read": (ctypes.c_int, [_vp, _sz, _i32, _i32, _vp, _vp]),
     "moe_mb_empty": (ctypes.c_int, [_i32, _vp]),
@@ -288,6 +290,14 @@ def moe_tier_lookup(state, layer_index: int, expert: int) -> int:
     slot = ctypes.c_int32()
     _check("moe_tier_lookup", _lib.moe_tier_lookup(_addr(state), int(layer_index), int(expert), ctypes.byref(slot)))
     return slot.value
+
+
+# GatedDeltaNet recurrent-state update (include/moe_gdn.h)
+def moe_gdn_update(n_heads: int, d_k: int, d_v: int, n_tokens: int, state, q, k, v, alpha, beta, out,
+                   stream=None) -> int:
+    return _check("moe_gdn_update",
+                  _lib.moe_gdn_update(int(n_heads), int(d_k), int(d_v), int(n_tokens), _addr(state), _addr(q),
+                                      _addr(k), _addr(v), _addr(alpha), _addr(beta), _addr(out), _stream(stream)))
 
 
 # measurement kernels (include/moe_microbench.h): no part of the layer

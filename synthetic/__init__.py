@@ -227,3 +227,23 @@ def layer_dense(seed: int, layer: int, dims: Dims) -> Dict[str, np.ndarray]:
 def tokens(seed: int, n: int, hidden: int, pool: int = 0) -> np.ndarray:
     """n activation vectors x ~ N(0, 1), fp32 [n][hidden]."""
     return _rng(seed, 7, pool).standard_normal(size=(n, hidden), dtype=np.float32)
+
+
+# --------------------------------------------------------------------------- #
+# GatedDeltaNet state update (the linear-attention layers: 64 heads, 128 x 128)
+# --------------------------------------------------------------------------- #
+def gdn_inputs(seed: int, n_heads: int, d: int, n_tokens: int, layer: int = 0) -> Dict[str, np.ndarray]:
+    """Inputs of the state update, fp32: state [heads][d][d] ~ N(0, 0.05);
+    q, k [tokens][heads][d] ~ N(0, 1) then unit L2 norm per head (q also scaled
+    by d^-1/2), as the model feeds them; v [tokens][heads][d] ~ N(0, 1);
+    alpha [tokens][heads] ~ U(0.9, 1) (a gate's decay close to one); beta ~ U(0, 1)."""
+    r = _rng(seed, 11, layer)
+    state = r.normal(0.0, 0.05, (n_heads, d, d)).astype(np.float32)
+    q = r.standard_normal((n_tokens, n_heads, d)).astype(np.float32)
+    k = r.standard_normal((n_tokens, n_heads, d)).astype(np.float32)
+    q = (q / np.linalg.norm(q, axis=-1, keepdims=True) / np.sqrt(d)).astype(np.float32)
+    k = (k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)
+    v = r.standard_normal((n_tokens, n_heads, d)).astype(np.float32)
+    alpha = r.uniform(0.9, 1.0, (n_tokens, n_heads)).astype(np.float32)
+    beta = r.uniform(0.0, 1.0, (n_tokens, n_heads)).astype(np.float32)
+    return {"state": state, "q": q, "k": k, "v": v, "alpha": alpha, "beta": beta}

@@ -197,6 +197,20 @@ def test_microbench_rejects():
     assert f(1, 256, 8, None, n, None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_gdn_rejects():
+    """Argument checks of the GatedDeltaNet update, all on the host."""
+    f = moe._lib.moe_gdn_update
+    P = [A + 0x1000 * i for i in range(7)]
+    assert f(0, 128, 128, 1, *P, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(4097, 128, 128, 1, *P, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(64, 128, 128, 0, *P, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(64, 64, 128, 1, *P, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(64, 128, 256, 1, *P, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(64, 128, 128, 1, None, *P[1:], None) == moe.MOE_ERR_INVALID_ARG
+    assert f(64, 128, 128, 1, P[0] + 8, *P[1:], None) == moe.MOE_ERR_ALIGNMENT
+    assert f(64, 128, 128, 1, P[0], P[1] + 4, *P[2:], None) == moe.MOE_ERR_ALIGNMENT
+
+
 def test_stage_rejects():
     dims = d()
     wsb = moe.moe_workspace_bytes(dims, 1)

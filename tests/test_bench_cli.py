@@ -18,7 +18,7 @@ def test_workloads_listed():
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True, text=True,
                          timeout=120)
     assert res.returncode == 0
-    for w in ("layer4", "layer2", "batch32", "tier4", "stack60", "tiny", "stream", "gap", "exchange"):
+    for w in ("layer4", "layer2", "batch32", "tier4", "stack60", "tiny", "gdn", "stream", "gap", "exchange"):
         assert w in res.stdout
 
 
@@ -66,3 +66,10 @@ def test_default_steps_per_workload():
     assert b.parse_args([]).steps == 2048 and b.parse_args([]).workload == "layer4"
     assert b.parse_args(["--workload", "stack60"]).steps == 64
     assert b.parse_args(["--workload", "stack60", "--steps", "5"]).steps == 5
+
+
+def test_gdn_bytes():
+    """One token through 64 heads of 128 x 128 fp32 state: 4 MiB read and
+    4 MiB written, plus q, k, v and the output (4 x 32 KiB) and the gates."""
+    b = _bench()
+    assert b.gdn_step_bytes(64, 128) == 2 * 4 * 1024 * 1024 + 4 * 32 * 1024 + 64 * 8
