@@ -93,9 +93,21 @@ __device__ __forceinline__ bool arrive_last(uint32_t *w, int c_first, int c_top,
     return true;
 }
 
-// the generation advances once every block has left (two-level exit counters)
+// the generation advances once every block has left (two-level exit
+// counters).  Relaxed: these words guard no other data (the exchanged words
+// carry their own tags), so no cache write-back or invalidation is needed
+__device__ __forceinline__ uint32_t add_relaxed(uint32_t *p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void leave(uint32_t *w, const XLayout &L, int g, int members, int groups, uint32_t next) {
-    if (arrive_last(w, L.exitc(0), L.exit_top(), g, members, groups)) st_release(w + L.gen(), next);
+    if (add_relaxed(w + L.exitc(g), 1u) + 1 != (uint32_t)members) return;
+    st_relaxed(w + L.exitc(g), 0u);
+    if (add_relaxed(w + L.exit_top(), 1u) + 1 != (uint32_t)groups) return;
+    st_relaxed(w + L.exit_top(), 0u);
+    st_relaxed(w + L.gen(), next);
 }
 
 __global__ __launch_bounds__(kMbThreads) void k_mb_exchange(int kind, int groups, uint32_t *w) {
@@ -155,7 +167,7 @@ __global__ __launch_bounds__(kMbThreads) void k_mb_exchange(int kind, int groups
             if (lane == 0) {
                 __hip_atomic_store(slot + b, ((uint64_t)tag << 32) | (uint32_t)b, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-                add_acq_rel(w + L.ctr(b % groups), 1u);  // release: the slot before the count
+                add_relaxed(w + L.ctr(b % groups), 1u);  // the slot carries its own tag
             }
         } else {
             // lanes g < groups poll counter g until the producers have all arrived
@@ -170,8 +182,8 @@ __global__ __launch_bounds__(kMbThreads) void k_mb_exchange(int kind, int groups
                     break;
                 }
             }
-            acquire_fence();
-            // then every producer's word, which must carry this call's tag
+            // then every producer's word, which must carry this call's tag (a
+            // word seen before its store landed is counted as a give-up)
             bool ok = true;
             for (int i = lane; i < P; i += 64) {
                 const uint64_t v = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -66,8 +66,10 @@ int moe_mb_empty(int32_t blocks, void *stream);
  *           and checks every producer's word (a router's logits reaching the
  *           expert blocks of the same launch).  Producers never wait, so the
  *           grid need not be resident all at once.
- * Polls are relaxed agent-scope loads, followed by one acquire fence once the
- * wait succeeds.
+ * Polls are relaxed agent-scope loads.  The barriers (kinds 1, 2) release
+ * and acquire (one acquire fence once the wait succeeds); the exchanges of
+ * tagged words (kinds 3, 4) are relaxed throughout, as their words validate
+ * themselves.
  * `buf`: device memory of at least moe_mb_exchange_bytes(blocks, groups)
  * bytes, 256-byte aligned, zeroed once before the first call (for example by
  * hipMemset); every call leaves it valid for the next.  Calls on one `buf`
