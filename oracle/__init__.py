@@ -220,6 +220,31 @@ def layer(dims, x: np.ndarray, dense: Dict[str, np.ndarray],
     return {"out": out, "idx": idx, "w": w, "z": z, "gs": gs, "h": h}
 
 
+def layer_forced(dims, x: np.ndarray, dense: Dict[str, np.ndarray],
+                 fetch_expert: Callable[[int], Dict[str, List[np.ndarray]]], idx: Sequence[int]):
+    """The layer for one token with the selection given (K distinct experts, in
+    the order given): for a near tie, where either selection is correct, the
+    outputs the other selection defines.  The weights are the softmax restricted
+    to the selection, exp(z_k - m) / sum_j exp(z_j - m) with m the largest
+    selected logit, which equals the full softmax renormalised over it."""
+    E, K = dims.n_experts, dims.top_k
+    idx = [int(e) for e in idx]
+    if len(idx) != K or len(set(idx)) != K or min(idx) < 0 or max(idx) >= E:
+        raise ValueError("layer_forced: K distinct experts expected")
+    h = rmsnorm(x, dense["norm_weight"], dims.rms_eps)
+    z = gemv_bf16(dense["router_weight"], h)
+    gs = float(gemv_bf16(np.asarray(dense["shared_gate"]).reshape(1, -1), h)[0])
+    zs = z[idx]
+    p = np.exp(zs - np.max(zs))
+    w = p / np.sum(p)
+    out = np.asarray(x, np.float32).astype(np.float64)
+    for k in range(K + 1):
+        e = idx[k] if k < K else E
+        coef = float(w[k]) if k < K else sigmoid(gs)
+        out = out + coef * expert(fetch_expert(e), h, dims.group_size)
+    return {"out": out, "idx": np.array(idx, np.int32), "w": w, "z": z, "gs": gs, "h": h}
+
+
 def near_tie(z: np.ndarray, k: int, rel: float = 1e-5) -> bool:
     """True when the K-th and (K+1)-th largest logits are closer than
     rel * max(1, max|z|): then either selection is a correct routing."""

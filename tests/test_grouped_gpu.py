@@ -13,7 +13,7 @@ import pytest
 
 import synthetic as syn
 
-from _parity import check_token, dense_layer, log, oracle_layer_generated, run_layer
+from _parity import check_token, dense_layer, log, oracle_layer_canonical, oracle_layer_generated, run_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -131,7 +131,7 @@ def test_many_experts_grouped(moe):
     x = syn.tokens(15, 25, dims.hidden)
     assert moe.moe_forward_stage_count(dims, 25) == 7
     out, idx, wt = run_layer(dims, lw, x)
-    refs = [oracle.layer_all(dims, x[t], dense, experts) for t in range(x.shape[0])]
+    refs = [oracle_layer_canonical(dims, x[t], dense, experts) for t in range(x.shape[0])]
     for t in range(x.shape[0]):
         check_token(out[t], idx[t], wt[t], refs[t], dims.top_k, f"1024 experts token {t}")
     out, idx, wt = run_layer(dims, lw, x[:2])
@@ -173,7 +173,7 @@ def test_batch_past_grouping_limit(moe):
     x = syn.tokens(17, T, dims.hidden)
     out, idx, wt = run_layer(dims, lw, x)
     for t in (0, 1, 1000, 2047, 2048):
-        check_token(out[t], idx[t], wt[t], oracle.layer_all(dims, x[t], dense, experts), dims.top_k,
+        check_token(out[t], idx[t], wt[t], oracle_layer_canonical(dims, x[t], dense, experts), dims.top_k,
                     f"token {t} of {T}")
     og, ig, wg = run_layer(dims, lw, x[:T - 1])
     assert np.array_equal(ig, idx[:T - 1])

@@ -337,3 +337,30 @@ def test_sigmoid_values():
     assert oracle.sigmoid(0.0) == 0.5
     assert abs(oracle.sigmoid(np.log(3.0)) - 0.75) < 1e-15
     assert abs(oracle.sigmoid(-np.log(3.0)) - 0.25) < 1e-15
+
+
+def test_layer_forced_equals_layer_on_its_own_selection_and_renormalises():
+    """With the oracle's own selection, the forced layer is the layer; with
+    another selection its weights are that selection's renormalised softmax
+    (they sum to 1 and follow the logits' order) and its output is the same
+    combine with those experts."""
+    d = syn.WORKLOADS["tiny"].dims
+    dense = syn.layer_dense(0, 0, d)
+    experts = [syn.expert_canonical(0, 0, e, d) for e in range(d.n_experts + 1)]
+    x = syn.tokens(0, 2, d.hidden)
+    for t in range(2):
+        a = oracle.layer(d, x[t], dense, lambda e: experts[e])
+        b = oracle.layer_forced(d, x[t], dense, lambda e: experts[e], a["idx"])
+        np.testing.assert_allclose(b["out"], a["out"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(b["w"], a["w"], rtol=0, atol=1e-15)
+        other = [int(a["idx"][0]), [e for e in range(d.n_experts) if e not in a["idx"]][0]]
+        c = oracle.layer_forced(d, x[t], dense, lambda e: experts[e], other)
+        assert abs(float(np.sum(c["w"])) - 1.0) < 1e-15
+        z = c["z"][other]
+        assert (c["w"][0] > c["w"][1]) == (z[0] > z[1])
+        ref = np.asarray(x[t], np.float64) + sum(c["w"][k] * oracle.expert(experts[other[k]], c["h"])
+                                                 for k in range(2)) + \
+            oracle.sigmoid(c["gs"]) * oracle.expert(experts[d.n_experts], c["h"])
+        np.testing.assert_allclose(c["out"], ref, rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.layer_forced(d, x[0], dense, lambda e: experts[e], [1, 1])

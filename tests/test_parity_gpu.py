@@ -10,8 +10,8 @@ import pytest
 import oracle
 import synthetic as syn
 
-from _parity import (canon_expert, check_token, dense_layer, log, oracle_layer_generated, rel_l2,
-                     run_layer)
+from _parity import (NEAR_TIES, canon_expert, check_token, dense_layer, log, oracle_layer_canonical,
+                     oracle_layer_generated, rel_l2, run_layer)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +44,7 @@ def test_tiny_layer(moe):
     x = syn.tokens(0, 53, dims.hidden)  # a ragged grouped batch (106 assignments), plus single-token calls
     out, idx, wt = run_layer(dims, lw, x)
     for t in range(x.shape[0]):
-        ref = oracle.layer_all(dims, x[t], dense, experts)
+        ref = oracle_layer_canonical(dims, x[t], dense, experts)
         check_token(out[t], idx[t], wt[t], ref, dims.top_k, f"tiny token {t}")
     # single-token calls (ungrouped kernels) agree with the grouped batch
     for t in (0, 7):
@@ -81,7 +81,7 @@ def test_small_shapes(moe, shape):
     T = max(5, -(-GROUPED_MIN_ASSIGN // K))
     x = syn.tokens(3, T, H)
     checked = list(range(5)) + [T - 1]
-    refs = {t: oracle.layer_all(dims, x[t], dense, experts) for t in checked}
+    refs = {t: oracle_layer_canonical(dims, x[t], dense, experts) for t in checked}
     assert moe.moe_forward_stage_count(dims, T) == 7
     out, idx, wt = run_layer(dims, lw, x)
     for t in checked:
@@ -107,7 +107,7 @@ def test_inplace_determinism_and_optional_outputs(moe, n_tokens):
     assert np.array_equal(a, b) and np.array_equal(ia, ib) and np.array_equal(wa, wb)
     assert np.array_equal(a, c) and np.array_equal(a, d)
     for t in range(n_tokens):
-        check_token(a[t], ia[t], wa[t], oracle.layer_all(dims, x[t], dense, experts), dims.top_k, f"token {t}")
+        check_token(a[t], ia[t], wa[t], oracle_layer_canonical(dims, x[t], dense, experts), dims.top_k, f"token {t}")
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 3), ("tiny", 50), ("layer4", 1), ("layer4", 6)])
@@ -171,7 +171,7 @@ def test_zero_router_selects_first_experts(moe):
     assert (idx == np.arange(dims.top_k)).all() and np.all(wt == np.float32(1.0 / dims.top_k))
     dense0 = dict(dense, router_weight=np.zeros_like(dense["router_weight"]))
     for t in range(3):
-        check_token(out[t], idx[t], wt[t], oracle.layer_all(dims, x[t], dense0, experts), dims.top_k)
+        check_token(out[t], idx[t], wt[t], oracle_layer_canonical(dims, x[t], dense0, experts), dims.top_k)
 
 
 # --------------------------------------------------------------------------- #
@@ -257,25 +257,27 @@ def _stack(moe, n_layers, n_check_tokens=1):
     for t in range(T):
         xo = x[t].astype(np.float32)  # oracle, free running
         xg = x[t].astype(np.float32)  # GPU state fed to each oracle layer
-        free_ok = True
         for l in range(n_layers):
             ref_tf = oracle_layer_generated(dims, w.seed, l, xg)
             og, ig, wg = run_layer(dims, layers[l], xg[None])
             check_token(og[0], ig[0], wg[0], ref_tf, K, f"stack layer {l} (teacher-forced)", unit_scale=True)
-            if free_ok:
-                ref_fr = oracle_layer_generated(dims, w.seed, l, xo)
-                if list(ref_fr["idx"]) != list(ridx[l, t]):
-                    assert oracle.near_tie(ref_fr["z"], K), f"layer {l}: {ridx[l, t]} vs {ref_fr['idx']}"
-                    free_ok = False
-                xo = ref_fr["out"].astype(np.float32)
+            ref_fr = oracle_layer_generated(dims, w.seed, l, xo)
+            if list(ref_fr["idx"]) != list(ridx[l, t]):
+                # either selection is correct at a near tie: the free-running
+                # oracle follows the GPU's from here
+                assert oracle.near_tie(ref_fr["z"], K), f"layer {l}: {ridx[l, t]} vs {ref_fr['idx']}"
+                NEAR_TIES.append((f"stack layer {l} (free-running)", list(ridx[l, t]), list(ref_fr["idx"])))
+                log(f"stack layer {l}: near tie, free-running oracle follows the GPU's selection")
+                ref_fr = ref_fr["refit"]([int(e) for e in ridx[l, t]])
+            xo = ref_fr["out"].astype(np.float32)
             xg = og[0]
         assert np.array_equal(xg, y[t]), "stack call and chained layer calls differ"
-        if free_ok:
-            e2 = rel_l2(y[t], ref_fr["out"])
-            ea = float(np.max(np.abs(y[t] - ref_fr["out"])))
-            rms = float(np.sqrt(np.mean(np.square(ref_fr["out"]))))
-            log(f"stack free-running: rel-L2 {e2:.2e}, max-abs {ea:.2e}, rms(out) {rms:.3g}")
-            assert e2 <= 1e-4 and ea <= 1e-3 * max(1.0, rms)
+        e2 = rel_l2(y[t], ref_fr["out"])
+        ea = float(np.max(np.abs(y[t] - ref_fr["out"])))
+        rms = float(np.sqrt(np.mean(np.square(ref_fr["out"]))))
+        log(f"stack of {n_layers} free-running: rel-L2 {e2:.2e}, max-abs {ea:.2e}, rms(out) {rms:.3g}, "
+            f"near ties so far {len(NEAR_TIES)}")
+        assert e2 <= 1e-4 and ea <= 1e-3 * max(1.0, rms)
 
 
 def test_stack_4_layers(moe):

@@ -80,15 +80,22 @@ def _run(moe, dims, n_layers, n_slots, max_tokens, calls, seed=0, oracle_first=F
             ir = torch.full_like(it, -2)
             wt = torch.full((T, K), -1.0, dtype=torch.float32, device="cuda")
             wr = torch.full_like(wt, -2.0)
+            xin = xt.cpu().numpy() if oracle_first and c == 0 else None
             moe.moe_tier_layer_forward(state, l, tier_layer, xt, yt, T, it, wt, ws)
             moe.moe_layer_forward(dims, lw.descriptor(), xr, yr, T, ir, wr, ws_ref)
             torch.cuda.synchronize()
             assert torch.equal(it, ir), (c, l)
             assert _same(wt, wr), (c, l)
             assert _same(yt, yr), (c, l)
-            if oracle_first and c == 0 and l == 0:
-                ref = oracle_layer_generated(dims, seed, 0, x_all[0])
-                check_token(yt[0].cpu().numpy(), it[0].cpu().numpy(), wt[0].cpu().numpy(), ref, K, "tier token 0")
+            if oracle_first and c == 0:
+                # up to four tokens of every layer of the first call against the
+                # oracle, fed the layer's input as the GPU saw it (teacher forcing)
+                yh, ih, wh = yt.cpu().numpy(), it.cpu().numpy(), wt.cpu().numpy()
+                for t in range(min(T, 4)):
+                    if not np.all(np.isfinite(xin[t])):
+                        continue
+                    ref = oracle_layer_generated(dims, seed, l, xin[t])
+                    check_token(yh[t], ih[t], wh[t], ref, K, f"tier layer {l} token {t}", unit_scale=l > 0)
             accesses += layer_accesses(l, ir.cpu().numpy(), E)
             xt, xr = yt, yr
     hits, cache = lru_run(accesses, n_slots)
