@@ -53,14 +53,16 @@ METRIC = "MoE-layer decode tokens/s (effective expert-weight HBM GB/s and % of p
 # on.  FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0, the ratios of bytes
 # moved to counts reported for a 256 MiB copy.
 KERNEL_TRAFFIC = {
-    ("layer4", "k_gateup"): {"source_sha256_prefix": "5271af809b8e5ad3", "fetch_kib": 11640.0, "write_kib": 20.1,
+    ("layer4", "k_gateup"): {"source_sha256_prefix": "4a64665a77e8a6b1", "fetch_kib": 11642.6, "write_kib": 20.1,
                              "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer4", "k_down"): {"source_sha256_prefix": "5271af809b8e5ad3", "fetch_kib": 5929.5, "write_kib": 16.0,
+    ("layer4", "k_down"): {"source_sha256_prefix": "4a64665a77e8a6b1", "fetch_kib": 5910.0, "write_kib": 16.0,
                            "fetch_scale": 2.0, "write_scale": 1.0},
     ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "8bcffc6967ec026c", "fetch_kib": 576830.0,
                                       "write_kib": 3622.5, "fetch_scale": 2.0, "write_scale": 1.0},
     ("batch32", "k_grouped_down"): {"source_sha256_prefix": "8bcffc6967ec026c", "fetch_kib": 289846.8,
                                     "write_kib": 6145.0, "fetch_scale": 2.0, "write_scale": 1.0},
+    ("gdn", "k_gdn"): {"source_sha256_prefix": "e92c6a24a6b75ce2", "fetch_kib": 2354.5, "write_kib": 4128.0,
+                       "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
 DEFAULT_STEPS = {"layer4": 2048, "layer2": 2048, "tiny": 2048, "batch32": 256, "stack60": 64, "tier4": 512,
@@ -69,15 +71,23 @@ LAYER_WORKLOADS = ("layer4", "layer2", "tiny", "batch32")
 MICRO_WORKLOADS = ("stream", "gap", "exchange")
 
 
-def kernel_source_hash(grouped):
-    """sha256 of the sources the expert kernels are built from."""
+def source_hash(names):
     h = hashlib.sha256()
-    names = ["moe_device.h", "moe_internal.h", "moe_layout.h",
-             "moe_grouped.hip" if grouped else "moe_forward.hip"]
     for n in names:
         with open(os.path.join(ROOT, "bit_dequant_expert_router_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def kernel_source_hash(grouped):
+    """sha256 of the sources the expert kernels are built from."""
+    return source_hash(["moe_device.h", "moe_internal.h", "moe_layout.h",
+                        "moe_grouped.hip" if grouped else "moe_forward.hip"])
+
+
+def gdn_source_hash():
+    """sha256 of the sources the GatedDeltaNet kernel is built from."""
+    return source_hash(["moe_device.h", "moe_gdn.hip"])
 
 
 def parse_args(argv=None):
@@ -166,9 +176,11 @@ def stage_names(n_stages):
     return ["k_router", "k_gateup", "k_down"]
 
 
-def traffic_of(wl_name, kernel, grouped):
+def traffic_of(wl_name, kernel, sha):
+    """Measured HBM bytes per launch, or None when the sources (hash `sha`)
+    have changed since the counters were taken."""
     tr = KERNEL_TRAFFIC.get((wl_name, kernel))
-    if tr is not None and tr["source_sha256_prefix"] == kernel_source_hash(grouped)[:16]:
+    if tr is not None and tr["source_sha256_prefix"] == sha[:16]:
         return round((tr["fetch_kib"] * tr["fetch_scale"] + tr["write_kib"] * tr["write_scale"]) * 1024)
     return None
 
@@ -354,7 +366,8 @@ def bench_layer(args, wl):
     expert_stages = [k for k, n in enumerate(names) if "gateup" in n or "down" in n]
     dom = max(expert_stages, key=lambda k: stage_s[k])
     roof = dict(stages[dom])
-    roof["traffic"] = traffic_of(wl.name, names[dom], grouped) if T == wl.n_tokens else None
+    roof["traffic"] = (traffic_of(wl.name, names[dom], kernel_source_hash(grouped))
+                       if T == wl.n_tokens else None)
 
     result = {
         "metric": METRIC,
@@ -683,7 +696,7 @@ def bench_gdn(args):
     launch_s = time_replay(g) / nsteps
     nb = gdn_step_bytes(Hh, D)
     roof = roofline_entry("k_gdn", nb, launch_s)
-    roof["traffic"] = None
+    roof["traffic"] = traffic_of("gdn", "k_gdn", gdn_source_hash())
     result = {
         "metric": "GatedDeltaNet state updates per second (one token through one layer) and state GB/s",
         "value": round(nsteps / elapsed, 1),
