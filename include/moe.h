@@ -225,9 +225,17 @@ int moe_forward_stage_count(const moe_dims_t *dims, int32_t n_tokens);
 
 /*
  * n_layers layers chained: x_{l+1} = layer_l(x_l), x_0 = x, y = x_{n_layers}
- * (no final norm).  `layers` is a HOST array of n_layers layer descriptors.
- * route_idx / route_w (device or NULL): [n_layers][n_tokens][K].
+ * (no final norm), the per-layer pipeline repeated over the model's 60 layers
+ * ("48GB内存运行397B模型", section "MoE稀疏架构": 60 layers, each with 512 experts
+ * and top-K routing; flash-moe README translation, "Pipeline mỗi lớp": a layer's
+ * expert command buffer runs the experts, the combine and the norm, and the
+ * next layer starts from its output).  `layers` is a HOST array of n_layers
+ * layer descriptors.  route_idx / route_w (device or NULL):
+ * [n_layers][n_tokens][K].
  * Every layer is enqueued back to back on `stream`; nothing waits on the host.
+ * The result equals n_layers chained moe_layer_forward calls bit for bit: the
+ * next layer's RMSNorm stays in its router kernel, which reads all of x_{l+1}
+ * for the router product anyway.
  */
 int moe_stack_forward(const moe_dims_t *dims, const moe_layer_t *layers, int32_t n_layers,
                       const float *x, float *y, int32_t n_tokens, int32_t *route_idx,

@@ -284,6 +284,42 @@ def test_stack_4_layers(moe):
     _stack(moe, 4)
 
 
+def _stack_run(moe, dims, layers, x):
+    T, K, L = x.shape[0], dims.top_k, len(layers)
+    xt = torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+    yt = torch.empty_like(xt)
+    ridx = torch.empty((L, T, K), dtype=torch.int32, device="cuda")
+    rw = torch.empty((L, T, K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_workspace_bytes(dims, T), dtype=torch.uint8, device="cuda")
+    moe.moe_workspace_init(ws)
+    moe.moe_stack_forward(dims, [l.descriptor() for l in layers], xt, yt, T, ridx, rw, ws)
+    torch.cuda.synchronize()
+    return yt.cpu().numpy(), ridx.cpu().numpy(), rw.cpu().numpy()
+
+
+@pytest.mark.parametrize("workload,T", [("stack60", 1), ("stack60", 2), ("stack60", 3), ("stack60", 4),
+                                        ("layer2", 3), ("tiny", 3)])
+def test_stack_each_layer_against_the_oracle(moe, workload, T):
+    """Layer l of an n-layer stack call (n = 1, 2, 3) against the oracle layer
+    fed the stack's own output after l layers: every layer of the stack is held
+    to the single-layer bar on the state the stack itself produced (1 to 4
+    tokens; the 4-bit and 2-bit decode shapes and the tiny shape)."""
+    from bit_dequant_expert_router_amd.weights import layer_generated
+    w = syn.WORKLOADS[workload]
+    dims = w.dims
+    layers = [layer_generated(dims, dense_layer(w.seed, l, dims), w.seed, l) for l in range(3)]
+    x = syn.tokens(w.seed + 17, T, dims.hidden)
+    prev = x.astype(np.float32)
+    for n in (1, 2, 3):
+        log(f"{workload} stack of {n}, {T} tokens")
+        y, ridx, rw = _stack_run(moe, dims, layers[:n], x)
+        for t in range(T):
+            ref = oracle_layer_generated(dims, w.seed, n - 1, prev[t])
+            check_token(y[t], ridx[n - 1, t], rw[n - 1, t], ref, dims.top_k,
+                        f"{workload} stack of {n}, token {t}", unit_scale=True)
+        prev = y
+
+
 def test_stack_60_layers(moe):
     torch.cuda.empty_cache()
     _stack(moe, 60)
