@@ -13,7 +13,9 @@ import os
 from typing import Optional, Sequence
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
+# MOE_LIBRARY names another build of the same library (the host-sanitizer
+# build of tests/sanitize_host.py); it is loaded in its place, never as a fallback
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(PKG_DIR, "libmoe.so")
 
 # torch first: its bundled HIP runtime (soname libamdhip64.so.7) must be the
 # one libmoe.so binds to.  Loading libmoe.so first would bring in a second HIP

@@ -33,6 +33,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 SRC_PATH = os.path.join(_HERE, "moe_oracle.c")
+# ORACLE_LIBRARY: another build of moe_oracle.c to load (the host-sanitizer
+# build of tests/sanitize_host.py)
+_LOAD_PATH = os.environ.get("ORACLE_LIBRARY") or LIB_PATH
 
 
 def build(force: bool = False) -> str:
@@ -58,9 +61,9 @@ _i64 = ctypes.c_int64
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
+        if _LOAD_PATH == LIB_PATH and not os.path.exists(LIB_PATH):
             build()
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(_LOAD_PATH)
         L.oracle_threads.restype = ctypes.c_int
         L.oracle_dequant.restype = ctypes.c_double
         L.oracle_dequant.argtypes = [ctypes.c_uint8, ctypes.c_uint16, ctypes.c_uint16]
