@@ -57,10 +57,14 @@ KERNEL_TRAFFIC = {
                              "fetch_scale": 2.0, "write_scale": 1.0},
     ("layer4", "k_down"): {"source_sha256_prefix": "4a64665a77e8a6b1", "fetch_kib": 5910.0, "write_kib": 16.0,
                            "fetch_scale": 2.0, "write_scale": 1.0},
-    ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "8bcffc6967ec026c", "fetch_kib": 576830.0,
-                                      "write_kib": 3622.5, "fetch_scale": 2.0, "write_scale": 1.0},
-    ("batch32", "k_grouped_down"): {"source_sha256_prefix": "8bcffc6967ec026c", "fetch_kib": 289846.8,
-                                    "write_kib": 6145.0, "fetch_scale": 2.0, "write_scale": 1.0},
+    ("layer2", "k_gateup"): {"source_sha256_prefix": "4a64665a77e8a6b1", "fetch_kib": 6521.75, "write_kib": 20.125,
+                             "fetch_scale": 2.0, "write_scale": 1.0},
+    ("layer2", "k_down"): {"source_sha256_prefix": "4a64665a77e8a6b1", "fetch_kib": 3349.5, "write_kib": 16.0,
+                           "fetch_scale": 2.0, "write_scale": 1.0},
+    ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "4e71aef98f1e1d78", "fetch_kib": 570919.375,
+                                      "write_kib": 3619.953, "fetch_scale": 2.0, "write_scale": 1.0},
+    ("batch32", "k_grouped_down"): {"source_sha256_prefix": "4e71aef98f1e1d78", "fetch_kib": 287824.531,
+                                    "write_kib": 6141.469, "fetch_scale": 2.0, "write_scale": 1.0},
     ("gdn", "k_gdn"): {"source_sha256_prefix": "e92c6a24a6b75ce2", "fetch_kib": 2354.5, "write_kib": 4128.0,
                        "fetch_scale": 2.0, "write_scale": 1.0},
 }
@@ -505,7 +509,11 @@ def bench_stack(args, wl):
     stages = [roofline_entry(n, b, s) for n, b, s in zip(names, sbytes, stage_s)]
     dom = 1 if stage_s[1] >= stage_s[2] else 2
     roof = dict(stages[dom])
-    roof["traffic"] = None
+    # the stack runs the single layer's kernels on the same shape, one token
+    # per launch: their measured traffic per launch is the single layer's
+    single = {(4, 4096, 1024, 512, 4): "layer4", (2, 4096, 1024, 512, 4): "layer2"}.get(
+        (dims.bits, dims.hidden, dims.ffn, dims.n_experts, dims.top_k))
+    roof["traffic"] = traffic_of(single, names[dom], kernel_source_hash(False)) if single else None
 
     result = {
         "metric": METRIC,
