@@ -303,7 +303,11 @@ def test_stack_each_layer_against_the_oracle(moe, workload, T):
     """Layer l of an n-layer stack call (n = 1, 2, 3) against the oracle layer
     fed the stack's own output after l layers: every layer of the stack is held
     to the single-layer bar on the state the stack itself produced (1 to 4
-    tokens; the 4-bit and 2-bit decode shapes and the tiny shape)."""
+    tokens; the 4-bit and 2-bit decode shapes and the tiny shape).  The
+    synthetic 2-bit layers (weights of negative mean) pass their input through
+    from the second layer on: every gate sum is so negative that SiLU leaves
+    nothing of it in fp32 or fp64, so there those layers check the routing
+    (exact) and the identity."""
     from bit_dequant_expert_router_amd.weights import layer_generated
     w = syn.WORKLOADS[workload]
     dims = w.dims
