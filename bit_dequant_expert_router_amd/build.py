@@ -22,6 +22,9 @@ FLAGS = [
     # a single-lane atomic keeps its own return (the wave-combining rewrite
     # reads the result at once, which waits for every load in flight)
     "-Xarch_device", "-mllvm=-amdgpu-atomic-optimizer-strategy=None",
+    # kernel-argument preloading: a kernel's leading scalar parameters (up to
+    # 16 dwords) arrive in SGPRs, so its first loads wait for no argument read
+    "-Xarch_device", "-mllvm=-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

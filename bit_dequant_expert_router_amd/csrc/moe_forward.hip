@@ -126,7 +126,13 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_router_split (H = 2048 or 4096): the 4 waves of a block split H into
+// k_router_split (H = 2048 or 4096): the router rows, shared gate, x, gamma,
+// H and E come as leading scalar parameters, which the hardware preloads into
+// SGPRs (the library is built with kernel-argument preloading), so the first
+// loads wait for no read of the argument segment: 0.25 us less per layer.
+// (The expert kernels' first loads need the workspace areas and the expert
+// layout, more than the 16 preloadable dwords; deriving those on the device
+// cost more than the read.)  The 4 waves of a block split H into
 // quarters of the block's RB router rows (one row per block measures fastest:
 // 513 blocks spread the 4 MiB over the whole chip), so a wave reads 1/4 of x
 // and gamma instead of all of it.  The dot products use x * gamma; the factor
@@ -137,12 +143,14 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router(FwdArgs a) {
 constexpr int kRouterSplitRows = 1;
 
 template <int CPL_R>
-__global__ __launch_bounds__(256) void k_router_split(FwdArgs a) {
+__global__ __launch_bounds__(256) void k_router_split(const uint16_t *__restrict__ p_router,
+                                                      const uint16_t *__restrict__ p_sgate,
+                                                      const float *__restrict__ p_x,
+                                                      const uint16_t *__restrict__ p_gamma, int H, int E, FwdArgs a) {
     constexpr int RB = kRouterSplitRows;
     const int t = blockIdx.y;
-    const int H = a.s.H, E = a.s.E;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const float *x = a.x + (size_t)t * H;
+    const float *x = p_x + (size_t)t * H;
     const int r0 = blockIdx.x * RB;
     // lane's chunks of 8 entries: wave quarter + lane + 64 j
     const int kq = wave * (H / 4);
@@ -150,7 +158,7 @@ __global__ __launch_bounds__(256) void k_router_split(FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
         const int row = r0 + r <= E ? r0 + r : E;  // rows past the end re-read the gate row, unused
-        const uint16_t *src = (row < E) ? a.router + (size_t)row * H : a.sgate;
+        const uint16_t *src = (row < E) ? p_router + (size_t)row * H : p_sgate;
 #pragma unroll
         for (int j = 0; j < CPL_R; ++j) wv[r][j] = ld_stream16(src + kq + 8 * (lane + 64 * j));
     }
@@ -163,13 +171,13 @@ __global__ __launch_bounds__(256) void k_router_split(FwdArgs a) {
         const float4 x1 = *(const float4 *)(x + k0 + 4);
         xv[8 * j + 0] = x0.x; xv[8 * j + 1] = x0.y; xv[8 * j + 2] = x0.z; xv[8 * j + 3] = x0.w;
         xv[8 * j + 4] = x1.x; xv[8 * j + 5] = x1.y; xv[8 * j + 6] = x1.z; xv[8 * j + 7] = x1.w;
-        gv[j] = *(const uint4 *)(a.gamma + k0);
+        gv[j] = *(const uint4 *)(p_gamma + k0);
     }
     // this block's share of the limb encoding: entry k of h (x and gamma fetched now)
     const int ke = blockIdx.x * 256 + threadIdx.x;
     const bool enc = blockIdx.x * 256 < H;
     const float xe = x[ke < H ? ke : 0];
-    const float ge = __uint_as_float((uint32_t)a.gamma[ke < H ? ke : 0] << 16);
+    const float ge = __uint_as_float((uint32_t)p_gamma[ke < H ? ke : 0] << 16);
 
     float ss = 0.0f;
     float xg[CPL_R * 8];
@@ -788,10 +796,10 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st, const SlotP
         const bool one = T < kRouterTokens;
         const dim3 grid(blocks, one ? T : (T + kRouterTokens - 1) / kRouterTokens);
         if (H == 4096) {
-            if (one) hipLaunchKernelGGL(k_router_split<2>, grid, dim3(256), 0, st, a);
+            if (one) hipLaunchKernelGGL(k_router_split<2>, grid, dim3(256), 0, st, a.router, a.sgate, a.x, a.gamma, H, E, a);
             else hipLaunchKernelGGL((k_router_tokens<2, kRouterTokens>), grid, dim3(256), 0, st, a);
         } else {
-            if (one) hipLaunchKernelGGL(k_router_split<1>, grid, dim3(256), 0, st, a);
+            if (one) hipLaunchKernelGGL(k_router_split<1>, grid, dim3(256), 0, st, a.router, a.sgate, a.x, a.gamma, H, E, a);
             else hipLaunchKernelGGL((k_router_tokens<1, kRouterTokens>), grid, dim3(256), 0, st, a);
         }
     } else if (stage == 0) {  // RMSNorm + router + limbs of h
