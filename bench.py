@@ -53,13 +53,13 @@ METRIC = "MoE-layer decode tokens/s (effective expert-weight HBM GB/s and % of p
 # on.  FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0, the ratios of bytes
 # moved to counts reported for a 256 MiB copy.
 KERNEL_TRAFFIC = {
-    ("layer4", "k_gateup"): {"source_sha256_prefix": "4a64665a77e8a6b1", "fetch_kib": 11642.6, "write_kib": 20.1,
+    ("layer4", "k_gateup"): {"source_sha256_prefix": "0a20177202daafe6", "fetch_kib": 11639.688, "write_kib": 20.125,
                              "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer4", "k_down"): {"source_sha256_prefix": "4a64665a77e8a6b1", "fetch_kib": 5910.0, "write_kib": 16.0,
+    ("layer4", "k_down"): {"source_sha256_prefix": "0a20177202daafe6", "fetch_kib": 5910.031, "write_kib": 16.0,
                            "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer2", "k_gateup"): {"source_sha256_prefix": "4a64665a77e8a6b1", "fetch_kib": 6521.75, "write_kib": 20.125,
+    ("layer2", "k_gateup"): {"source_sha256_prefix": "0a20177202daafe6", "fetch_kib": 6521.781, "write_kib": 20.125,
                              "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer2", "k_down"): {"source_sha256_prefix": "4a64665a77e8a6b1", "fetch_kib": 3349.5, "write_kib": 16.0,
+    ("layer2", "k_down"): {"source_sha256_prefix": "0a20177202daafe6", "fetch_kib": 3348.0, "write_kib": 16.0,
                            "fetch_scale": 2.0, "write_scale": 1.0},
     ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "4e71aef98f1e1d78", "fetch_kib": 570919.375,
                                       "write_kib": 3619.953, "fetch_scale": 2.0, "write_scale": 1.0},
