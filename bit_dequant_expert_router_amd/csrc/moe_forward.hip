@@ -130,9 +130,10 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router(FwdArgs a) {
 // H and E come as leading scalar parameters, which the hardware preloads into
 // SGPRs (the library is built with kernel-argument preloading), so the first
 // loads wait for no read of the argument segment: 0.25 us less per layer.
-// (The expert kernels' first loads need the workspace areas and the expert
-// layout, more than the 16 preloadable dwords; deriving those on the device
-// cost more than the read.)  The 4 waves of a block split H into
+// k_gateup and k_down take the pointers of their own first loads the same way
+// (the expert layout and pointers, needed once those are issued, stay in
+// FwdArgs: deriving them on the device costs more scalar instructions per
+// wave than the argument read).  The 4 waves of a block split H into
 // quarters of the block's RB router rows (one row per block measures fastest:
 // 513 blocks spread the 4 MiB over the whole chip), so a wave reads 1/4 of x
 // and gamma instead of all of it.  The dot products use x * gamma; the factor
@@ -384,11 +385,39 @@ __global__ __launch_bounds__(256) void k_router_tokens(FwdArgs a) {
 // TIER: the selected experts' routing is already done (k_route) and their
 // weights sit in cache slots, sl.s[t * K + rank] (a.experts = the slots' base)
 template <int BITS, int CPL, int RPW, int EPL, int LPR, bool TIER>
-__global__ __launch_bounds__(256) void k_gateup(FwdArgs a, SlotParam<TIER> sl) {
+__global__ __launch_bounds__(256) void k_gateup(const float *__restrict__ p_z, const float *__restrict__ p_gs,
+                                                const uint32_t *__restrict__ p_hl, const float *__restrict__ p_hs,
+                                                const float *__restrict__ p_hx, int H, int E, FwdArgs a,
+                                                SlotParam<TIER> sl) {
     using Q = QSlice<BITS, CPL>;
     const int t = blockIdx.y;
-    const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+    // 1. loads that do not depend on the routing, from the preloaded
+    //    parameters alone (issued before anything reads FwdArgs): the logits
+    //    (resident path), the shared-gate logit and this thread's share of h's
+    //    limb form
+    float zv[EPL];
+    if constexpr (!TIER) load_logits_lane<EPL>(p_z + (size_t)t * logit_stride(E), logit_stride(E), zv);
+    const float gs = p_gs[t];
+    // kStage 16-byte pieces per thread (a native vector type: an array of
+    // int4 can keep dead copies in scratch memory)
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    constexpr int kStage = (kLimbs * kMaxDim / 32 + 255) / 256;
+    const int n16 = kLimbs * H / 32;
+    i32x4 st[kStage];
+    {
+        const i32x4 *src = (const i32x4 *)(p_hl + (size_t)t * kLimbs * (H / 8));
+#pragma unroll
+        for (int j = 0; j < kStage; ++j) {
+            const int i = threadIdx.x + 256 * j;
+            st[j] = src[i < n16 ? i : 0];
+        }
+    }
+    const float hs = p_hs[(size_t)t * (H / 64) + (threadIdx.x < H / 64 ? threadIdx.x : 0)];
+    const float hx = p_hx[(size_t)t * (H / 32) + (threadIdx.x < H / 32 ? threadIdx.x : 0)];
+
+    const int F = a.s.F, K = a.s.K;
     const QMat &G = a.L.m[0];
     const QMat &U = a.L.m[1];
     const int lpr = G.lpr, rpi = 64 / lpr;
@@ -406,28 +435,6 @@ __global__ __launch_bounds__(256) void k_gateup(FwdArgs a, SlotParam<TIER> sl) {
     __shared__ __align__(16) uint32_t s_hl[kLimbs * kMaxDim / 8];  // limbs of h, [kLimbs][H/8]
     __shared__ float s_hs[kMaxDim / 64];
     __shared__ float s_hx[kMaxDim / 32];
-
-    // 1. loads that do not depend on the routing: the logits (resident path),
-    //    the shared-gate logit and this thread's share of h's limb form
-    float zv[EPL];
-    if constexpr (!TIER) load_logits_lane<EPL>(a.ws.z + (size_t)t * logit_stride(E), logit_stride(E), zv);
-    const float gs = a.ws.gs[t];
-    // kStage 16-byte pieces per thread (a native vector type: an array of
-    // int4 can keep dead copies in scratch memory)
-    typedef int i32x4 __attribute__((ext_vector_type(4)));
-    constexpr int kStage = (kLimbs * kMaxDim / 32 + 255) / 256;
-    const int n16 = kLimbs * H / 32;
-    i32x4 st[kStage];
-    {
-        const i32x4 *src = (const i32x4 *)((const uint32_t *)a.ws.hl + (size_t)t * kLimbs * (H / 8));
-#pragma unroll
-        for (int j = 0; j < kStage; ++j) {
-            const int i = threadIdx.x + 256 * j;
-            st[j] = src[i < n16 ? i : 0];
-        }
-    }
-    const float hs = a.ws.hs[(size_t)t * (H / 64) + (threadIdx.x < H / 64 ? threadIdx.x : 0)];
-    const float hx = a.ws.hx[(size_t)t * (H / 32) + (threadIdx.x < H / 32 ? threadIdx.x : 0)];
 
     // 2. the wave's expert (the shared expert's waves do not wait for the logits)
     const uint8_t *ex;
@@ -568,12 +575,15 @@ constexpr int kDownStageValues = 5120;  // activations staged per batch (batch *
 // TIER: the selected experts sit in cache slots, sl.s[t * K + rank] (a.experts
 // = the slots' base)
 template <int BITS, int CPL, int RPW, int LPR, bool ONE, bool TIER, int SPLIT>
-__global__ __launch_bounds__(256 * SPLIT) void k_down(FwdArgs a, int batch, uint32_t f4_recip, SlotParam<TIER> sl) {
+__global__ __launch_bounds__(256 * SPLIT) void k_down(const float *__restrict__ p_x, const int32_t *__restrict__ p_sel,
+                                                     const float *__restrict__ p_coef, const float *__restrict__ p_act,
+                                                     int H, int F, int K, int batch, uint32_t f4_recip, FwdArgs a,
+                                                     SlotParam<TIER> sl) {
     using Q = QSlice<BITS, CPL>;
     constexpr int NT = 256 * SPLIT;                                  // threads per block
     constexpr int kPer = (kDownBatch + SPLIT - 1) / SPLIT;          // slot positions per wave group
     const int t = blockIdx.y;
-    const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K;
+    const int E = a.s.E;
     const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3, grp = threadIdx.x >> 8;
     const QMat &Dm = a.L.m[2];
     const int lpr = LPR ? LPR : Dm.lpr, rpi = 64 / lpr;
@@ -589,7 +599,7 @@ __global__ __launch_bounds__(256 * SPLIT) void k_down(FwdArgs a, int batch, uint
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int rs = rs0 + i < nrs ? rs0 + i : nrs - 1;
-        xres[i] = a.x[(size_t)t * H + rs * rpi + rsub];
+        xres[i] = p_x[(size_t)t * H + rs * rpi + rsub];
     }
 
     constexpr int NVP = Q::NV + 4;  // padded slice
@@ -603,8 +613,8 @@ __global__ __launch_bounds__(256 * SPLIT) void k_down(FwdArgs a, int batch, uint
     // past the end read a valid entry)
     int my_e;
     if constexpr (TIER) my_e = sl.s[t * K + (lane < K ? lane : K - 1)];
-    else my_e = a.ws.sel[t * K + (lane < K ? lane : K - 1)];
-    const float my_c = a.ws.coef[t * (K + 1) + (lane <= K ? lane : K)];
+    else my_e = p_sel[t * K + (lane < K ? lane : K - 1)];
+    const float my_c = p_coef[t * (K + 1) + (lane <= K ? lane : K)];
 
     float acc[RPW];
 #pragma unroll
@@ -623,7 +633,7 @@ __global__ __launch_bounds__(256 * SPLIT) void k_down(FwdArgs a, int batch, uint
         // with f4_recip = ceil(2^32 / (F/4)) (exact: p (F/4) < 2^32)
         float4 stv[kStageMax];
         uint32_t sti[kStageMax], stj[kStageMax];
-        const float *act_t = a.ws.act + (size_t)t * (K + 1) * F;
+        const float *act_t = p_act + (size_t)t * (K + 1) * F;
 #pragma unroll
         for (int r = 0; r < kStageMax; ++r) {
             const uint32_t p = threadIdx.x + NT * r;
@@ -827,12 +837,12 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st, const SlotP
         const bool wide = E > 512;
         const bool full = G.lpr == 64;  // rows of 64 lanes: one butterfly for the whole step
         switch (G.cpl * 4 + (wide ? 2 : 0) + (full ? 1 : 0)) {
-            case 4: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 0, TIER>), grid, dim3(256), 0, st, a, sl); break;
-            case 5: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 64, TIER>), grid, dim3(256), 0, st, a, sl); break;
-            case 6: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 0, TIER>), grid, dim3(256), 0, st, a, sl); break;
-            case 7: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 64, TIER>), grid, dim3(256), 0, st, a, sl); break;
-            case 9: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 8, 64, TIER>), grid, dim3(256), 0, st, a, sl); break;
-            case 11: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 16, 64, TIER>), grid, dim3(256), 0, st, a, sl); break;
+            case 4: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 0, TIER>), grid, dim3(256), 0, st, a.ws.z, a.ws.gs, (const uint32_t *)a.ws.hl, a.ws.hs, a.ws.hx, H, E, a, sl); break;
+            case 5: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 64, TIER>), grid, dim3(256), 0, st, a.ws.z, a.ws.gs, (const uint32_t *)a.ws.hl, a.ws.hs, a.ws.hx, H, E, a, sl); break;
+            case 6: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 0, TIER>), grid, dim3(256), 0, st, a.ws.z, a.ws.gs, (const uint32_t *)a.ws.hl, a.ws.hs, a.ws.hx, H, E, a, sl); break;
+            case 7: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 64, TIER>), grid, dim3(256), 0, st, a.ws.z, a.ws.gs, (const uint32_t *)a.ws.hl, a.ws.hs, a.ws.hx, H, E, a, sl); break;
+            case 9: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 8, 64, TIER>), grid, dim3(256), 0, st, a.ws.z, a.ws.gs, (const uint32_t *)a.ws.hl, a.ws.hs, a.ws.hx, H, E, a, sl); break;
+            case 11: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 16, 64, TIER>), grid, dim3(256), 0, st, a.ws.z, a.ws.gs, (const uint32_t *)a.ws.hl, a.ws.hs, a.ws.hx, H, E, a, sl); break;
             default: return hipErrorInvalidValue;
         }
     } else if (stage == 2) {  // down + combine + residual
@@ -855,23 +865,23 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st, const SlotP
         const bool split = one && K + 1 >= 2;
         const dim3 b1(256), b2(512);
         if (Dm.cpl == 2) {
-            if (split) hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, true, TIER, 2>), grid, b2, lds, st, a, batch, f4r, sl);
-            else if (one) hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, true, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl);
-            else hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, false, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl);
+            if (split) hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, true, TIER, 2>), grid, b2, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl);
+            else if (one) hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, true, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl);
+            else hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, false, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl);
         } else if (Dm.cpl == 1) {
             const int key = (Dm.lpr == 64 ? 0 : Dm.lpr == 32 ? 1 : Dm.lpr == 16 ? 2 : 3) * 3 + (split ? 2 : one ? 1 : 0);
             switch (key) {
-                case 0: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, false, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
-                case 1: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, true, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
-                case 2: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, true, TIER, 2>), grid, b2, lds, st, a, batch, f4r, sl); break;
-                case 3: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, false, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
-                case 4: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, true, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
-                case 5: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, true, TIER, 2>), grid, b2, lds, st, a, batch, f4r, sl); break;
-                case 6: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, false, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
-                case 7: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, true, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
-                case 8: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, true, TIER, 2>), grid, b2, lds, st, a, batch, f4r, sl); break;
-                case 9: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, false, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
-                default: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, true, TIER, 1>), grid, b1, lds, st, a, batch, f4r, sl); break;
+                case 0: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, false, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
+                case 1: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, true, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
+                case 2: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, true, TIER, 2>), grid, b2, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
+                case 3: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, false, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
+                case 4: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, true, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
+                case 5: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, true, TIER, 2>), grid, b2, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
+                case 6: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, false, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
+                case 7: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, true, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
+                case 8: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, true, TIER, 2>), grid, b2, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
+                case 9: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, false, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
+                default: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, true, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
             }
         } else {
             return hipErrorInvalidValue;
