@@ -25,40 +25,40 @@ constexpr int kGdnD = 128;   // d_k = d_v
 constexpr int kGdnRw = 2;    // row-steps (two rows each) per wave
 constexpr int kGdnStepsPerHead = kGdnD / 2;
 
-struct GdnArgs {
-    int n_heads, T;
-    float *state;
-    const float *q, *k, *v, *alpha, *beta;
-    float *out;
-};
-
 __device__ __forceinline__ float dot4(const float4 a, const float4 b) {
     return fmaf(a.w, b.w, fmaf(a.z, b.z, fmaf(a.y, b.y, a.x * b.x)));
 }
 
+// The first 14 dwords of arguments (the sizes and every input's pointer) are
+// preloaded into SGPRs (the library is built with kernel-argument preloading),
+// so no load waits for a read of the argument segment; the output pointer,
+// needed only at the stores, is read from it.
 template <int RW>
-__global__ __launch_bounds__(256) void k_gdn(GdnArgs g) {
+__global__ __launch_bounds__(256) void k_gdn(int n_heads, int T, float *__restrict__ state,
+                                             const float *__restrict__ qp, const float *__restrict__ kp,
+                                             const float *__restrict__ vp, const float *__restrict__ alphap,
+                                             const float *__restrict__ betap, float *__restrict__ outp) {
     static_assert(kGdnStepsPerHead % RW == 0, "a wave's row-steps belong to one head");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 31, half = lane >> 5;
     const int rs0 = (blockIdx.x * 4 + wave) * RW;  // the wave's first row-step
-    if (rs0 >= g.n_heads * kGdnStepsPerHead) return;  // no barrier in this kernel
+    if (rs0 >= n_heads * kGdnStepsPerHead) return;  // no barrier in this kernel
     const int h = rs0 / kGdnStepsPerHead;
     int row[RW];
     float4 S[RW];
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
         row[r] = 2 * (rs0 + r - h * kGdnStepsPerHead) + half;  // row of the head's state
-        S[r] = *(const float4 *)(g.state + ((size_t)h * kGdnD + row[r]) * kGdnD + 4 * lr);
+        S[r] = *(const float4 *)(state + ((size_t)h * kGdnD + row[r]) * kGdnD + 4 * lr);
     }
-    for (int t = 0; t < g.T; ++t) {
-        const size_t th = (size_t)t * g.n_heads + h;
-        const float4 kv = *(const float4 *)(g.k + th * kGdnD + 4 * lr);
-        const float4 qv = *(const float4 *)(g.q + th * kGdnD + 4 * lr);
-        const float alpha = g.alpha[th], beta = g.beta[th];
+    for (int t = 0; t < T; ++t) {
+        const size_t th = (size_t)t * n_heads + h;
+        const float4 kv = *(const float4 *)(kp + th * kGdnD + 4 * lr);
+        const float4 qv = *(const float4 *)(qp + th * kGdnD + 4 * lr);
+        const float alpha = alphap[th], beta = betap[th];
         float vv[RW];
 #pragma unroll
-        for (int r = 0; r < RW; ++r) vv[r] = g.v[th * kGdnD + row[r]];
+        for (int r = 0; r < RW; ++r) vv[r] = vp[th * kGdnD + row[r]];
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
             // scale: the decayed state
@@ -74,11 +74,15 @@ __global__ __launch_bounds__(256) void k_gdn(GdnArgs g) {
             S[r] = s;
             // matrix-vector product: the head's output
             const float o = lane_sum<32>(dot4(s, qv));
-            if (lr == 0) g.out[th * kGdnD + row[r]] = o;
+            // (the empty asm keeps the output pointer's read out of the loop
+            // head, so that the first token's loads do not wait for it)
+            float *op = outp;
+            asm volatile("" : "+s"(op));
+            if (lr == 0) op[th * kGdnD + row[r]] = o;
         }
     }
 #pragma unroll
-    for (int r = 0; r < RW; ++r) *(float4 *)(g.state + ((size_t)h * kGdnD + row[r]) * kGdnD + 4 * lr) = S[r];
+    for (int r = 0; r < RW; ++r) *(float4 *)(state + ((size_t)h * kGdnD + row[r]) * kGdnD + 4 * lr) = S[r];
 }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -95,19 +99,10 @@ extern "C" int moe_gdn_update(int32_t n_heads, int32_t d_k, int32_t d_v, int32_t
     if (!aligned(state, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 4) || !aligned(alpha, 4) ||
         !aligned(beta, 4) || !aligned(out, 4))
         return MOE_ERR_ALIGNMENT;
-    GdnArgs g;
-    g.n_heads = n_heads;
-    g.T = n_tokens;
-    g.state = state;
-    g.q = q;
-    g.k = k;
-    g.v = v;
-    g.alpha = alpha;
-    g.beta = beta;
-    g.out = out;
     const int waves = n_heads * kGdnStepsPerHead / kGdnRw;
     const int blocks = (waves + 3) / 4;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(k_gdn<kGdnRw>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, g);
+    hipLaunchKernelGGL(k_gdn<kGdnRw>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (int)n_heads, (int)n_tokens,
+                       state, q, k, v, alpha, beta, out);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
