@@ -370,21 +370,25 @@ __global__ __launch_bounds__(256) void k_router_tokens(FwdArgs a) {
 // ---------------------------------------------------------------------------
 // k_gateup: RPW row-steps per wave over the (K+1) x F gate/up row pairs.
 // A wave's row-steps belong to one slot (F / rows-per-step is a multiple of
-// RPW).  A wave of a routed slot s loads all E logits of the token (EPL per
-// lane, two or four 16-byte loads) and runs s + 1 routing rounds (route_slot)
-// to find its expert; a wave of the shared expert needs none, and its blocks
-// are dispatched first.  Each wave issues its weight loads as soon as its
-// expert is known, with no barrier before them.
-// The limb form of h is staged in LDS once per block, and the block's one
-// barrier comes after every wave has issued its weight loads, so it only
-// orders the staging before the products.  Block 0's wave 0 finally takes all
-// K rounds and writes the selection, the renormalised weights and sigmoid(g_s).
+// RPW).  Every wave loads all E logits of the token (EPL per lane, two or four
+// 16-byte loads); a routed slot s takes s + 1 routing rounds (route_slot) to
+// find its expert; the shared expert needs none, and its blocks are
+// dispatched first.  The limb form of h is staged in LDS once per block.
+// BR false: every wave of a routed slot routes and issues its weight loads as
+// soon as its expert is known; the block's one barrier comes after every wave
+// has issued them, so it only orders the staging before the products.
+// BR true (a block's waves share one slot): only wave 0 of a routed block
+// routes and hands the expert to the other waves through LDS at the block's
+// barrier, which then also orders the staging; the other waves' routing
+// instructions are saved (the products are VALU-bound once the weights land).
+// Block 0's wave 0 finally takes all K rounds and writes the selection, the
+// renormalised weights and sigmoid(g_s).
 // ---------------------------------------------------------------------------
 // LPR: lanes per row when the step's partial sums are reduced together (64);
 // 0: one reduction per row
 // TIER: the selected experts' routing is already done (k_route) and their
 // weights sit in cache slots, sl.s[t * K + rank] (a.experts = the slots' base)
-template <int BITS, int CPL, int RPW, int EPL, int LPR, bool TIER>
+template <int BITS, int CPL, int RPW, int EPL, int LPR, bool TIER, bool BR>
 __global__ __launch_bounds__(256) void k_gateup(const float *__restrict__ p_z, const float *__restrict__ p_gs,
                                                 const uint32_t *__restrict__ p_hl, const float *__restrict__ p_hs,
                                                 const float *__restrict__ p_hx, int H, int E, FwdArgs a,
@@ -429,25 +433,52 @@ __global__ __launch_bounds__(256) void k_gateup(const float *__restrict__ p_z, c
     const int lb = blockIdx.x < nbs ? blockIdx.x + gridDim.x - nbs : blockIdx.x - nbs;
     const int rs0 = (lb * 4 + wave) * RPW;
     const bool active = rs0 < nrs;
-    // slot of every row-step of the wave (waves past the end take the last one)
-    const int slot = ((active ? rs0 : nrs - 1) * rpi) / F;
+    // slot of every row-step of the wave (waves past the end take the last one;
+    // with BR the whole block's)
+    const int slot = __builtin_amdgcn_readfirstlane(((active ? rs0 : nrs - 1) * rpi) / F);
 
     __shared__ __align__(16) uint32_t s_hl[kLimbs * kMaxDim / 8];  // limbs of h, [kLimbs][H/8]
     __shared__ float s_hs[kMaxDim / 64];
     __shared__ float s_hx[kMaxDim / 32];
+    __shared__ int s_ex;  // BR: the block's expert
 
     // 2. the wave's expert (the shared expert's waves do not wait for the logits)
-    const uint8_t *ex;
+    const uint8_t *ex = a.shared;
+    bool late = false;  // BR, routed block: weight loads after the barrier
     if constexpr (TIER) {
         ex = (slot < K) ? a.experts + (size_t)sl.s[t * K + slot] * a.L.bytes : a.shared;
+    } else if constexpr (BR) {
+        late = slot < K;
+        if (late && __builtin_amdgcn_readfirstlane(wave) == 0) {
+            uint32_t key[EPL];
+            logit_keys<EPL>(zv, E, key);
+            const int e = route_slot<EPL>(key, E, slot);
+            if (lane == 0) s_ex = e;
+        }
     } else {
         if (slot < K) {
             uint32_t key[EPL];
             logit_keys<EPL>(zv, E, key);
             ex = a.experts + (size_t)route_slot<EPL>(key, E, slot) * a.L.bytes;
-        } else {
-            ex = a.shared;
         }
+    }
+
+    // h's limbs into LDS (the staged loads were issued first, so this waits
+    // for them only), then the block's barrier
+    auto stage = [&]() {
+        i32x4 *dst = (i32x4 *)s_hl;
+#pragma unroll
+        for (int j = 0; j < kStage; ++j) {
+            const int i = threadIdx.x + 256 * j;
+            if (i < n16) dst[i] = st[j];
+        }
+        if (threadIdx.x < H / 64) s_hs[threadIdx.x] = hs;
+        if (threadIdx.x < H / 32) s_hx[threadIdx.x] = hx;
+        __syncthreads();
+    };
+    if (late) {  // block-uniform
+        stage();
+        ex = a.experts + (size_t)s_ex * a.L.bytes;
     }
 
     // 3. weight loads, all unconditional (row-steps past the end re-read the
@@ -471,19 +502,8 @@ __global__ __launch_bounds__(256) void k_gateup(const float *__restrict__ p_z, c
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // 4. h's limbs into LDS (the staged loads were issued before the weights,
-    //    so this waits for them only), then the block's barrier
-    {
-        i32x4 *dst = (i32x4 *)s_hl;
-#pragma unroll
-        for (int j = 0; j < kStage; ++j) {
-            const int i = threadIdx.x + 256 * j;
-            if (i < n16) dst[i] = st[j];
-        }
-        if (threadIdx.x < H / 64) s_hs[threadIdx.x] = hs;
-        if (threadIdx.x < H / 32) s_hx[threadIdx.x] = hx;
-    }
-    __syncthreads();
+    // 4. the staging and barrier of the other blocks, behind their weight loads
+    if (!late) stage();
 
     // 5. codes prepared once, then every row against the lane's limb slice of h
     //    in LDS, limb-major
@@ -789,7 +809,10 @@ __global__ __launch_bounds__(256) void k_fetch(FetchArgs f) {
     }
 }
 
-constexpr int kRpwGateUp = 2;
+// gate/up row-steps per wave: with 4-bit codes the routed blocks route once
+// per block and take one row-step per wave (more waves share the products)
+template <int BITS, bool TIER>
+constexpr int kRpwGateUp = (BITS == 4 && !TIER) ? 1 : 2;
 constexpr int kRouterTokens = 4;  // tokens per k_router_tokens block
 constexpr int kRpwDown4 = 2;  // 4-bit codes
 constexpr int kRpwDown2 = 1;  // 2-bit codes
@@ -830,21 +853,35 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st, const SlotP
     } else if (stage == 1) {  // routing + gate/up + SwiGLU
         const QMat &G = a.L.m[0];
         const int rpi = 64 / G.lpr;
-        if ((F / rpi) % kRpwGateUp != 0) return hipErrorInvalidValue;  // a wave's row-steps share one slot
+        constexpr int RG = kRpwGateUp<BITS, TIER>;
+        if ((F / rpi) % RG != 0) return hipErrorInvalidValue;  // a wave's row-steps share one slot
         const int nrs = (K + 1) * F / rpi;
-        const int blocks = (nrs + 4 * kRpwGateUp - 1) / (4 * kRpwGateUp);
+        const int blocks = (nrs + 4 * RG - 1) / (4 * RG);
         dim3 grid(blocks, T);
         const bool wide = E > 512;
         const bool full = G.lpr == 64;  // rows of 64 lanes: one butterfly for the whole step
-        switch (G.cpl * 4 + (wide ? 2 : 0) + (full ? 1 : 0)) {
-            case 4: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 0, TIER>), grid, dim3(256), 0, st, a.ws.z, a.ws.gs, (const uint32_t *)a.ws.hl, a.ws.hs, a.ws.hx, H, E, a, sl); break;
-            case 5: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 8, 64, TIER>), grid, dim3(256), 0, st, a.ws.z, a.ws.gs, (const uint32_t *)a.ws.hl, a.ws.hs, a.ws.hx, H, E, a, sl); break;
-            case 6: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 0, TIER>), grid, dim3(256), 0, st, a.ws.z, a.ws.gs, (const uint32_t *)a.ws.hl, a.ws.hs, a.ws.hx, H, E, a, sl); break;
-            case 7: hipLaunchKernelGGL((k_gateup<BITS, 1, kRpwGateUp, 16, 64, TIER>), grid, dim3(256), 0, st, a.ws.z, a.ws.gs, (const uint32_t *)a.ws.hl, a.ws.hs, a.ws.hx, H, E, a, sl); break;
-            case 9: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 8, 64, TIER>), grid, dim3(256), 0, st, a.ws.z, a.ws.gs, (const uint32_t *)a.ws.hl, a.ws.hs, a.ws.hx, H, E, a, sl); break;
-            case 11: hipLaunchKernelGGL((k_gateup<BITS, 2, kRpwGateUp, 16, 64, TIER>), grid, dim3(256), 0, st, a.ws.z, a.ws.gs, (const uint32_t *)a.ws.hl, a.ws.hs, a.ws.hx, H, E, a, sl); break;
+        // routing once per block when a block's waves share one slot
+        const bool br = !TIER && (F / rpi) % (4 * RG) == 0;
+        const int sel = (br ? 16 : 0) + G.cpl * 4 + (wide ? 2 : 0) + (full ? 1 : 0);
+#define MOE_GATEUP(CPL, EPL, LPR, BR)                                                                      \
+    hipLaunchKernelGGL((k_gateup<BITS, CPL, RG, EPL, LPR, TIER, BR>), grid, dim3(256), 0, st, a.ws.z, a.ws.gs, \
+                       (const uint32_t *)a.ws.hl, a.ws.hs, a.ws.hx, H, E, a, sl)
+        switch (sel) {
+            case 4: MOE_GATEUP(1, 8, 0, false); break;
+            case 5: MOE_GATEUP(1, 8, 64, false); break;
+            case 6: MOE_GATEUP(1, 16, 0, false); break;
+            case 7: MOE_GATEUP(1, 16, 64, false); break;
+            case 9: MOE_GATEUP(2, 8, 64, false); break;
+            case 11: MOE_GATEUP(2, 16, 64, false); break;
+            case 20: MOE_GATEUP(1, 8, 0, !TIER); break;
+            case 21: MOE_GATEUP(1, 8, 64, !TIER); break;
+            case 22: MOE_GATEUP(1, 16, 0, !TIER); break;
+            case 23: MOE_GATEUP(1, 16, 64, !TIER); break;
+            case 25: MOE_GATEUP(2, 8, 64, !TIER); break;
+            case 27: MOE_GATEUP(2, 16, 64, !TIER); break;
             default: return hipErrorInvalidValue;
         }
+#undef MOE_GATEUP
     } else if (stage == 2) {  // down + combine + residual
         const QMat &Dm = a.L.m[2];
         const int rpi = 64 / Dm.lpr;
