@@ -135,8 +135,8 @@ hipError_t scratch_address(void **out) {
 
 // ---------------------------------------------------------------------------
 // tiered expert residency: the state the caller holds in pinned host memory,
-// a header followed by int32 arrays (the LRU lists and key map, the landing
-// area of the selection and one flag per token); pointers into it are derived
+// a header followed by int32 arrays (the LRU lists and key map), then the
+// 8-byte landing area of one call's selection; pointers into it are derived
 // from its base on every call
 // ---------------------------------------------------------------------------
 constexpr uint64_t kTierMagic = 0x7265695465754d31ull;
@@ -147,7 +147,7 @@ struct TierState {
     int32_t n_layers, n_slots, max_tokens, pad;
     uint64_t expert_bytes;
     uint8_t *slots;      // device: n_slots packed experts
-    int32_t *route_dev;  // the landing area as the device addresses it (set by the first call)
+    uint64_t *route_dev;  // the landing area as the device addresses it (set by the first call)
     moe_tier_stats_t stats;
     int32_t head, tail;  // of the LRU list
 };
@@ -155,14 +155,14 @@ struct TierState {
 struct TierView {
     TierState *st;
     SlotLru lru;
-    int32_t *route;  // [max_tokens][K] host landing area of the selected experts
+    uint64_t *route;  // [max_tokens][K] host landing area of the selected experts (tag << 32 | expert)
 };
 
 constexpr size_t tier_header_bytes() { return (sizeof(TierState) + 255) / 256 * 256; }
 
 size_t tier_ints(const moe_dims_t *d, int32_t n_layers, int32_t n_slots, int32_t max_tokens) {
-    // the LRU, the selection of one call and one flag per token
-    return SlotLru::ints(n_slots, n_layers * d->n_experts) + (size_t)max_tokens * d->top_k + max_tokens;
+    // the LRU (padded to 8 bytes), then the selection of one call in 8-byte entries
+    return (SlotLru::ints(n_slots, n_layers * d->n_experts) + 1) / 2 * 2 + 2 * (size_t)max_tokens * d->top_k;
 }
 
 int check_tier_args(const moe_dims_t *dims, int32_t n_layers, int32_t n_slots, int32_t max_tokens) {
@@ -189,7 +189,7 @@ TierView tier_view(void *state) {
     v.lru.slot_of = ints + 3 * (size_t)ns;
     v.lru.head = v.st->head;
     v.lru.tail = v.st->tail;
-    v.route = ints + SlotLru::ints(ns, nk);
+    v.route = (uint64_t *)(ints + (SlotLru::ints(ns, nk) + 1) / 2 * 2);
     return v;
 }
 
@@ -416,33 +416,32 @@ int moe_tier_layer_forward(void *state, int32_t layer_index, const moe_layer_t *
     if (!st->route_dev) {
         void *p = nullptr;
         if (hipHostGetDevicePointer(&p, v.route, 0) != hipSuccess || !p) return MOE_ERR_INVALID_ARG;  // not pinned
-        st->route_dev = (int32_t *)p;
+        st->route_dev = (uint64_t *)p;
     }
-    // each token's block then raises its flag (after the state's selection
-    // area); flags are cleared before the launch and raised to an odd value
-    // that changes from call to call
+    // every entry carries a tag, odd and different from call to call, in its
+    // high half; the entries are cleared before the launch
     a.sel_host = st->route_dev;
-    a.flag_host = st->route_dev + n_tokens * K;
-    a.flag_value = (int32_t)(st->stats.calls + 1) * 2 + 1;
-    volatile int32_t *flags = (volatile int32_t *)(v.route + n_tokens * K);
-    for (int t = 0; t < n_tokens; ++t) flags[t] = 0;
+    a.sel_tag = (uint32_t)(st->stats.calls + 1) * 2u + 1u;
+    for (int i = 0; i < n; ++i) __atomic_store_n(&v.route[i], (uint64_t)0, __ATOMIC_RELAXED);
     if (hip_status(launch_forward_route(a, hs)) != MOE_OK) return MOE_ERR_HIP;
-    // 2. wait for it by polling the flags: the thread sees the selection as soon
-    // as it lands, where a stream synchronisation would add the runtime's
-    // completion signal and the thread's wake-up to every layer.  A flag that
-    // never rises (a failed launch) ends the spin after ~1e8 polls: the stream
-    // is then synchronised, which reports the error.
+    // 2. wait for it by polling the entries: the thread sees the selection as
+    // soon as it lands, where a stream synchronisation would add the runtime's
+    // completion signal and the thread's wake-up to every layer.  An entry is
+    // taken only once it holds this call's tag, whatever order the writes
+    // reach host memory in.  An entry that never lands (a failed launch) ends
+    // the spin after ~1e8 polls: the stream is then synchronised, which
+    // reports the error.
     {
         long spins = 0;
-        for (int t = 0; t < n_tokens; ++t) {
-            while (flags[t] != a.flag_value) {
+        for (int i = 0; i < n; ++i) {
+            while ((uint32_t)(__atomic_load_n(&v.route[i], __ATOMIC_ACQUIRE) >> 32) != a.sel_tag) {
                 if (++spins > 100000000L) {
                     if (hip_status(hipStreamSynchronize(hs)) != MOE_OK) return MOE_ERR_HIP;
-                    if (flags[t] != a.flag_value) return hip_status(hipErrorUnknown);
+                    if ((uint32_t)(__atomic_load_n(&v.route[i], __ATOMIC_ACQUIRE) >> 32) != a.sel_tag)
+                        return hip_status(hipErrorUnknown);
                 }
             }
         }
-        __atomic_thread_fence(__ATOMIC_ACQUIRE);
     }
     // 3. lookups in token order, then rank order; a miss takes a slot and is
     // listed for copying
@@ -454,7 +453,7 @@ int moe_tier_layer_forward(void *state, int32_t layer_index, const moe_layer_t *
     fa.dst = st->slots;
     fa.bytes = eb;
     for (int i = 0; i < n; ++i) {
-        const int32_t e = ((volatile const int32_t *)v.route)[i];
+        const int32_t e = (int32_t)(uint32_t)__atomic_load_n(&v.route[i], __ATOMIC_RELAXED);
         if (e < 0 || e >= E) return hip_status(hipErrorUnknown);  // cannot happen: routing selects valid experts
         bool hit;
         const int32_t slot = v.lru.acquire(layer_index * E + e, &hit);
@@ -491,7 +490,6 @@ int moe_tier_layer_forward(void *state, int32_t layer_index, const moe_layer_t *
     // 4. the expert kernels, reading the selected experts from their slots
     // (passed as kernel arguments)
     a.sel_host = nullptr;
-    a.flag_host = nullptr;
     a.experts = st->slots;
     if (hip_status(launch_forward_slots(a, sl, hs)) != MOE_OK) return MOE_ERR_HIP;
     st->stats.calls += 1;

@@ -619,21 +619,60 @@ __device__ __forceinline__ void load_row(const uint8_t *__restrict__ ex, const Q
 }
 
 // ---------------------------------------------------------------------------
-// fp32 dequantised dot product for byte-order codes (down projection)
+// down projection: codes against byte limbs of the activations
 // ---------------------------------------------------------------------------
+// Byte limbs of a fixed-point value |V| <= 2^22: V = L2 2^16 + L1 2^8 + L0,
+// L0 and L1 unsigned, L2 signed (in [-64, 64]).  Four values give one word per
+// limb, value b in byte b.
+__device__ __forceinline__ void byte_limbs(int v0, int v1, int v2, int v3, uint32_t &l0, uint32_t &l1,
+                                           uint32_t &l2) {
+    // v_perm_b32: byte k of the result is byte sel_k of {hi : lo} (lo = bytes 0-3)
+    const uint32_t t01 = __builtin_amdgcn_perm((uint32_t)v1, (uint32_t)v0, 0x05010400u);  // v0.0 v1.0 v0.1 v1.1
+    const uint32_t t23 = __builtin_amdgcn_perm((uint32_t)v3, (uint32_t)v2, 0x05010400u);
+    const uint32_t u01 = __builtin_amdgcn_perm((uint32_t)v1, (uint32_t)v0, 0x07030602u);  // v0.2 v1.2 v0.3 v1.3
+    const uint32_t u23 = __builtin_amdgcn_perm((uint32_t)v3, (uint32_t)v2, 0x07030602u);
+    l0 = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+    l1 = __builtin_amdgcn_perm(t23, t01, 0x07060302u);
+    l2 = __builtin_amdgcn_perm(u23, u01, 0x05040100u);
+}
+
+// 32-bit maximum over aligned groups of W lanes
+template <int W>
+__device__ __forceinline__ uint32_t lane_max_u32(uint32_t v) {
+    auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    if constexpr (W >= 2) v = mx(v, dpp_u<kDppXor1>(v));
+    if constexpr (W >= 4) v = mx(v, dpp_u<kDppXor2>(v));
+    if constexpr (W >= 8) v = mx(v, dpp_u<kDppHalfMirror>(v));
+    if constexpr (W >= 16) v = mx(v, dpp_u<kDppMirror>(v));
+    if constexpr (W >= 32) {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = mx(p[0], p[1]);
+    }
+    if constexpr (W >= 64) {
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = mx(p[0], p[1]);
+    }
+    return v;
+}
+
+// One row's dequantised dot product over the lane's slice of NV codes.  The
+// four codes 4n..4n+3 of a dword, masked into the bytes of a word, meet the
+// byte limbs of the same four activations in one v_dot4 per limb (u8 x u8 for
+// L0 and L1, i8 x i8 for L2; codes are below 16).  Per group of 64 codes the
+// integer sums give sum(q V) = 2^16 S2 + 2^8 S1 + S0 (S1 2^8 + S0 < 2^32),
+// sum(q a) = sum(q V) * lsc (the slice's 2^(e-22)), and the group folds as
+// s * sum(q a) + b * sum(a).
 template <int BITS, int CPL>
-__device__ __forceinline__ float qdot_f32(const uint4 (&c)[CPL], const uint32_t (&sb)[QSlice<BITS, CPL>::NGL],
-                                          const float (&av)[QSlice<BITS, CPL>::NV],
-                                          const float (&X)[QSlice<BITS, CPL>::NGL]) {
+__device__ __forceinline__ float qdot_limbs(const uint4 (&c)[CPL], const uint32_t (&sb)[QSlice<BITS, CPL>::NGL],
+                                            const uint32_t (&L)[3][QSlice<BITS, CPL>::NV / 4], float lsc,
+                                            const float (&X)[QSlice<BITS, CPL>::NGL]) {
     using Q = QSlice<BITS, CPL>;
-    constexpr int NS = 8 / BITS;  // code slots per byte
-    // one accumulator per slot: slot n holds q << (BITS n) once masked in place,
-    // and the power of two is removed once per group
-    float acc[Q::NGL][NS];
+    constexpr int NS = 8 / BITS;   // four-code groups per dword
+    constexpr int PG = Q::GL / 4;  // four-code groups per quantisation group
+    uint32_t s0[Q::NGL], s1[Q::NGL];
+    int s2[Q::NGL];
 #pragma unroll
-    for (int g = 0; g < Q::NGL; ++g)
-#pragma unroll
-        for (int n = 0; n < NS; ++n) acc[g][n] = 0.0f;
+    for (int g = 0; g < Q::NGL; ++g) s0[g] = s1[g] = 0u, s2[g] = 0;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const uint32_t d[4] = {c[j].x, c[j].y, c[j].z, c[j].w};
@@ -641,25 +680,19 @@ __device__ __forceinline__ float qdot_f32(const uint4 (&c)[CPL], const uint32_t 
         for (int w4 = 0; w4 < 4; ++w4) {
 #pragma unroll
             for (int n = 0; n < NS; ++n) {
-                uint32_t m = d[w4] & (Q::kByteMask << (BITS * n));
-                // opaque from here: byte b of m then converts with
-                // v_cvt_f32_ubyte{b} (seen through, each code would be
-                // narrowed to a bit-field extract plus a conversion)
-                asm("" : "+v"(m));
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int i = j * Q::C + w4 * Q::D + 4 * n + b;
-                    acc[i / Q::GL][n] = fmaf((float)((m >> (8 * b)) & 0xFFu), av[i], acc[i / Q::GL][n]);
-                }
+                const uint32_t q = (d[w4] >> (BITS * n)) & Q::kByteMask;
+                const int pc = (j * 4 + w4) * NS + n, g = pc / PG;
+                s0[g] = __builtin_amdgcn_udot4(q, L[0][pc], s0[g], false);
+                s1[g] = __builtin_amdgcn_udot4(q, L[1][pc], s1[g], false);
+                s2[g] = __builtin_amdgcn_sdot4((int)q, (int)L[2][pc], s2[g], false);
             }
         }
     }
     float total = 0.0f;
 #pragma unroll
     for (int g = 0; g < Q::NGL; ++g) {
-        float qa = acc[g][NS - 1];
-#pragma unroll
-        for (int n = NS - 2; n >= 0; --n) qa = fmaf(qa, 1.0f / (float)(1 << BITS), acc[g][n]);
+        const float lo = (float)((s1[g] << 8) + s0[g]);
+        const float qa = fmaf((float)s2[g], 65536.0f, lo) * lsc;
         total = fmaf(bf16_lo(sb[g]), qa, total);
         total = fmaf(bf16_hi(sb[g]), X[g], total);
     }

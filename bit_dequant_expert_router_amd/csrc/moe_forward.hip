@@ -570,16 +570,19 @@ __global__ __launch_bounds__(256) void k_gateup(const float *__restrict__ p_z, c
 
 // ---------------------------------------------------------------------------
 // k_down: RPW row-steps of the H output rows per wave, all K+1 experts in
-// batches of SB slots whose loads are all in flight together.  The SwiGLU
-// activations vary widely in magnitude, so this product stays in fp32:
-// codes are converted with v_cvt_f32_ubyte and folded per group as
-// s * sum(q a) + b * sum(a).
+// batches of SB slots whose loads are all in flight together.
 // ---------------------------------------------------------------------------
 // k_down processes the K+1 slots in batches of at most kDownBatch; a batch's
-// activations and their half-group sums are staged in LDS once per block.
-// Each lane reads the NV consecutive activations of its slice; a pad of 4
-// floats after every slice puts consecutive lanes on consecutive 16-byte bank
-// groups (unpadded, slices 128 or 256 bytes apart share their banks).
+// activations are staged in LDS once per block, in fixed point: the NV
+// consecutive activations that one lane multiplies with its codes (a lane
+// slice) share one exponent e (max |a| < 2^e, from the slice's 2 to 8 staging
+// threads), and a value is V = rint(a 2^(22-e)) in three byte limbs
+// (byte_limbs), with the slice's scale 2^(e-22) (NaN when the slice holds a
+// NaN or an inf) and the half-group sums of the activations beside them.  The
+// products then take one v_dot4 per limb and four codes (qdot_limbs) instead
+// of a conversion and an fma per code: they are what remains once the
+// weights land, on one SIMD for two waves.  A pad of 4 words after every
+// slice's limbs puts consecutive lanes on odd multiples of 16 bytes.
 constexpr int kDownBatch = 5;
 constexpr int kDownStageValues = 5120;  // activations staged per batch (batch * F <= this)
 
@@ -622,11 +625,13 @@ __global__ __launch_bounds__(256 * SPLIT) void k_down(const float *__restrict__ 
         xres[i] = p_x[(size_t)t * H + rs * rpi + rsub];
     }
 
-    constexpr int NVP = Q::NV + 4;  // padded slice
-    const int FP = F / Q::NV * NVP;  // padded activations of one slot
+    constexpr int NP = Q::NV / 4;   // four-value pieces per lane slice
+    constexpr int LS = 3 * NP + 4;  // words per staged slice: limbs L0, L1, L2, pad
+    const int nsl = F / Q::NV;      // slices per slot
     extern __shared__ __align__(16) unsigned char smem[];
-    float *s_act = (float *)smem;               // [batch][F / NV][NVP]
-    float *s_half = s_act + (size_t)batch * FP;  // [batch][F/32]
+    uint32_t *s_lmb = (uint32_t *)smem;                          // [batch][nsl][LS]
+    float *s_lsc = (float *)(s_lmb + (size_t)batch * nsl * LS);  // [batch][nsl]
+    float *s_half = s_lsc + (size_t)batch * nsl;                 // [batch][F/32]
 
     // lane s (s <= K) holds slot s: expert index (s < K) and combine
     // coefficient; only those lanes are ever read (unconditional loads, lanes
@@ -686,18 +691,36 @@ __global__ __launch_bounds__(256 * SPLIT) void k_down(const float *__restrict__ 
                 load_row<BITS, CPL>(ex, Dm, rs * rpi + rsub, lr, wc[u][i], wsb[u][i]);
             }
         }
-        // stage this batch's activations and half-group sums
+        // stage this batch's activations (limbs and slice scales) and
+        // half-group sums; a slice's NP pieces are NP consecutive threads
         if (b0 > 0) __syncthreads();  // the previous batch is done with the LDS
 #pragma unroll
         for (int r = 0; r < kStageMax; ++r) {
             const int v0 = threadIdx.x * 4 + 4 * NT * r;
-            if (4 * NT * r < batch * F) {  // uniform: whole 8-thread groups are live or not
+            if (4 * NT * r < batch * F) {  // uniform: whole slices are live or not
                 const bool live = v0 < nb * F;
                 const uint32_t si = sti[r], j = stj[r];
-                if (live) *(float4 *)(s_act + si * FP + j / Q::NV * NVP + j % Q::NV) = stv[r];
                 const float4 v = stv[r];
+                // the slice maximum of |a| as bits (NaN and inf above every finite value)
+                uint32_t mb = __float_as_uint(v.x) & 0x7FFFFFFFu;
+                mb = max(mb, __float_as_uint(v.y) & 0x7FFFFFFFu);
+                mb = max(mb, __float_as_uint(v.z) & 0x7FFFFFFFu);
+                mb = max(mb, __float_as_uint(v.w) & 0x7FFFFFFFu);
+                const float m = __uint_as_float(lane_max_u32<NP>(mb));
+                const float up = pow2f(kFixBits - limb_exponent(m));
+                uint32_t l0, l1, l2;
+                byte_limbs((int)rintf(v.x * up), (int)rintf(v.y * up), (int)rintf(v.z * up), (int)rintf(v.w * up),
+                           l0, l1, l2);
                 const float half = lane_sum<8>((v.x + v.y) + (v.z + v.w));  // 8 threads = 32 values
-                if (live && (threadIdx.x & 7) == 0) s_half[v0 / 32] = half;
+                if (live) {
+                    const uint32_t sl = si * nsl + j / Q::NV, pc = (j % Q::NV) / 4;
+                    uint32_t *d = s_lmb + sl * LS + pc;
+                    d[0] = l0;
+                    d[NP] = l1;
+                    d[2 * NP] = l2;
+                    if (pc == 0) s_lsc[sl] = limb_scale(m);
+                    if ((threadIdx.x & 7) == 0) s_half[v0 / 32] = half;
+                }
             }
         }
         __syncthreads();
@@ -708,12 +731,16 @@ __global__ __launch_bounds__(256 * SPLIT) void k_down(const float *__restrict__ 
                 if (si < nb) {
                     const int s = (b0 + si == 0) ? K : b0 + si - 1;
                     const float c = lane_bcast(my_c, s);
-                    float av[Q::NV];
+                    uint32_t L[3][NP];
+                    const uint32_t *src = s_lmb + (si * nsl + lr) * LS;
 #pragma unroll
-                    for (int i = 0; i < Q::NV / 4; ++i) {
-                        const float4 v = *(const float4 *)(s_act + si * FP + lr * NVP + 4 * i);
-                        av[4 * i] = v.x; av[4 * i + 1] = v.y; av[4 * i + 2] = v.z; av[4 * i + 3] = v.w;
-                    }
+                    for (int x = 0; x < 3; ++x)
+#pragma unroll
+                        for (int i = 0; i < NP / 4; ++i) {
+                            const uint4 w = *(const uint4 *)(src + x * NP + 4 * i);
+                            L[x][4 * i] = w.x; L[x][4 * i + 1] = w.y; L[x][4 * i + 2] = w.z; L[x][4 * i + 3] = w.w;
+                        }
+                    const float lsc = s_lsc[si * nsl + lr];
                     float X[Q::NGL];
 #pragma unroll
                     for (int g = 0; g < Q::NGL; ++g) {
@@ -724,7 +751,7 @@ __global__ __launch_bounds__(256 * SPLIT) void k_down(const float *__restrict__ 
                     }
 #pragma unroll
                     for (int i = 0; i < RPW; ++i)
-                        if (rs0 + i < nrs) acc[i] = fmaf(c, qdot_f32<BITS, CPL>(wc[u][i], wsb[u][i], av, X), acc[i]);
+                        if (rs0 + i < nrs) acc[i] = fmaf(c, qdot_limbs<BITS, CPL>(wc[u][i], wsb[u][i], L, lsc, X), acc[i]);
                 }
             }
         }
@@ -784,14 +811,12 @@ __global__ __launch_bounds__(64) void k_route(FwdArgs a) {
         a.ws.coef[t * (K + 1) + lane] = rt.w;
         if (a.route_idx) a.route_idx[t * K + lane] = rt.sel;
         if (a.route_w) a.route_w[t * K + lane] = rt.w;
-        if (a.sel_host) a.sel_host[t * K + lane] = rt.sel;
+        if (a.sel_host) a.sel_host[t * K + lane] = ((uint64_t)a.sel_tag << 32) | (uint32_t)rt.sel;
     }
     if (lane == 0) a.ws.coef[t * (K + 1) + K] = sigmoidf_(gs);
-    if (a.flag_host) {  // the selection first, then the flag, both pushed out to the host
-        __threadfence_system();
-        if (lane == 0) a.flag_host[t] = a.flag_value;
-        __threadfence_system();
-    }
+    // push the tagged entries out to host memory now (each entry validates
+    // itself, so no write has to land before another)
+    if (a.sel_host) __threadfence_system();
 }
 
 // k_fetch: whole experts from host memory into cache slots over the host
@@ -888,8 +913,9 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st, const SlotP
         const int nrs = H / rpi;
         const int blocks = (nrs + 4 * RD - 1) / (4 * RD);
         dim3 grid(blocks, T);
-        // padded activations (4 floats per lane slice) and half-group sums
-        const size_t per_slot = (size_t)(F + 4 * Dm.lpr) * 4 + (size_t)(F / 32) * 4;
+        // per slot: limb words (3 per 4 values, a 4-word pad per lane slice),
+        // slice scales and half-group sums
+        const size_t per_slot = (size_t)(3 * F / 4 + 5 * Dm.lpr + F / 32) * 4;
         int batch = kDownStageValues / F;
         if (batch > kDownBatch) batch = kDownBatch;
         if (batch > K + 1) batch = K + 1;

@@ -185,11 +185,12 @@ struct FwdArgs {
     float *route_w;
     Workspace ws;
     // k_route only: where the selection also goes (host memory mapped into the
-    // device's address space), or null; flag_host[t] is set to flag_value once
-    // token t's selection is visible there
-    int32_t *sel_host = nullptr;
-    int32_t *flag_host = nullptr;
-    int32_t flag_value = 0;
+    // device's address space), or null.  Entry t * K + k is one 8-byte word,
+    // sel_tag in the high half and the expert in the low half, so that the
+    // host can tell a landed entry from a stale one without relying on the
+    // order in which separate writes reach host memory.
+    uint64_t *sel_host = nullptr;
+    uint32_t sel_tag = 0;
 };
 
 // Slots of one call's selected experts, [T][K] with T*K <= kSlotArgs, passed

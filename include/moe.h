@@ -255,12 +255,12 @@ int moe_stack_forward(const moe_dims_t *dims, const moe_layer_t *layers, int32_t
  *
  * A call runs the per-token kernels only (n_tokens up to max_tokens):
  *   1. RMSNorm + router GEMV, then softmax/top-K/renormalise on the device,
- *      which also writes the selected indices into the state and raises a
- *      flag there per token;
- *   2. the calling thread WAITS for them, spinning on those flags (the one
- *      entry point that synchronises; a flag that does not rise within ~1e8
- *      polls, as after a failed launch, makes it synchronise `stream` and
- *      report the error);
+ *      which also writes the selected indices into the state, each as one
+ *      8-byte entry tagged with the call;
+ *   2. the calling thread WAITS for them, spinning until every entry holds
+ *      this call's tag (the one entry point that synchronises; an entry that
+ *      does not land within ~1e8 polls, as after a failed launch, makes it
+ *      synchronise `stream` and report the error);
  *   3. cache lookups in token order, then rank order; each miss takes the
  *      least recently used slot; one kernel then copies the missing experts
  *      into their slots, reading the host memory directly (a host store that

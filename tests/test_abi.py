@@ -298,10 +298,12 @@ def test_tier_sizes():
         assert moe.moe_tier_device_bytes(dims, ns, T) == ns * eb
     base = moe.moe_tier_state_bytes(dims, 1, 4, 1)
     assert base > 0
-    # int32 bookkeeping: 3 per slot, 1 per (layer, expert), 1 per assignment of one call, 1 per token
-    assert moe.moe_tier_state_bytes(dims, 1, 5, 1) - base == 12
+    # int32 bookkeeping (3 per slot, 1 per (layer, expert)) padded to 8 bytes, then one
+    # 8-byte tagged entry per assignment of one call
+    assert moe.moe_tier_state_bytes(dims, 1, 5, 1) - base == 16  # 12 + 512 ints, then 15 + 512 -> 528
+    assert moe.moe_tier_state_bytes(dims, 1, 6, 1) - base == 24
     assert moe.moe_tier_state_bytes(dims, 3, 4, 1) - base == 2 * 512 * 4
-    assert moe.moe_tier_state_bytes(dims, 1, 8, 2) - moe.moe_tier_state_bytes(dims, 1, 8, 1) == 5 * 4
+    assert moe.moe_tier_state_bytes(dims, 1, 8, 2) - moe.moe_tier_state_bytes(dims, 1, 8, 1) == dims.top_k * 8
     # at most 64 assignments per call (the slots travel as kernel arguments)
     assert moe.moe_tier_state_bytes(dims, 1, 64, 16) > 0
     assert moe.moe_tier_state_bytes(dims, 1, 68, 17) == 0
