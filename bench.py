@@ -53,19 +53,19 @@ METRIC = "MoE-layer decode tokens/s (effective expert-weight HBM GB/s and % of p
 # on.  FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0, the ratios of bytes
 # moved to counts reported for a 256 MiB copy.
 KERNEL_TRAFFIC = {
-    ("layer4", "k_gateup"): {"source_sha256_prefix": "a1b5e5e0c7cd121e", "fetch_kib": 11637.188, "write_kib": 20.125,
+    ("layer4", "k_gateup"): {"source_sha256_prefix": "a7c6f2e884d6bcb5", "fetch_kib": 11635.688, "write_kib": 40.125,
                              "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer4", "k_down"): {"source_sha256_prefix": "a1b5e5e0c7cd121e", "fetch_kib": 5908.688, "write_kib": 16.0,
+    ("layer4", "k_down"): {"source_sha256_prefix": "a7c6f2e884d6bcb5", "fetch_kib": 5911.0, "write_kib": 16.0,
                            "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer2", "k_gateup"): {"source_sha256_prefix": "a1b5e5e0c7cd121e", "fetch_kib": 6521.438, "write_kib": 20.125,
+    ("layer2", "k_gateup"): {"source_sha256_prefix": "a7c6f2e884d6bcb5", "fetch_kib": 6520.344, "write_kib": 20.125,
                              "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer2", "k_down"): {"source_sha256_prefix": "a1b5e5e0c7cd121e", "fetch_kib": 3348.0, "write_kib": 16.0,
+    ("layer2", "k_down"): {"source_sha256_prefix": "a7c6f2e884d6bcb5", "fetch_kib": 3349.5, "write_kib": 16.0,
                            "fetch_scale": 2.0, "write_scale": 1.0},
-    ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "4e71aef98f1e1d78", "fetch_kib": 570919.375,
-                                      "write_kib": 3619.953, "fetch_scale": 2.0, "write_scale": 1.0},
-    ("batch32", "k_grouped_down"): {"source_sha256_prefix": "4e71aef98f1e1d78", "fetch_kib": 287824.531,
-                                    "write_kib": 6141.469, "fetch_scale": 2.0, "write_scale": 1.0},
-    ("gdn", "k_gdn"): {"source_sha256_prefix": "ce208dae3eb6b410", "fetch_kib": 2350.0, "write_kib": 4128.0,
+    ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "2856d12fa671eb2c", "fetch_kib": 570923.719,
+                                      "write_kib": 3621.047, "fetch_scale": 2.0, "write_scale": 1.0},
+    ("batch32", "k_grouped_down"): {"source_sha256_prefix": "2856d12fa671eb2c", "fetch_kib": 287700.781,
+                                    "write_kib": 6141.422, "fetch_scale": 2.0, "write_scale": 1.0},
+    ("gdn", "k_gdn"): {"source_sha256_prefix": "6570258b0ce31403", "fetch_kib": 2350.0, "write_kib": 4128.0,
                        "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
