@@ -386,24 +386,40 @@ __device__ __forceinline__ void logit_keys(const float (&v)[EPL], int E, uint32_
 }
 
 // one round: the expert holding the wave's largest remaining key (wave-uniform,
-// clamped below E), whose key is then cleared; m receives that key
+// clamped below E), whose key is then cleared; m receives that key.  The
+// dependent chain is kept short: the lane's best key by a tree of 3-input
+// maxima, its first position (a bit mask of the equal keys, lowest bit) formed
+// while the DPP wave maximum runs, and only the winning entry rewritten.
+template <int EPL>
+__device__ __forceinline__ uint32_t lane_best_key(const uint32_t (&key)[EPL]) {
+    // groups of three (v_max3_u32), then the group maxima the same way
+    uint32_t t[(EPL + 2) / 3];
+#pragma unroll
+    for (int i = 0; i < (EPL + 2) / 3; ++i) {
+        uint32_t v = key[3 * i];
+        if (3 * i + 1 < EPL) v = max(v, key[3 * i + 1]);
+        if (3 * i + 2 < EPL) v = max(v, key[3 * i + 2]);
+        t[i] = v;
+    }
+    uint32_t b = t[0];
+#pragma unroll
+    for (int i = 1; i < (EPL + 2) / 3; ++i) b = max(b, t[i]);
+    return b;
+}
+
 template <int EPL>
 __device__ __forceinline__ int route_round(uint32_t (&key)[EPL], int E, uint32_t &m) {
     const int lane = threadIdx.x & 63;
-    uint32_t best = key[0];
-    int bq = 0;
+    const uint32_t best = lane_best_key<EPL>(key);
+    uint32_t pm = 0;
 #pragma unroll
-    for (int q = 1; q < EPL; ++q) {
-        const bool gt = key[q] > best;
-        best = gt ? key[q] : best;
-        bq = gt ? q : bq;
-    }
+    for (int q = 0; q < EPL; ++q) pm |= (key[q] == best) ? (1u << q) : 0u;
+    const int bq = __builtin_ctz(pm);  // best is one of the keys: pm != 0
     m = wave_max_u32(best);
     const int w = __ffsll((unsigned long long)__ballot(best == m)) - 1;
     const int qw = __builtin_amdgcn_readlane(bq, w);
-    const uint32_t clear = (lane == w) ? (1u << qw) : 0u;
 #pragma unroll
-    for (int q = 0; q < EPL; ++q) key[q] = ((clear >> q) & 1u) ? 0u : key[q];
+    for (int q = 0; q < EPL; ++q) key[q] = (q == qw && lane == w) ? 0u : key[q];
     const int e = w * EPL + qw;
     return e < E ? e : E - 1;
 }
