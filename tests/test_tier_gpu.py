@@ -3,8 +3,10 @@
 The experts live in pinned host memory; the device holds an LRU cache of
 n_slots expert slots.  Every output, routing index and routing weight must
 equal, bit for bit, those of moe_layer_forward's per-token kernels with every
-expert resident (so the oracle parity of that path carries over; the first
-token is also checked against the oracle directly).  The cache's lookups,
+expert resident (so the oracle parity of that path carries over).  Every layer
+of every call is also checked against the oracle directly: up to four tokens
+of the first call, and the first token of each later call, whose experts come
+from slots that were filled, hit or refilled by the calls before.  The cache's lookups,
 hits, misses and copied bytes, and the set of experts it holds at the end,
 must equal the LRU oracle's on the same access sequence.
 """
@@ -50,8 +52,7 @@ def _same(a, b):
                                                                        torch.nan_to_num(b, nan=7.0))
 
 
-def _run(moe, dims, n_layers, n_slots, max_tokens, calls, seed=0, oracle_first=False, nan_token=None,
-         pinned_store=True):
+def _run(moe, dims, n_layers, n_slots, max_tokens, calls, seed=0, nan_token=None, pinned_store=True):
     K, E = dims.top_k, dims.n_experts
     log(f"tier: {dims}, {n_layers} layers, {n_slots} slots, calls {calls}")
     lws, hosts = _layers(dims, n_layers, seed, pinned_store)
@@ -80,22 +81,22 @@ def _run(moe, dims, n_layers, n_slots, max_tokens, calls, seed=0, oracle_first=F
             ir = torch.full_like(it, -2)
             wt = torch.full((T, K), -1.0, dtype=torch.float32, device="cuda")
             wr = torch.full_like(wt, -2.0)
-            xin = xt.cpu().numpy() if oracle_first and c == 0 else None
+            xin = xt.cpu().numpy()
             moe.moe_tier_layer_forward(state, l, tier_layer, xt, yt, T, it, wt, ws)
             moe.moe_layer_forward(dims, lw.descriptor(), xr, yr, T, ir, wr, ws_ref)
             torch.cuda.synchronize()
             assert torch.equal(it, ir), (c, l)
             assert _same(wt, wr), (c, l)
             assert _same(yt, yr), (c, l)
-            if oracle_first and c == 0:
-                # up to four tokens of every layer of the first call against the
-                # oracle, fed the layer's input as the GPU saw it (teacher forcing)
-                yh, ih, wh = yt.cpu().numpy(), it.cpu().numpy(), wt.cpu().numpy()
-                for t in range(min(T, 4)):
-                    if not np.all(np.isfinite(xin[t])):
-                        continue
-                    ref = oracle_layer_generated(dims, seed, l, xin[t])
-                    check_token(yh[t], ih[t], wh[t], ref, K, f"tier layer {l} token {t}", unit_scale=l > 0)
+            # against the oracle, fed the layer's input as the GPU saw it
+            # (teacher forcing): up to four tokens of the first call, the first
+            # token of every later one
+            yh, ih, wh = yt.cpu().numpy(), it.cpu().numpy(), wt.cpu().numpy()
+            for t in range(min(T, 4) if c == 0 else 1):
+                if not np.all(np.isfinite(xin[t])):
+                    continue
+                ref = oracle_layer_generated(dims, seed, l, xin[t])
+                check_token(yh[t], ih[t], wh[t], ref, K, f"tier call {c} layer {l} token {t}", unit_scale=l > 0)
             accesses += layer_accesses(l, ir.cpu().numpy(), E)
             xt, xr = yt, yr
     hits, cache = lru_run(accesses, n_slots)
@@ -119,7 +120,7 @@ def _run(moe, dims, n_layers, n_slots, max_tokens, calls, seed=0, oracle_first=F
 
 def test_tiny_three_layers(moe):
     dims = syn.WORKLOADS["tiny"].dims  # 8 experts, top-2
-    st = _run(moe, dims, 3, 5, 2, [1, 2, 1, 1, 2, 2, 1, 2, 1, 1, 2, 1], oracle_first=True)
+    st = _run(moe, dims, 3, 5, 2, [1, 2, 1, 1, 2, 2, 1, 2, 1, 1, 2, 1])
     assert 0 < st.hits < st.lookups
 
 
@@ -145,7 +146,7 @@ def test_many_experts_and_four_tokens(moe):
 def test_full_size_layers(moe):
     # two 4096/1024 layers of 512 experts (7.1 GB of pinned host memory)
     dims = syn.WORKLOADS["layer4"].dims
-    _run(moe, dims, 2, 20, 4, [1, 4, 2, 1, 3, 1], oracle_first=True)
+    _run(moe, dims, 2, 20, 4, [1, 4, 2, 1, 3, 1])
 
 
 def test_sixty_four_assignments(moe):
