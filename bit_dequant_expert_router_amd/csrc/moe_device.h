@@ -19,8 +19,14 @@
 // products and their sums are exact.  The VALU does about one instruction
 // per weight against ~2.3 for convert-and-FMA.
 //
-// Down (activation a = SwiGLU output, widely spread magnitudes): fp32, codes
-// converted with v_cvt_f32_ubyte (byte code order) and folded per group.
+// Down (activation a = SwiGLU output, widely spread magnitudes): fixed point
+// per lane slice, not per group.  The single-token kernel (qdot_limbs) writes
+// the NV activations of a lane slice as V = rint(a 2^(22-e)) with one exponent
+// e for the slice, in three byte limbs; four codes masked into the bytes of a
+// word (byte code order) meet four values' limbs in one v_dot4 per limb.  The
+// grouped kernels take the activations in the six-limb form above (one
+// exponent per group, from k_encode_act), in the nibble order of the byte-order
+// codes, with v_dot8.
 #pragma once
 #include "moe_internal.h"
 

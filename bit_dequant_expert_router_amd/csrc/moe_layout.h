@@ -17,8 +17,8 @@
 //     (2-bit) is then eight 4-bit lanes holding consecutive codes, the operand
 //     form of v_dot8.
 //   byte order (down): code t in byte t % 4 at bits [bits*(t/4), +bits) of
-//     that byte.  One mask per bit slot leaves four codes in bytes, the operand
-//     form of v_cvt_f32_ubyte{0..3}.
+//     that byte.  One mask per bit slot leaves four consecutive codes in bytes,
+//     the operand form of v_dot4 against four values' byte limbs.
 //
 // Chunks are ordered for coalescing: a row of NC chunks is read by LPR =
 // min(NC, 64) lanes, each lane owning CPL = NC/LPR logically consecutive
