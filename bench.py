@@ -614,6 +614,23 @@ def bench_micro(args):
         g = graph_of(lambda: [three(i) for i in range(R)])
         rows["three_dependent_reads_4_24_12_MiB_us"] = round(time_replay(g) / R * 1e6, 3)
         del g
+        # the same with the layer's in-kernel dependencies: the second and
+        # third kernels first read a 2 KiB vector that the kernel before wrote
+        # (as the logits and the selection are), and only then their bytes
+        vec = torch.zeros(3, 2048, dtype=torch.uint8, device=dev)
+        nslot_d = (big - (64 << 10)) // tot
+
+        def three_dep(i):
+            off = (i % nslot_d) * tot
+            moe.moe_mb_dependent_read(buf[off:], sizes[0], 1024, 2, None, vec[0], sink)
+            off += sizes[0]
+            moe.moe_mb_dependent_read(buf[off:], sizes[1], 1024, 2, vec[0], vec[1], sink)
+            off += sizes[1]
+            moe.moe_mb_dependent_read(buf[off:], sizes[2], 1024, 2, vec[1], vec[2], sink)
+
+        g = graph_of(lambda: [three_dep(i) for i in range(R)])
+        rows["three_dependent_reads_with_vector_reads_us"] = round(time_replay(g) / R * 1e6, 3)
+        del g
         g = graph_of(lambda: [moe.moe_mb_stream_read(buf[(i % nslot) * tot:], tot, 1024, 2, sink) for i in range(R)])
         rows["one_read_40_MiB_us"] = round(time_replay(g) / R * 1e6, 3)
         del g
@@ -621,7 +638,8 @@ def bench_micro(args):
                       value=rows["empty_256_blocks_us"], unit="us per empty kernel", higher_is_better=False,
                       ms_per_step=None, dtype="none",
                       config={"workload": "gap: chains of empty kernels (1, 256, 1024 blocks) in one graph; "
-                                          "three dependent reads of 4 + 24 + 12 MiB against one 40 MiB read"},
+                                          "three dependent reads of 4 + 24 + 12 MiB, also with each read behind a "
+                                          "2 KiB vector the previous kernel wrote, against one 40 MiB read"},
                       **rows)
     else:  # exchange
         rows = []

@@ -85,6 +85,7 @@ _SIGS = {
     "moe_gdn_update": (ctypes.c_int, [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     # measurement kernels (include/moe_microbench.h)
     "moe_mb_stream_read": (ctypes.c_int, [_vp, _sz, _i32, _i32, _vp, _vp]),
+    "moe_mb_dependent_read": (ctypes.c_int, [_vp, _sz, _i32, _i32, _vp, _vp, _vp, _vp]),
     "moe_mb_empty": (ctypes.c_int, [_i32, _vp]),
     "moe_mb_exchange": (ctypes.c_int, [_i32, _i32, _i32, _vp, _sz, _vp]),
     "moe_mb_exchange_bytes": (_sz, [_i32, _i32]),
@@ -306,6 +307,12 @@ def moe_gdn_update(n_heads: int, d_k: int, d_v: int, n_tokens: int, state, q, k,
 def moe_mb_stream_read(src, nbytes: int, blocks: int, in_flight: int, sink, stream=None) -> int:
     return _check("moe_mb_stream_read", _lib.moe_mb_stream_read(_addr(src), int(nbytes), int(blocks),
                                                                 int(in_flight), _addr(sink), _stream(stream)))
+
+
+def moe_mb_dependent_read(src, nbytes: int, blocks: int, in_flight: int, dep, out, sink, stream=None) -> int:
+    return _check("moe_mb_dependent_read",
+                  _lib.moe_mb_dependent_read(_addr(src), int(nbytes), int(blocks), int(in_flight), _addr(dep),
+                                             _addr(out), _addr(sink), _stream(stream)))
 
 
 def moe_mb_empty(blocks: int, stream=None) -> int:

@@ -25,12 +25,26 @@ constexpr uint32_t kSinkMagic = 0x9E3779B9u;
 // streaming read: block b reads the b-th of `gridDim.x` contiguous ranges,
 // N 16-byte nontemporal loads per lane in flight before the first use
 // ---------------------------------------------------------------------------
-template <int N>
+// DEP: the layer kernels' dependency first.  Every lane loads 16 bytes of the
+// 2 KiB vector `dep` (written by the previous kernel, as the logits or the
+// selection are), and its loads of the range start `off` 16-byte units in,
+// off = (XOR of those words) & (kMbDepSlack - 1): no load of the range can
+// issue before `dep` has arrived.  OUT: at the end block b < 512 writes word b
+// of `out` (0 unless its data XOR to the magic constant).
+constexpr uint64_t kMbDepSlack = 4096;  // 16-byte units past `bytes` that src must hold
+template <int N, bool DEP, bool OUT>
 __global__ __launch_bounds__(kMbThreads) void k_mb_read(const u32x4_t *__restrict__ p, uint64_t n16,
-                                                        uint32_t *sink) {
+                                                        uint32_t *sink, const u32x4_t *__restrict__ dep,
+                                                        uint32_t *out) {
     const uint64_t per = (n16 + gridDim.x - 1) / gridDim.x;
-    const uint64_t begin = (uint64_t)blockIdx.x * per;
-    const uint64_t end = begin + per < n16 ? begin + per : n16;
+    uint64_t begin = (uint64_t)blockIdx.x * per;
+    uint64_t end = begin + per < n16 ? begin + per : n16;
+    if constexpr (DEP) {
+        const u32x4_t d = dep[threadIdx.x & 127];
+        const uint64_t off = (uint64_t)((d.x ^ d.y ^ d.z ^ d.w) & (uint32_t)(kMbDepSlack - 1));
+        begin += off;
+        end += off;
+    }
     uint32_t acc = 0;
     for (uint64_t i = begin + threadIdx.x; i < end; i += (uint64_t)kMbThreads * N) {
         u32x4_t v[N];
@@ -43,6 +57,9 @@ __global__ __launch_bounds__(kMbThreads) void k_mb_read(const u32x4_t *__restric
         for (int u = 0; u < N; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     if (acc == kSinkMagic) sink[threadIdx.x & 3] = acc;
+    if constexpr (OUT) {
+        if (threadIdx.x == 0 && blockIdx.x < 512) out[blockIdx.x] = acc == kSinkMagic ? 1u : 0u;
+    }
 }
 
 __global__ __launch_bounds__(kMbThreads) void k_mb_empty(uint32_t *p) {
@@ -216,13 +233,38 @@ int moe_mb_stream_read(const void *src, size_t bytes, int32_t blocks, int32_t in
     const u32x4_t *p = (const u32x4_t *)src;
     const uint64_t n16 = bytes / 16;
     (void)hipGetLastError();
+    uint32_t *sk = (uint32_t *)sink;
     switch (in_flight) {
-        case 1: hipLaunchKernelGGL(k_mb_read<1>, dim3(blocks), dim3(kMbThreads), 0, st, p, n16, (uint32_t *)sink); break;
-        case 2: hipLaunchKernelGGL(k_mb_read<2>, dim3(blocks), dim3(kMbThreads), 0, st, p, n16, (uint32_t *)sink); break;
-        case 4: hipLaunchKernelGGL(k_mb_read<4>, dim3(blocks), dim3(kMbThreads), 0, st, p, n16, (uint32_t *)sink); break;
-        case 8: hipLaunchKernelGGL(k_mb_read<8>, dim3(blocks), dim3(kMbThreads), 0, st, p, n16, (uint32_t *)sink); break;
+        case 1: hipLaunchKernelGGL((k_mb_read<1, false, false>), dim3(blocks), dim3(kMbThreads), 0, st, p, n16, sk, nullptr, nullptr); break;
+        case 2: hipLaunchKernelGGL((k_mb_read<2, false, false>), dim3(blocks), dim3(kMbThreads), 0, st, p, n16, sk, nullptr, nullptr); break;
+        case 4: hipLaunchKernelGGL((k_mb_read<4, false, false>), dim3(blocks), dim3(kMbThreads), 0, st, p, n16, sk, nullptr, nullptr); break;
+        case 8: hipLaunchKernelGGL((k_mb_read<8, false, false>), dim3(blocks), dim3(kMbThreads), 0, st, p, n16, sk, nullptr, nullptr); break;
         default: return MOE_ERR_INVALID_ARG;
     }
+    return hip_rc(hipGetLastError());
+}
+
+int moe_mb_dependent_read(const void *src, size_t bytes, int32_t blocks, int32_t in_flight, const void *dep,
+                          void *out, void *sink, void *stream) {
+    if (!src || !out || !sink || bytes < 16 || bytes % 16 != 0) return MOE_ERR_INVALID_ARG;
+    if (blocks < 1 || blocks > 65536) return MOE_ERR_INVALID_ARG;
+    if (!aligned(src, 16) || !aligned(dep, 16) || !aligned(out, 16) || !aligned(sink, 16)) return MOE_ERR_ALIGNMENT;
+    const hipStream_t st = (hipStream_t)stream;
+    const u32x4_t *p = (const u32x4_t *)src, *d = (const u32x4_t *)dep;
+    uint32_t *sk = (uint32_t *)sink, *o = (uint32_t *)out;
+    const uint64_t n16 = bytes / 16;
+    (void)hipGetLastError();
+#define MB_DEP(N)                                                                                         \
+    if (d) hipLaunchKernelGGL((k_mb_read<N, true, true>), dim3(blocks), dim3(kMbThreads), 0, st, p, n16, sk, d, o); \
+    else hipLaunchKernelGGL((k_mb_read<N, false, true>), dim3(blocks), dim3(kMbThreads), 0, st, p, n16, sk, d, o)
+    switch (in_flight) {
+        case 1: MB_DEP(1); break;
+        case 2: MB_DEP(2); break;
+        case 4: MB_DEP(4); break;
+        case 8: MB_DEP(8); break;
+        default: return MOE_ERR_INVALID_ARG;
+    }
+#undef MB_DEP
     return hip_rc(hipGetLastError());
 }
 

@@ -41,6 +41,21 @@ extern "C" {
 int moe_mb_stream_read(const void *src, size_t bytes, int32_t blocks, int32_t in_flight, void *sink,
                        void *stream);
 
+/*
+ * As moe_mb_stream_read, with the dependency the layer's second and third
+ * kernels have on the one before (the logits, then the selection): every lane
+ * first loads 16 bytes of `dep` (2 KiB of device memory, 16-byte aligned,
+ * typically the `out` of the previous call), and the block's loads start
+ * off = (XOR of those words) & 4095 16-byte units into its range, so that no
+ * load of the range issues before `dep` has arrived.  `src` must therefore
+ * hold bytes + 64 KiB; a zero `dep` gives off = 0; a NULL `dep` means no
+ * dependency (as the router's first loads have none).  At the end, block
+ * b < 512 writes word b of `out` (2 KiB, 16-byte aligned): 0, unless its data
+ * XOR to the sink's magic constant.  The rest as moe_mb_stream_read.
+ */
+int moe_mb_dependent_read(const void *src, size_t bytes, int32_t blocks, int32_t in_flight, const void *dep,
+                          void *out, void *sink, void *stream);
+
 /* An empty kernel of `blocks` (1 .. 65536) blocks of 256 threads. */
 int moe_mb_empty(int32_t blocks, void *stream);
 

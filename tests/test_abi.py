@@ -183,6 +183,11 @@ def test_microbench_rejects():
     assert moe._lib.moe_mb_stream_read(A, 1024, 4, 3, A, None) == moe.MOE_ERR_INVALID_ARG
     assert moe._lib.moe_mb_stream_read(A, 1024, 0, 2, A, None) == moe.MOE_ERR_INVALID_ARG
     assert moe._lib.moe_mb_stream_read(A + 8, 1024, 4, 2, A, None) == moe.MOE_ERR_ALIGNMENT
+    g = moe._lib.moe_mb_dependent_read
+    assert g(None, 1024, 4, 2, A, A, A, None) == moe.MOE_ERR_INVALID_ARG
+    assert g(A, 1024, 4, 2, A, None, A, None) == moe.MOE_ERR_INVALID_ARG  # no output vector
+    assert g(A, 1024, 4, 8, A, A + 8, A, None) == moe.MOE_ERR_ALIGNMENT
+    assert g(A, 1024, 4, 3, A, A, A, None) == moe.MOE_ERR_INVALID_ARG
     assert moe._lib.moe_mb_empty(0, None) == moe.MOE_ERR_INVALID_ARG
     assert moe.moe_mb_exchange_bytes(256, 8) > 256 * 8
     assert moe.moe_mb_exchange_bytes(256, 7) == 0  # blocks not a multiple of groups
