@@ -632,12 +632,16 @@ template <int BITS, int CPL>
 __device__ __forceinline__ void load_row(const uint8_t *__restrict__ ex, const QMat &q, int r, int lr,
                                          uint4 (&c)[CPL], uint32_t (&sb)[QSlice<BITS, CPL>::NGL]) {
     using Q = QSlice<BITS, CPL>;
-    const uint8_t *row = ex + q.codes_off + (size_t)r * q.row_bytes;
+    // 32-bit offsets from the expert's base (an expert is far below 4 GiB): with
+    // a wave-uniform base the loads take the scalar-base form, one 32-bit
+    // offset per lane instead of a 64-bit address
+    const uint32_t row = (uint32_t)q.codes_off + (uint32_t)r * (uint32_t)q.row_bytes;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) c[j] = ld_stream16(row + 16 * (lr + q.lpr * j));
-    const uint32_t *sbr = (const uint32_t *)(ex + q.sb_off) + (size_t)r * q.ngroups + (lr * Q::NV) / kGroup;
+    for (int j = 0; j < CPL; ++j) c[j] = ld_stream16(ex + (row + 16u * (uint32_t)(lr + q.lpr * j)));
+    const uint32_t sbr =
+        (uint32_t)q.sb_off + 4u * ((uint32_t)r * (uint32_t)q.ngroups + (uint32_t)((lr * Q::NV) / kGroup));
 #pragma unroll
-    for (int g = 0; g < Q::NGL; ++g) sb[g] = ld_stream4(sbr + g);
+    for (int g = 0; g < Q::NGL; ++g) sb[g] = ld_stream4((const uint32_t *)(ex + (sbr + 4u * g)));
 }
 
 // ---------------------------------------------------------------------------

@@ -482,7 +482,7 @@ __global__ __launch_bounds__(256) void k_gateup(const float *__restrict__ p_z, c
     };
     if (late) {  // block-uniform
         stage();
-        ex = a.experts + (size_t)s_ex * a.L.bytes;
+        ex = a.experts + (size_t)__builtin_amdgcn_readfirstlane(s_ex) * a.L.bytes;
     }
 
     // 3. weight loads, all unconditional (row-steps past the end re-read the
@@ -612,7 +612,10 @@ __global__ __launch_bounds__(256 * SPLIT) void k_down(const float *__restrict__ 
     constexpr int kPer = (kDownBatch + SPLIT - 1) / SPLIT;          // slot positions per wave group
     const int t = blockIdx.y;
     const int E = a.s.E;
-    const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3, grp = threadIdx.x >> 8;
+    // wave and group are wave-uniform (so are the slots and experts they select:
+    // the weight loads then take the scalar-base form)
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3),
+              grp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
     const QMat &Dm = a.L.m[2];
     const int lpr = LPR ? LPR : Dm.lpr, rpi = 64 / lpr;
     const int lr = lane % lpr, rsub = lane / lpr;
