@@ -336,24 +336,6 @@ __device__ __forceinline__ RouteSel route_select(int K, const uint64_t *s_cand) 
     return r;
 }
 
-// the expert selected for slot s (wave-uniform, s < K)
-__device__ __forceinline__ int routed_expert(const RouteSel &r, int s) {
-    const uint64_t b = __ballot(r.rank == s);
-    return __builtin_amdgcn_readlane(r.sel, __ffsll((unsigned long long)b) - 1);
-}
-
-// the logits of one token a block's wave routes: e = 256 q + 64 w + lane
-// (clamped index: all loads in flight at once)
-template <int EPW>
-__device__ __forceinline__ void load_logits_quarter(const float *__restrict__ z, int E, float (&zq)[EPW]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int q = 0; q < EPW; ++q) {
-        const int e = 256 * q + 64 * wave + lane;
-        zq[q] = z[e < E ? e : E - 1];
-    }
-}
-
 // ---------------------------------------------------------------------------
 // routing by one wave over all E logits of a token (E <= 64 EPL), without LDS
 // or barriers.  Lane l holds the keys of experts EPL l .. EPL l + EPL - 1 (the
