@@ -53,19 +53,19 @@ METRIC = "MoE-layer decode tokens/s (effective expert-weight HBM GB/s and % of p
 # on.  FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0, the ratios of bytes
 # moved to counts reported for a 256 MiB copy.
 KERNEL_TRAFFIC = {
-    ("layer4", "k_gateup"): {"source_sha256_prefix": "97235959c093b253", "fetch_kib": 11636.188, "write_kib": 40.125,
+    ("layer4", "k_gateup"): {"source_sha256_prefix": "a7f3856396f84859", "fetch_kib": 11636.125, "write_kib": 40.125,
                              "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer4", "k_down"): {"source_sha256_prefix": "97235959c093b253", "fetch_kib": 5908.5, "write_kib": 16.0,
+    ("layer4", "k_down"): {"source_sha256_prefix": "a7f3856396f84859", "fetch_kib": 5908.5, "write_kib": 16.0,
                            "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer2", "k_gateup"): {"source_sha256_prefix": "97235959c093b253", "fetch_kib": 6521.031, "write_kib": 20.125,
+    ("layer2", "k_gateup"): {"source_sha256_prefix": "a7f3856396f84859", "fetch_kib": 6521.0, "write_kib": 20.125,
                              "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer2", "k_down"): {"source_sha256_prefix": "97235959c093b253", "fetch_kib": 3347.0, "write_kib": 16.0,
+    ("layer2", "k_down"): {"source_sha256_prefix": "a7f3856396f84859", "fetch_kib": 3347.0, "write_kib": 16.0,
                            "fetch_scale": 2.0, "write_scale": 1.0},
-    ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "0d1a6dea6518bc86", "fetch_kib": 570353.281,
-                                      "write_kib": 3623.375, "fetch_scale": 2.0, "write_scale": 1.0},
-    ("batch32", "k_grouped_down"): {"source_sha256_prefix": "0d1a6dea6518bc86", "fetch_kib": 287792.656,
-                                    "write_kib": 6141.594, "fetch_scale": 2.0, "write_scale": 1.0},
-    ("gdn", "k_gdn"): {"source_sha256_prefix": "1f26e16781829098", "fetch_kib": 2350.0, "write_kib": 4128.0,
+    ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "564545cf2eca3ad0", "fetch_kib": 570311.469,
+                                      "write_kib": 3621.875, "fetch_scale": 2.0, "write_scale": 1.0},
+    ("batch32", "k_grouped_down"): {"source_sha256_prefix": "564545cf2eca3ad0", "fetch_kib": 287767.75,
+                                    "write_kib": 6141.469, "fetch_scale": 2.0, "write_scale": 1.0},
+    ("gdn", "k_gdn"): {"source_sha256_prefix": "6242c5a17ee646a0", "fetch_kib": 2350.0, "write_kib": 4128.0,
                        "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
