@@ -412,15 +412,18 @@ def bench_layer(args, wl):
 
 def call_latency_p50(moe, dims, descs, pool, out, ridx, rw, ws, wsb, T, R, P, n=1000, warm=50):
     """Median microseconds of one moe_layer_forward call: an event pair around
-    each of n calls (after warm calls), issued one at a time."""
+    each of n calls (after warm calls), issued one at a time.  The calls' arguments
+    are marshalled before the loop (layer_forward_call), so that the figure is the
+    C ABI call's, as a C caller sees it, and not Python's tensor indexing."""
     import numpy as np
     import torch
+    calls = [moe.layer_forward_call(dims, descs[i % R], pool[i % P], out[i % P], T, ridx[i % P], rw[i % P], ws, wsb)
+             for i in range(warm + n)]
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     for i in range(warm + n):
-        j = i % P
         if i >= warm:
             ev[i - warm][0].record()
-        moe.moe_layer_forward(dims, descs[i % R], pool[j], out[j], T, ridx[j], rw[j], ws, wsb)
+        calls[i]()
         if i >= warm:
             ev[i - warm][1].record()
     torch.cuda.synchronize()

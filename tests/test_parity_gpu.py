@@ -110,6 +110,29 @@ def test_inplace_determinism_and_optional_outputs(moe, n_tokens):
         check_token(a[t], ia[t], wa[t], oracle_layer_canonical(dims, x[t], dense, experts), dims.top_k, f"token {t}")
 
 
+def test_marshalled_call_equals_binding_call(moe):
+    """layer_forward_call (arguments marshalled once, for repeated calls) gives
+    the moe_layer_forward result bit for bit, on every repeat."""
+    import torch
+    dims = syn.WORKLOADS["tiny"].dims
+    _, _, lw = _canonical_layer(dims)
+    x = syn.tokens(2, 1, dims.hidden)
+    ref, iref, wref = run_layer(dims, lw, x)
+    xt = torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+    yt = torch.empty_like(xt)
+    ridx = torch.empty((1, dims.top_k), dtype=torch.int32, device="cuda")
+    rw = torch.empty((1, dims.top_k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_workspace_bytes(dims, 1), dtype=torch.uint8, device="cuda")
+    moe.moe_workspace_init(ws)
+    call = moe.layer_forward_call(dims, lw.descriptor(), xt, yt, 1, ridx, rw, ws)
+    for _ in range(3):
+        yt.fill_(float("nan"))
+        call()
+        torch.cuda.synchronize()
+        assert np.array_equal(yt.cpu().numpy(), ref)
+        assert np.array_equal(ridx.cpu().numpy(), iref) and np.array_equal(rw.cpu().numpy(), wref)
+
+
 @pytest.mark.parametrize("name,T", [("tiny", 3), ("tiny", 50), ("layer4", 1), ("layer4", 6)])
 def test_stages_equal_full_forward(moe, name, T):
     """The stages enqueued one by one give exactly the one-call result, on the
