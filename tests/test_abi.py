@@ -234,8 +234,8 @@ def test_stage_count():
     dims = d()
     K = dims.top_k
     assert moe.moe_forward_stage_count(dims, 1) == 3
-    assert moe.moe_forward_stage_count(dims, 24) == 3  # 96 assignments: per-token kernels
-    assert moe.moe_forward_stage_count(dims, 25) == 7  # 100: grouped by expert
+    assert moe.moe_forward_stage_count(dims, 17) == 3  # 68 assignments: per-token kernels
+    assert moe.moe_forward_stage_count(dims, 18) == 7  # 72: grouped by expert
     assert moe.moe_forward_stage_count(dims, 4096 // K) == 7
     assert moe.moe_forward_stage_count(dims, 4096 // K + 1) == 3
     f = moe._lib.moe_forward_stage_count

@@ -53,7 +53,7 @@ def test_tiny_layer(moe):
         np.testing.assert_allclose(o1[0], out[t], rtol=1e-5, atol=1e-4)
 
 
-GROUPED_MIN_ASSIGN = 100  # tokens x top-K from which a batch is grouped by expert (include/moe.h)
+GROUPED_MIN_ASSIGN = 72  # tokens x top-K from which a batch is grouped by expert (include/moe.h)
 
 SMALL_SHAPES = [
     # hidden, ffn, experts, top_k, bits
