@@ -595,21 +595,26 @@ constexpr int kDownStageValues = 5120;  // activations staged per batch (batch *
 // 0: one reduction per row
 // ONE: all K+1 slots in a single batch (straight-line code: no loop-header
 // wait holds back the first loads)
-// SPLIT: wave groups per block (1 or 2).  Group g of 4 waves takes the slot
-// positions g, g + SPLIT, ... of every batch for the block's rows, so that a
-// SIMD runs SPLIT waves (one alone exposes its LDS and VALU latencies: the
-// products are VALU-bound once the weights land).  The groups' row sums are
-// added in group order through LDS before the one write per row.
+// SPLIT: wave groups per block (1 or 2), so that a SIMD runs SPLIT waves (one
+// alone exposes its LDS and VALU latencies: the products are VALU-bound once
+// the weights land).
+// ROWS: group g takes the g-th 4 RPW row-steps of the block and every wave
+// every slot position; else group g takes the slot positions g, g + SPLIT, ...
+// of every batch for all the block's rows, and the groups' row sums are added
+// in group order through LDS before the one write per row.  With the K + 1 = 5
+// slot positions of top-4, the slot split leaves 3 products per row on one
+// group and 2 on the other, and the group with 3 sets the block's end; the row
+// split gives every wave the same work and needs no exchange.
 // TIER: the selected experts sit in cache slots, sl.s[t * K + rank] (a.experts
 // = the slots' base)
-template <int BITS, int CPL, int RPW, int LPR, bool ONE, bool TIER, int SPLIT>
+template <int BITS, int CPL, int RPW, int LPR, bool ONE, bool TIER, int SPLIT, bool ROWS = false>
 __global__ __launch_bounds__(256 * SPLIT) void k_down(const float *__restrict__ p_x, const int32_t *__restrict__ p_sel,
                                                      const float *__restrict__ p_coef, const float *__restrict__ p_act,
                                                      int H, int F, int K, int batch, uint32_t f4_recip, FwdArgs a,
                                                      SlotParam<TIER> sl) {
     using Q = QSlice<BITS, CPL>;
     constexpr int NT = 256 * SPLIT;                                  // threads per block
-    constexpr int kPer = (kDownBatch + SPLIT - 1) / SPLIT;          // slot positions per wave group
+    constexpr int kPer = ROWS ? kDownBatch : (kDownBatch + SPLIT - 1) / SPLIT;  // slot positions per wave
     const int t = blockIdx.y;
     const int E = a.s.E;
     // wave and group are wave-uniform (so are the slots and experts they select:
@@ -620,7 +625,7 @@ __global__ __launch_bounds__(256 * SPLIT) void k_down(const float *__restrict__ 
     const int lpr = LPR ? LPR : Dm.lpr, rpi = 64 / lpr;
     const int lr = lane % lpr, rsub = lane / lpr;
     const int nrs = H / rpi;
-    const int rs0 = (blockIdx.x * 4 + wave) * RPW;
+    const int rs0 = (ROWS ? blockIdx.x * 4 * SPLIT + grp * 4 + wave : blockIdx.x * 4 + wave) * RPW;
     const bool active = rs0 < nrs;
     const int k0 = lr * Q::NV;
     const uint32_t F4 = F / 4;
@@ -683,7 +688,7 @@ __global__ __launch_bounds__(256 * SPLIT) void k_down(const float *__restrict__ 
         uint32_t wsb[kPer][RPW][Q::NGL];
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
-            const int si = grp + SPLIT * u;
+            const int si = ROWS ? u : grp + SPLIT * u;
             const int sc = si < nb ? si : nb - 1;
             const int s = (b0 + sc == 0) ? K : b0 + sc - 1;
             const uint8_t *ex;
@@ -735,7 +740,7 @@ __global__ __launch_bounds__(256 * SPLIT) void k_down(const float *__restrict__ 
         if (active) {
 #pragma unroll
             for (int u = 0; u < kPer; ++u) {
-                const int si = grp + SPLIT * u;
+                const int si = ROWS ? u : grp + SPLIT * u;
                 if (si < nb) {
                     const int s = (b0 + si == 0) ? K : b0 + si - 1;
                     const float c = lane_bcast(my_c, s);
@@ -774,7 +779,7 @@ __global__ __launch_bounds__(256 * SPLIT) void k_down(const float *__restrict__ 
         float v = multi_reduce<RPW, LPR>(acc);
         const int i = multi_index<RPW, LPR>(lane);
         constexpr int DL = LPR / RPW;  // lanes sharing one reduced row
-        if constexpr (SPLIT > 1) {
+        if constexpr (SPLIT > 1 && !ROWS) {
             __shared__ float s_part[SPLIT - 1][4][64];
             if (grp > 0) s_part[grp - 1][wave][lane] = v;
             __syncthreads();
@@ -788,7 +793,7 @@ __global__ __launch_bounds__(256 * SPLIT) void k_down(const float *__restrict__ 
         for (int q = 1; q < RPW; ++q) xr = (i == q) ? xres[q] : xr;
         if ((lane & (DL - 1)) == 0 && rs0 + i < nrs) a.y[(size_t)t * H + (rs0 + i) * rpi + rsub] = xr + v;
     } else {
-        static_assert(SPLIT == 1, "split slots need the one-butterfly reduction");
+        static_assert(SPLIT == 1 || ROWS, "split slots need the one-butterfly reduction");
         if (!active) return;
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
@@ -853,7 +858,11 @@ constexpr int kRpwDown2 = 1;  // 2-bit codes
 template <int BITS, bool TIER>
 hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st, const SlotParam<TIER> &sl = {}) {
     const int H = a.s.H, F = a.s.F, E = a.s.E, K = a.s.K, T = a.T;
-    constexpr int RD = BITS == 4 ? kRpwDown4 : kRpwDown2;  // down row-steps per wave
+    constexpr int RD = BITS == 4 ? kRpwDown4 : kRpwDown2;  // down row-steps per wave group
+    // two wave groups per block split its rows when the row-steps halve
+    // (4-bit k_down 4.97 -> 4.58 us), else its slot positions
+    constexpr bool DR = RD % 2 == 0;
+    constexpr int RDS = DR ? RD / 2 : RD;  // row-steps per wave with two groups
     if (stage == 0 && (H == 2048 || H == 4096)) {  // RMSNorm + router + limbs of h, H split over 4 waves
         const int rows = (E + 1 + kRouterSplitRows - 1) / kRouterSplitRows;
         const int blocks = rows > H / 256 ? rows : H / 256;
@@ -936,7 +945,7 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st, const SlotP
         const bool split = one && K + 1 >= 2;
         const dim3 b1(256), b2(512);
         if (Dm.cpl == 2) {
-            if (split) hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, true, TIER, 2>), grid, b2, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl);
+            if (split) hipLaunchKernelGGL((k_down<BITS, 2, RDS, 64, true, TIER, 2, DR>), grid, b2, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl);
             else if (one) hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, true, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl);
             else hipLaunchKernelGGL((k_down<BITS, 2, RD, 64, false, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl);
         } else if (Dm.cpl == 1) {
@@ -944,13 +953,13 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st, const SlotP
             switch (key) {
                 case 0: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, false, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
                 case 1: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, true, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
-                case 2: hipLaunchKernelGGL((k_down<BITS, 1, RD, 64, true, TIER, 2>), grid, b2, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
+                case 2: hipLaunchKernelGGL((k_down<BITS, 1, RDS, 64, true, TIER, 2, DR>), grid, b2, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
                 case 3: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, false, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
                 case 4: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, true, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
-                case 5: hipLaunchKernelGGL((k_down<BITS, 1, RD, 32, true, TIER, 2>), grid, b2, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
+                case 5: hipLaunchKernelGGL((k_down<BITS, 1, RDS, 32, true, TIER, 2, DR>), grid, b2, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
                 case 6: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, false, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
                 case 7: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, true, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
-                case 8: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, true, TIER, 2>), grid, b2, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
+                case 8: hipLaunchKernelGGL((k_down<BITS, 1, RDS, 16, true, TIER, 2, DR>), grid, b2, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
                 case 9: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, false, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
                 default: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, true, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
             }
