@@ -130,10 +130,14 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router(FwdArgs a) {
 // H and E come as leading scalar parameters, which the hardware preloads into
 // SGPRs (the library is built with kernel-argument preloading), so the first
 // loads wait for no read of the argument segment: 0.25 us less per layer.
-// k_gateup and k_down take the pointers of their own first loads the same way
-// (the expert layout and pointers, needed once those are issued, stay in
-// FwdArgs: deriving them on the device costs more scalar instructions per
-// wave than the argument read).  The 4 waves of a block split H into
+// k_gateup and k_down take the pointers of their own first loads the same way.
+// k_gateup also takes the shared expert's pointer and F, and derives the gate
+// and up matrices' layout from H and F with a few shifts, so that the shared
+// expert's weight loads wait for no argument read either (2-bit layer 13.35 ->
+// 12.78 us, 4-bit 15.05 -> 14.86 us); the rest of the layout and the other
+// pointers, needed once those loads are out, stay in FwdArgs (deriving all of
+// them on the device costs more scalar instructions per wave than the
+// argument read).  The 4 waves of a block split H into
 // quarters of the block's RB router rows (one row per block measures fastest:
 // 513 blocks spread the 4 MiB over the whole chip), so a wave reads 1/4 of x
 // and gamma instead of all of it.  The dot products use x * gamma; the factor
@@ -381,9 +385,32 @@ __global__ __launch_bounds__(256) void k_router_tokens(FwdArgs a) {
 // routes and hands the expert to the other waves through LDS at the block's
 // barrier, which then also orders the staging; the other waves' routing
 // instructions are saved (the products are VALU-bound once the weights land).
+// With BR every block holds one slot, so the shared expert's blocks find their
+// rows from blockIdx and the preloaded F alone and issue their weight loads
+// before the argument segment arrives.
 // Block 0's wave 0 finally takes all K rounds and writes the selection, the
 // renormalised weights and sigmoid(g_s).
 // ---------------------------------------------------------------------------
+// the gate (m = 0) or up (m = 1) matrix of make_layout(H, F, BITS), for H and
+// F powers of two: shifts and adds only
+template <int BITS>
+__device__ __forceinline__ QMat gate_up_qmat(int H, int F, int m) {
+    QMat q;
+    q.rows = F;
+    q.cols = H;
+    q.bits = BITS;
+    q.order = kOrderNibble;
+    q.row_bytes = H * BITS / 8;
+    q.ngroups = H / kGroup;
+    q.nchunks = H / codes_per_chunk(BITS);
+    q.lpr = q.nchunks < 64 ? q.nchunks : 64;
+    q.cpl = q.nchunks >> __builtin_ctz((unsigned)q.lpr);
+    const size_t mat = (size_t)F * q.row_bytes;  // one matrix's codes
+    q.codes_off = (size_t)m * mat;
+    q.sb_off = 3 * mat + (size_t)m * F * q.ngroups * 4;
+    return q;
+}
+
 // LPR: lanes per row when the step's partial sums are reduced together (64);
 // 0: one reduction per row
 // TIER: the selected experts' routing is already done (k_route) and their
@@ -391,10 +418,11 @@ __global__ __launch_bounds__(256) void k_router_tokens(FwdArgs a) {
 template <int BITS, int CPL, int RPW, int EPL, int LPR, bool TIER, bool BR>
 __global__ __launch_bounds__(256) void k_gateup(const float *__restrict__ p_z, const float *__restrict__ p_gs,
                                                 const uint32_t *__restrict__ p_hl, const float *__restrict__ p_hs,
-                                                const float *__restrict__ p_hx, int H, int E, FwdArgs a,
-                                                SlotParam<TIER> sl) {
+                                                const float *__restrict__ p_hx, int H, uint32_t ef,
+                                                const uint8_t *__restrict__ p_shared, FwdArgs a, SlotParam<TIER> sl) {
     using Q = QSlice<BITS, CPL>;
     const int t = blockIdx.y;
+    const int E = (int)(ef & 0xFFFFu), F = (int)(ef >> 16);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
     // 1. loads that do not depend on the routing, from the preloaded
@@ -421,21 +449,28 @@ __global__ __launch_bounds__(256) void k_gateup(const float *__restrict__ p_z, c
     const float hs = p_hs[(size_t)t * (H / 64) + (threadIdx.x < H / 64 ? threadIdx.x : 0)];
     const float hx = p_hx[(size_t)t * (H / 32) + (threadIdx.x < H / 32 ? threadIdx.x : 0)];
 
-    const int F = a.s.F, K = a.s.K;
-    const QMat &G = a.L.m[0];
-    const QMat &U = a.L.m[1];
-    const int lpr = G.lpr, rpi = 64 / lpr;
-    const int lr = lane % lpr, rsub = lane / lpr;
-    const int nrs = (K + 1) * F / rpi;
+    const int K = a.s.K;
+    // the gate and up matrices' layout from H and F (powers of two), not from
+    // FwdArgs: the shared expert's loads then wait for no argument read
+    const QMat G = gate_up_qmat<BITS>(H, F, 0);
+    const QMat U = gate_up_qmat<BITS>(H, F, 1);
+    const int lpr = G.lpr, lsh = __builtin_ctz((unsigned)lpr), rpi = 64 >> lsh;
+    const int lr = lane & (lpr - 1), rsub = lane >> lsh;
+    const int fsh = __builtin_ctz((unsigned)F) - (6 - lsh);  // log2(F / rpi): row-steps per slot
     // the blocks of the shared expert (the last slot) run first: their loads
     // need no routing and keep HBM busy while the routed waves route
-    const int nbs = (F / rpi + 4 * RPW - 1) / (4 * RPW);
-    const int lb = blockIdx.x < nbs ? blockIdx.x + gridDim.x - nbs : blockIdx.x - nbs;
+    const int nbs = ((1 << fsh) + 4 * RPW - 1) / (4 * RPW);
+    // BR (slots fill whole blocks, grid (K + 1) nbs): a block's slot and rows
+    // from blockIdx alone
+    constexpr bool kAligned = BR && !TIER;
+    const int nrs = (K + 1) << fsh;
+    const int lb = blockIdx.x < nbs ? blockIdx.x + (kAligned ? K * nbs : gridDim.x - nbs) : blockIdx.x - nbs;
     const int rs0 = (lb * 4 + wave) * RPW;
-    const bool active = rs0 < nrs;
+    const bool active = kAligned || rs0 < nrs;
     // slot of every row-step of the wave (waves past the end take the last one;
     // with BR the whole block's)
-    const int slot = __builtin_amdgcn_readfirstlane(((active ? rs0 : nrs - 1) * rpi) / F);
+    const int slot = kAligned ? (blockIdx.x < nbs ? K : __builtin_amdgcn_readfirstlane((blockIdx.x - nbs) * 4 * RPW) >> fsh)
+                              : __builtin_amdgcn_readfirstlane((active ? rs0 : nrs - 1) >> fsh);
 
     __shared__ __align__(16) uint32_t s_hl[kLimbs * kMaxDim / 8];  // limbs of h, [kLimbs][H/8]
     __shared__ float s_hs[kMaxDim / 64];
@@ -443,12 +478,12 @@ __global__ __launch_bounds__(256) void k_gateup(const float *__restrict__ p_z, c
     __shared__ int s_ex;  // BR: the block's expert
 
     // 2. the wave's expert (the shared expert's waves do not wait for the logits)
-    const uint8_t *ex = a.shared;
-    bool late = false;  // BR, routed block: weight loads after the barrier
+    const uint8_t *ex = p_shared;
+    // BR, routed block: weight loads after the barrier (known without K)
+    const bool late = kAligned && blockIdx.x >= nbs;
     if constexpr (TIER) {
-        ex = (slot < K) ? a.experts + (size_t)sl.s[t * K + slot] * a.L.bytes : a.shared;
+        ex = (slot < K) ? a.experts + (size_t)sl.s[t * K + slot] * a.L.bytes : p_shared;
     } else if constexpr (BR) {
-        late = slot < K;
         if (late && __builtin_amdgcn_readfirstlane(wave) == 0) {
             // 2-bit codes: the routing wave takes issue priority over the
             // product waves sharing its SIMD until its weight loads are out
@@ -493,9 +528,10 @@ __global__ __launch_bounds__(256) void k_gateup(const float *__restrict__ p_z, c
         int jr[RPW];
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
-            const int rs = rs0 + i < nrs ? rs0 + i : nrs - 1;
-            const int p = rs * rpi + rsub;
-            jr[i] = p - (p / F) * F;
+            // row within the expert (aligned slots: from the block's position in its slot)
+            const int rs = kAligned ? ((blockIdx.x < nbs ? blockIdx.x : blockIdx.x - nbs) * 4 + wave) * RPW + i
+                                    : (rs0 + i < nrs ? rs0 + i : nrs - 1);
+            jr[i] = ((rs * rpi) & (F - 1)) + rsub;
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -907,7 +943,7 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st, const SlotP
         const int sel = (br ? 16 : 0) + G.cpl * 4 + (wide ? 2 : 0) + (full ? 1 : 0);
 #define MOE_GATEUP(CPL, EPL, LPR, BR)                                                                      \
     hipLaunchKernelGGL((k_gateup<BITS, CPL, RG, EPL, LPR, TIER, BR>), grid, dim3(256), 0, st, a.ws.z, a.ws.gs, \
-                       (const uint32_t *)a.ws.hl, a.ws.hs, a.ws.hx, H, E, a, sl)
+                       (const uint32_t *)a.ws.hl, a.ws.hs, a.ws.hx, H, (uint32_t)E | (uint32_t)F << 16, a.shared, a, sl)
         switch (sel) {
             case 4: MOE_GATEUP(1, 8, 0, false); break;
             case 5: MOE_GATEUP(1, 8, 64, false); break;
