@@ -580,14 +580,16 @@ __global__ __launch_bounds__(256) void k_gateup(const float *__restrict__ p_z, c
             constexpr int DL = LPR / NV;  // lanes sharing one reduced entry
             const int rs = rs0 + multi_index<NV, LPR>(lane) / 2;
             const float up = xchg<DL>(r);  // the up sum sits across the last halving bit
-            if ((lane & (2 * DL - 1)) == 0 && rs < nrs) act[rs * rpi + rsub] = r * sigmoidf_(r) * up;
+            // SwiGLU with the hardware exp and reciprocal (as in the grouped
+            // kernels): the IEEE division's ~15 instructions sat in the tail
+            if ((lane & (2 * DL - 1)) == 0 && rs < nrs) act[rs * rpi + rsub] = r * up * __builtin_amdgcn_rcpf(1.0f + __expf(-r));
         } else {
 #pragma unroll
             for (int i = 0; i < RPW; ++i) {
                 const int rs = rs0 + i;
                 const float g = lane_group_sum(part[2 * i], lpr);
                 const float u = lane_group_sum(part[2 * i + 1], lpr);
-                if (rs < nrs && lr == 0) act[rs * rpi + rsub] = g * sigmoidf_(g) * u;
+                if (rs < nrs && lr == 0) act[rs * rpi + rsub] = g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
             }
         }
     }
