@@ -465,18 +465,9 @@ struct QSlice {
     static constexpr float kCodeOffset = BITS == 4 ? 8.0f : 0.0f;  // signed code = q - offset
 };
 
-// 4-bit codes made signed (q - 8, as v_dot8_i32_i4 reads them) by one XOR per
-// dword, once per row; 2-bit codes are used as stored
-template <int BITS, int CPL>
-__device__ __forceinline__ void prep_codes(uint4 (&c)[CPL]) {
-    if constexpr (BITS == 4) {
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-            c[j] = make_uint4(c[j].x ^ 0x88888888u, c[j].y ^ 0x88888888u, c[j].z ^ 0x88888888u, c[j].w ^ 0x88888888u);
-    }
-}
-
-// NR prepared rows (prep_codes) against one vector's lane slice held in LDS.
+// NR rows of codes as stored (4-bit nibbles hold q XOR 8, the signed q - 8 that
+// v_dot8_i32_i4 reads; 2-bit codes are masked per dot) against one vector's
+// lane slice held in LDS.
 // The limb words are read one limb at a time, limb-major, so that only 8 of
 // them are live; each row keeps two integer Horner accumulators (limbs 5-4 and
 // 3-0, each below 2^25), combined in fp32 as hi * 2^16 + lo.  s: the rows'

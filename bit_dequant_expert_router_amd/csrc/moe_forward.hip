@@ -545,8 +545,7 @@ __global__ __launch_bounds__(256) void k_gateup(const float *__restrict__ p_z, c
     // 4. the staging and barrier of the other blocks, behind their weight loads
     if (!late) stage();
 
-    // 5. codes prepared once, then every row against the lane's limb slice of h
-    //    in LDS, limb-major
+    // 5. every row against the lane's limb slice of h in LDS, limb-major
     if constexpr (BITS == 2 && BR) __builtin_amdgcn_s_setprio(0);
     if (active) {
         constexpr int NV = 2 * RPW;  // entries 2i (gate) and 2i + 1 (up) of row-step i
@@ -555,8 +554,6 @@ __global__ __launch_bounds__(256) void k_gateup(const float *__restrict__ p_z, c
         float sc[NV][Q::NGL], of[NV][Q::NGL];
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
-            prep_codes<BITS, CPL>(gc[i]);
-            prep_codes<BITS, CPL>(uc[i]);
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 cl[2 * i][j] = gc[i][j];

@@ -504,10 +504,11 @@ MOE_HD int mfma_lds_bytes(bool down) { return 3 * mfma_buf_words(down) * 4; }
 
 // the 8 codes of a dword as bf16 values 16 + q in reduction order (4 dwords,
 // value 2j in the low half of dword j): one byte-select and one shift-or per
-// two codes.  Nibble order: code j in nibble j; byte order: code j in byte
-// j % 4 at bit 4 (j / 4).
+// two codes.  Nibble order: code j in nibble j, stored as q XOR 8; byte order:
+// code j in byte j % 4 at bit 4 (j / 4).
 template <bool BYTE_CODES>
 __device__ __forceinline__ u32x4v codes_bf16(uint32_t d) {
+    if constexpr (!BYTE_CODES) d ^= 0x88888888u;
     const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;
     u32x4v r;
     if constexpr (BYTE_CODES) {
@@ -725,7 +726,15 @@ __global__ __launch_bounds__(256) void k_grouped_stream(FwdArgs a, StreamPlan pl
         for (int i = 0; i < RPW; ++i)
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                prep_codes<BITS, CPL>(w.c[m][i]);
+                // the down matrix's 4-bit codes (byte order) made signed, q XOR 8, as
+                // the gate and up codes are stored
+                if constexpr (DOWN && BITS == 4) {
+#pragma unroll
+                    for (int j = 0; j < CPL; ++j) {
+                        uint4 &c = w.c[m][i][j];
+                        c = make_uint4(c.x ^ 0x88888888u, c.y ^ 0x88888888u, c.z ^ 0x88888888u, c.w ^ 0x88888888u);
+                    }
+                }
 #pragma unroll
                 for (int g = 0; g < Q::NGL; ++g) {
                     sc[NM * i + m][g] = bf16_lo(w.sb[m][i][g]);

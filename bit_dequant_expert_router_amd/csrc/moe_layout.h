@@ -11,7 +11,8 @@
 // consecutive codes of the row ("logical chunk" L covers columns
 // [L*C, L*C + C)), D = 32/bits codes per dword; code i sits in dword i / D at a
 // bit position t = i % D that depends on the matrix's order:
-//   nibble order (gate, up): 4-bit code t at bits [4t, 4t+4); 2-bit code t < 8
+//   nibble order (gate, up): 4-bit code t at bits [4t, 4t+4), stored as
+//     q XOR 8 (the signed value q - 8 in two's complement); 2-bit code t < 8
 //     at bits [4t, 4t+2) and code t >= 8 at bits [4(t-8)+2, 4(t-8)+4).  The
 //     dword itself (4-bit) or each of d & 0x33333333 and (d >> 2) & 0x33333333
 //     (2-bit) is then eight 4-bit lanes holding consecutive codes, the operand

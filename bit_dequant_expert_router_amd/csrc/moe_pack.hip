@@ -55,10 +55,12 @@ __device__ __forceinline__ uint4 make_chunk(int bits, int order, CodeFn code_of)
     uint32_t d[4] = {0u, 0u, 0u, 0u};
     const int C = 128 / bits;
     const uint32_t mask = (1u << bits) - 1u;
+    // 4-bit nibble order stores q XOR 8: the signed code q - 8 as v_dot8_i32_i4 reads it
+    const uint32_t flip = (bits == 4 && order == kOrderNibble) ? 8u : 0u;
     for (int i = 0; i < C; ++i) {
         int dw, shift;
         code_pos(bits, order, i, dw, shift);
-        d[dw] |= ((uint32_t)code_of(i) & mask) << shift;
+        d[dw] |= (((uint32_t)code_of(i) & mask) ^ flip) << shift;
     }
     return make_uint4(d[0], d[1], d[2], d[3]);
 }
