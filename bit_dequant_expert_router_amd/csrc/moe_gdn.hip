@@ -49,7 +49,11 @@ __global__ __launch_bounds__(256) void k_gdn(int n_heads, int T, float *__restri
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
         row[r] = 2 * (rs0 + r - h * kGdnStepsPerHead) + half;  // row of the head's state
-        S[r] = *(const float4 *)(state + ((size_t)h * kGdnD + row[r]) * kGdnD + 4 * lr);
+        // the state streams through once per call: nontemporal loads (3.76 -> 3.22 us
+        // per update at 64 heads) and stores
+        const float *src = state + ((size_t)h * kGdnD + row[r]) * kGdnD + 4 * lr;
+        S[r] = make_float4(__builtin_nontemporal_load(src), __builtin_nontemporal_load(src + 1),
+                           __builtin_nontemporal_load(src + 2), __builtin_nontemporal_load(src + 3));
     }
     for (int t = 0; t < T; ++t) {
         const size_t th = (size_t)t * n_heads + h;
@@ -82,7 +86,13 @@ __global__ __launch_bounds__(256) void k_gdn(int n_heads, int T, float *__restri
         }
     }
 #pragma unroll
-    for (int r = 0; r < RW; ++r) *(float4 *)(state + ((size_t)h * kGdnD + row[r]) * kGdnD + 4 * lr) = S[r];
+    for (int r = 0; r < RW; ++r) {
+        float *dst = state + ((size_t)h * kGdnD + row[r]) * kGdnD + 4 * lr;
+        __builtin_nontemporal_store(S[r].x, dst);
+        __builtin_nontemporal_store(S[r].y, dst + 1);
+        __builtin_nontemporal_store(S[r].z, dst + 2);
+        __builtin_nontemporal_store(S[r].w, dst + 3);
+    }
 }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
