@@ -65,7 +65,7 @@ KERNEL_TRAFFIC = {
                                       "write_kib": 3621.21875, "fetch_scale": 2.0, "write_scale": 1.0},
     ("batch32", "k_grouped_down"): {"source_sha256_prefix": "2ab152e68fa0c42b", "fetch_kib": 287705.8125,
                                     "write_kib": 6141.5, "fetch_scale": 2.0, "write_scale": 1.0},
-    ("gdn", "k_gdn"): {"source_sha256_prefix": "9038968202900e66", "fetch_kib": 2350.0, "write_kib": 4128.0,
+    ("gdn", "k_gdn"): {"source_sha256_prefix": "aadb9822606e2f30", "fetch_kib": 2350.0, "write_kib": 4128.0,
                        "fetch_scale": 2.0, "write_scale": 1.0},
 }
 
