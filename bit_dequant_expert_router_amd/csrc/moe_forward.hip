@@ -965,7 +965,10 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st, const SlotP
         const QMat &Dm = a.L.m[2];
         const int rpi = 64 / Dm.lpr;
         const int nrs = H / rpi;
-        const int blocks = (nrs + 4 * RD - 1) / (4 * RD);
+        // rows of fewer than 16 lanes (small F, e.g. 128): one row-step per wave and
+        // twice the blocks (hidden 256 / FFN 128 layer: k_down 3.55 -> 3.11 us)
+        const int rdl = (Dm.cpl == 1 && Dm.lpr < 16) ? 1 : RD;
+        const int blocks = (nrs + 4 * rdl - 1) / (4 * rdl);
         dim3 grid(blocks, T);
         // per slot: limb words (3 per 4 values, a 4-word pad per lane slice),
         // slice scales and half-group sums
@@ -997,8 +1000,8 @@ hipError_t launch_stage(const FwdArgs &a, int stage, hipStream_t st, const SlotP
                 case 6: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, false, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
                 case 7: hipLaunchKernelGGL((k_down<BITS, 1, RD, 16, true, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
                 case 8: hipLaunchKernelGGL((k_down<BITS, 1, RDS, 16, true, TIER, 2, DR>), grid, b2, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
-                case 9: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, false, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
-                default: hipLaunchKernelGGL((k_down<BITS, 1, RD, 0, true, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
+                case 9: hipLaunchKernelGGL((k_down<BITS, 1, 1, 0, false, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
+                default: hipLaunchKernelGGL((k_down<BITS, 1, 1, 0, true, TIER, 1>), grid, b1, lds, st, a.x, a.ws.sel, a.ws.coef, a.ws.act, H, F, K, batch, f4r, a, sl); break;
             }
         } else {
             return hipErrorInvalidValue;
