@@ -53,13 +53,13 @@ METRIC = "MoE-layer decode tokens/s (effective expert-weight HBM GB/s and % of p
 # on.  FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0, the ratios of bytes
 # moved to counts reported for a 256 MiB copy.
 KERNEL_TRAFFIC = {
-    ("layer4", "k_gateup"): {"source_sha256_prefix": "1f1d15f14e0c3196", "fetch_kib": 11625.15625, "write_kib": 40.125,
+    ("layer4", "k_gateup"): {"source_sha256_prefix": "02152d97d7a87fca", "fetch_kib": 11625.28125, "write_kib": 40.125,
                              "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer4", "k_down"): {"source_sha256_prefix": "1f1d15f14e0c3196", "fetch_kib": 5907.5, "write_kib": 16.0,
+    ("layer4", "k_down"): {"source_sha256_prefix": "02152d97d7a87fca", "fetch_kib": 5907.5, "write_kib": 16.0,
                            "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer2", "k_gateup"): {"source_sha256_prefix": "1f1d15f14e0c3196", "fetch_kib": 6514.15625, "write_kib": 20.125,
+    ("layer2", "k_gateup"): {"source_sha256_prefix": "02152d97d7a87fca", "fetch_kib": 6514.0625, "write_kib": 20.125,
                              "fetch_scale": 2.0, "write_scale": 1.0},
-    ("layer2", "k_down"): {"source_sha256_prefix": "1f1d15f14e0c3196", "fetch_kib": 3347.0, "write_kib": 16.0,
+    ("layer2", "k_down"): {"source_sha256_prefix": "02152d97d7a87fca", "fetch_kib": 3347.0, "write_kib": 16.0,
                            "fetch_scale": 2.0, "write_scale": 1.0},
     ("batch32", "k_grouped_gateup"): {"source_sha256_prefix": "2ab152e68fa0c42b", "fetch_kib": 569578.6875,
                                       "write_kib": 3621.21875, "fetch_scale": 2.0, "write_scale": 1.0},
