@@ -191,7 +191,7 @@ def traffic_of(wl_name, kernel, sha):
 
 def refuse_multi_gpu(args):
     if args.gpus != 1:
-        msg = (f"bench.py: --gpus {args.gpus} is not supported: this build runs the expert layer on one GPU "
+        msg = (f"bench.py: --gpus {args.gpus} is not supported: the library runs the expert layer on one GPU "
                "(every expert resident in that GPU's HBM); run with --gpus 1")
         print(msg, flush=True)
         print(msg, file=sys.stderr, flush=True)
